@@ -1,0 +1,233 @@
+/*
+ * zero_mi355x.h -- C ABI of one data-parallel rank's share of ZeRO's
+ * partitioned mixed-precision Adam step, on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages on ZeRO, cited by page title and paragraph topic):
+ *   [legal]   "ZeRO Optimization", inferensys glossary, domain-specific
+ *             legal pre-training page
+ *   [instr]   "ZeRO Optimization", inferensys glossary, instruction-tuning
+ *             methodologies page
+ *   [genomic] "ZeRO Optimization", inferensys glossary, genomic MLOps page
+ *
+ * The step of rank r of R, per call:
+ *   zero_partition_plan     flat partition + bucket plan (host only)
+ *   zero_flatten_grads      half gradients -> the rank's flat gradient shard,
+ *                           with the inf/NaN test fused into the copy
+ *   zero_adam_step          unscale + Adam/AdamW + cast back to half, gated
+ *                           on the overflow flag; returns the flag
+ *   zero_update_loss_scale  dynamic loss-scale policy (host only)
+ *   zero_write_param_shard  fp32 master shard -> half params at its offset
+ *
+ * Conventions
+ *   Errors   every call returns an int: 0 (ZERO_OK) or a negative ZERO_E*
+ *            code; zero_adam_step returns 0 (applied) or 1 (overflow,
+ *            skipped).  A message for the last error of the calling thread
+ *            is available from zero_last_error().
+ *   Memory   the caller allocates and owns every device buffer and stream.
+ *            The plan owns only its host tables, a 4-byte device overflow
+ *            flag and a 4-byte pinned host mirror, created on the first
+ *            device call and released by zero_plan_destroy.  Buffers are
+ *            not retained between calls.
+ *   Streams  all device work is enqueued on the caller's stream (a
+ *            hipStream_t passed as void*; NULL means the default stream).
+ *            Only zero_adam_step waits, and only for its own stream, to read
+ *            the flag back.
+ *   Devices  a plan binds to the device that is current at its first device
+ *            call; later device calls must run with that device current.
+ *   Threads  a plan is not thread safe; distinct plans are independent.
+ *   Layout   element counts, offsets and indices are int64 elements, not
+ *            bytes.  Tensors are concatenated in registration order into
+ *            one flat index space [0, P).
+ *   Dtypes   gradients and parameters are fp16 (ZERO_F16) or bf16
+ *            (ZERO_BF16); master weights and both moments are fp32.
+ */
+#ifndef ZERO_MI355X_H
+#define ZERO_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct zero_plan zero_plan_t; /* opaque, library owned */
+
+enum zero_dtype { ZERO_F16 = 1, ZERO_BF16 = 2 };
+
+enum zero_status {
+    ZERO_OK = 0,
+    ZERO_EINVAL = -1, /* bad argument value */
+    ZERO_EALIGN = -2, /* a buffer is not aligned as required */
+    ZERO_ENULL = -3,  /* a required pointer is NULL */
+    ZERO_EHIP = -4,   /* the HIP runtime reported an error */
+    ZERO_ENOMEM = -5, /* host or device allocation failed */
+    ZERO_ESTATE = -6  /* call not valid in the plan's state (e.g. wrong device) */
+};
+
+/* One tensor's part of the rank's shard: elements
+ * [tensor_off, tensor_off + numel) of tensor `tensor` sit at
+ * [shard_off, shard_off + numel) of the shard; `bucket` is the tensor's
+ * bucket. */
+typedef struct {
+    int64_t tensor;
+    int64_t tensor_off;
+    int64_t shard_off;
+    int64_t numel;
+    int32_t bucket;
+    int32_t _pad;
+} zero_segment_t;
+
+typedef struct {
+    int64_t total_numel;  /* P: sum of tensor sizes */
+    int64_t padded_numel; /* P_pad: P rounded up to a multiple of R * align */
+    int64_t shard_numel;  /* S = P_pad / R: elements of every rank's shard */
+    int64_t shard_begin;  /* r * S: flat index of the shard's first element */
+    int64_t real_numel;   /* elements of the shard below P (the rest is padding) */
+    int64_t align_elems;
+    int64_t bucket_elems;
+    int64_t bytes_stage1; /* 4 P + 12 S  (optimizer states partitioned)       */
+    int64_t bytes_stage2; /* 2 P + 14 S  (+ gradients partitioned)            */
+    int64_t bytes_stage3; /* 16 S        (+ parameters partitioned)           */
+    int32_t world_size;
+    int32_t rank;
+    int32_t n_tensors;
+    int32_t n_segments;
+    int32_t n_buckets;
+    int32_t _pad;
+} zero_plan_info_t;
+
+typedef struct {
+    double lr;
+    double beta1;
+    double beta2;
+    double eps;
+    double weight_decay;
+    int32_t adamw; /* 1: decoupled decay (AdamW); 0: L2 term added to the gradient */
+    int32_t _pad;
+} zero_adam_hparams_t;
+
+typedef struct {
+    double scale;     /* current loss scale (> 0) */
+    double min_scale; /* floor for backoff (> 0) */
+    double backoff;   /* factor on overflow, in (0, 1] (0.5: halve) */
+    double growth;    /* factor after `window` clean steps, >= 1 (2: double) */
+    int32_t window;   /* clean steps before growth, >= 1 */
+    int32_t good_steps;
+    int32_t dynamic;  /* 0: static scale (bf16 needs none) */
+    int32_t _pad;
+} zero_scaler_t;
+
+/* Partition plan.  [instr] ZeRO-1 mechanism and memory reduction: each of
+ * the R data-parallel ranks owns one partition and updates only it;
+ * [genomic] memory breakdown: per-rank memory is the total divided by R.
+ * [legal] bandwidth bullet / [genomic] overlap paragraph: small tensors are
+ * fused into buckets.
+ *   P_pad = ceil(P / (R*align)) * R*align, S = P_pad / R, rank r owns the
+ *   contiguous flat range [r*S, (r+1)*S).  Buckets are formed from the last
+ *   tensor to the first, whole tensors only, each closed once it holds at
+ *   least bucket_elems elements; bucket 0 holds the last tensor.
+ * numels: host array of n_tensors sizes (>= 0; zero-size tensors allowed).
+ * world_size >= 1, 0 <= rank < world_size, align_elems >= 1 (64 keeps every
+ * shard 256-byte aligned in fp32), bucket_elems >= 1.
+ * Host only: needs no GPU.  *out receives a new plan (free with
+ * zero_plan_destroy).  Errors: ZERO_ENULL, ZERO_EINVAL, ZERO_ENOMEM. */
+int zero_partition_plan(const int64_t* numels, int32_t n_tensors, int32_t world_size,
+                        int32_t rank, int64_t align_elems, int64_t bucket_elems,
+                        zero_plan_t** out);
+
+/* Sizes and byte accounting of a plan (host only). */
+int zero_plan_info(const zero_plan_t* plan, zero_plan_info_t* out);
+
+/* Copies up to `cap` segments, in shard order, into `out` (host memory) and
+ * returns the plan's segment count (>= 0) or a negative error. */
+int64_t zero_plan_segments(const zero_plan_t* plan, zero_segment_t* out, int64_t cap);
+
+/* Writes the bucket id of each of the first min(cap, n_tensors) tensors. */
+int zero_plan_tensor_buckets(const zero_plan_t* plan, int32_t* out, int64_t cap);
+
+/* Releases the plan and its device flag (NULL is a no-op). */
+void zero_plan_destroy(zero_plan_t* plan);
+
+/* Bucketed flatten of half gradients into the rank's flat shard.
+ * [legal] ZeRO-2 bullet / [instr] ZeRO-2 mechanism: a rank keeps only the
+ * gradients of its partition.  For every segment of `bucket` (0 <= bucket
+ * < n_buckets) or of all buckets (bucket = -1):
+ *   flat_grad[shard_off + k] = grads[tensor][tensor_off + k]   (bit copy)
+ * and flat_grad[real, S) = 0 on every call.  While copying, any element
+ * whose exponent field is all ones (+-inf or NaN) raises the plan's device
+ * overflow flag ([legal] dynamic loss scaling bullet); the flag stays
+ * raised until the next zero_adam_step consumes it.
+ * grads: HOST array of n_tensors DEVICE pointers, each to tensor i's first
+ * element, 2-byte aligned; entries of tensors without a segment in the
+ * requested bucket(s) may be NULL.  flat_grad: device, >= S elements,
+ * 16-byte aligned.  Async on `stream`.
+ * Errors: ZERO_ENULL, ZERO_EINVAL (bucket, dtype), ZERO_EALIGN, ZERO_EHIP,
+ * ZERO_ESTATE (wrong device). */
+int zero_flatten_grads(zero_plan_t* plan, int32_t bucket, const void* const* grads,
+                       int32_t grad_dtype, void* flat_grad, void* stream);
+
+/* One gated Adam/AdamW step on the shard, with the half cast fused in.
+ * [genomic] memory breakdown / [instr] ZeRO-1 mechanism: fp32 master
+ * weights, momentum and variance of the partition, updated by their owner;
+ * [instr] mixed-precision bullets: the gradient is scaled down and upcast
+ * to fp32 for the update, and the weights are cast to fp16/bf16.
+ * If the flag is raised -- by zero_flatten_grads since the last step, or by
+ * a scan of flat_grad that runs first whenever not every bucket of the
+ * shard was flattened into this flat_grad since the last step -- nothing
+ * is written and 1 is returned.  Otherwise, per shard element k < S, in
+ * fp32 with one rounding per operation (scalars formed on the host in
+ * double and rounded once):
+ *   g = half(flat_grad[k]) * fp32(1/loss_scale)  [adamw=0: g += wd * p]
+ *   m = b1*m + (1-b1)*g ;  v = b2*v + (1-b2)*(g*g)
+ *   d = sqrt(v) * fp32(1/sqrt(1-b2^t)) + eps ;  u = m / d
+ *   p = p * fp32(1 - lr*wd [adamw] or 1) - fp32(lr/(1-b1^t)) * u
+ * and, if param != NULL, for k < real:
+ *   param[shard_begin + k - param_base] = round_to_nearest_even_half(p)
+ * step: the bias-correction step t >= 1 (count applied steps only).
+ * loss_scale: finite, > 0.  master/exp_avg/exp_avg_sq: device fp32 arrays
+ * of >= S elements, 16-byte aligned.  param: device buffer holding flat
+ * indices [param_base, param_base + param_numel), which must contain
+ * [shard_begin, shard_begin + real); 2-byte aligned.
+ * Returns 0 applied, 1 skipped, or a negative error (ZERO_ENULL,
+ * ZERO_EINVAL, ZERO_EALIGN, ZERO_EHIP, ZERO_ESTATE).  Waits for `stream`. */
+int zero_adam_step(zero_plan_t* plan, const zero_adam_hparams_t* hp, int64_t step,
+                   double loss_scale, const void* flat_grad, int32_t grad_dtype, float* master,
+                   float* exp_avg, float* exp_avg_sq, void* param, int64_t param_base,
+                   int64_t param_numel, int32_t param_dtype, void* stream);
+
+/* Dynamic loss scale, host only.  [legal] dynamic loss scaling bullet: the
+ * scale adjusts itself; [instr] loss-scaling bullet: scaled up before
+ * backward, down before the update; [legal] bfloat16 bullet: bf16 needs no
+ * loss scaling (use dynamic = 0).
+ *   overflow != 0: scale = max(scale * backoff, min_scale) (if dynamic),
+ *                  good_steps = 0
+ *   overflow == 0: good_steps += 1; if dynamic and good_steps >= window:
+ *                  scale *= growth, good_steps = 0
+ * Errors: ZERO_ENULL, ZERO_EINVAL (non-finite or non-positive fields). */
+int zero_update_loss_scale(zero_scaler_t* scaler, int32_t overflow);
+
+/* Standalone cast of the fp32 master shard to half parameters at the
+ * rank's offset ([instr] mixed-precision bullet: weights are cast to
+ * FP16/BF16): param[shard_begin + k - param_base] = rne_half(master[k]) for
+ * k < real; padding is never written.  Arguments as in zero_adam_step.
+ * Async on `stream`. */
+int zero_write_param_shard(zero_plan_t* plan, const float* master, void* param,
+                           int64_t param_base, int64_t param_numel, int32_t param_dtype,
+                           void* stream);
+
+/* Message of the calling thread's last error ("" if none). */
+const char* zero_last_error(void);
+
+/* Kernel timing with HIP events recorded on the launch stream around each
+ * kernel (off by default).  which: 0 flatten (all launches of the last
+ * call), 1 overflow scan, 2 fused Adam, 3 parameter write.  *ms receives
+ * the last launch's duration; the call waits for that launch to finish.
+ * Errors: ZERO_ESTATE if that kernel has not run since timing was enabled. */
+int zero_plan_set_timing(zero_plan_t* plan, int32_t on);
+int zero_plan_kernel_ms(zero_plan_t* plan, int32_t which, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_MI355X_H */

@@ -59,6 +59,7 @@ def _load_dev():
     if _dev is None:
         if not os.path.exists(DEV_LIB):
             raise ImportError(f"{DEV_LIB} is not built; run __graft_entry__.build()")
+        import torch  # noqa: F401  (bind to torch's HIP runtime: one runtime per process)
         lib = ctypes.CDLL(DEV_LIB)
         lib.synth_dev_fill_f32.restype = ctypes.c_int
         lib.synth_dev_fill_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,

@@ -1,0 +1,150 @@
+"""Host-side checks of libzero_mi355x (CPU only, no device compute).
+
+* the library loads and exports every function include/*.h declares;
+* its planner agrees with the oracle's on every rank of every workload and
+  on random small models (sizes, segments, buckets, byte accounting);
+* its loss-scale policy agrees with the oracle's on random sequences;
+* argument errors are reported before any device work.
+"""
+import ctypes
+import glob
+import os
+import random
+import re
+
+import pytest
+
+import oracle
+import zero_partitioned_mixed_plan_amd as z
+from zero_partitioned_mixed_plan_amd import _abi
+from synth.workloads import WORKLOADS, get
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"zero_partition_plan", "zero_flatten_grads", "zero_adam_step",
+            "zero_update_loss_scale", "zero_write_param_shard"} <= names
+    lib = ctypes.CDLL(_abi.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    # and the binding declares a signature for each
+    assert names == set(_abi.SIGNATURES)
+
+
+def _compare(numels, R, r, A, B):
+    op = oracle.plan(numels, R, r, A, B)
+    zp = z.zero_partition_plan(numels, R, r, A, B)
+    assert (zp.P, zp.P_pad, zp.S, zp.begin, zp.real) == (op.P, op.P_pad, op.S, op.begin, op.real)
+    assert zp.n_buckets == op.n_buckets and zp.n_segments == op.n_segments
+    segs = zp.segments()
+    got = [(s.tensor, s.tensor_off, s.shard_off, s.numel) for s in segs]
+    exp = list(zip(op.seg_tensor.tolist(), op.seg_tensor_off.tolist(), op.seg_shard_off.tolist(),
+                   op.seg_numel.tolist()))
+    assert got == exp
+    tb = zp.tensor_buckets()
+    assert tb == op.tensor_bucket.tolist()
+    assert [s.bucket for s in segs] == [tb[t] for t, *_ in got]
+    i = zp.info
+    assert (i.bytes_stage1, i.bytes_stage2, i.bytes_stage3) == (
+        op.bytes_stage1, op.bytes_stage2, op.bytes_stage3)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_planner_matches_oracle_on_workloads(name):
+    w = get(name)
+    for r in range(w.world_size):
+        for B in (w.bucket_elems, 1 << 20):
+            _compare(w.numels, w.world_size, r, w.align, B)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_planner_matches_oracle_random(seed):
+    rng = random.Random(seed)
+    numels = [rng.choice([0, 1, 2, 7, 64, 100, 4097]) for _ in range(rng.randint(0, 12))]
+    R = rng.randint(1, 9)
+    A = rng.choice([1, 3, 8, 64])
+    B = rng.choice([1, 50, 1000, 1 << 25])
+    for r in range(R):
+        _compare(numels, R, r, A, B)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_loss_scale_policy_matches_oracle(seed):
+    rng = random.Random(seed)
+    dynamic = rng.random() < 0.8
+    init = rng.choice([1.0, 1024.0, 65536.0])
+    window = rng.randint(1, 5)
+    zs = z.LossScaler(init, dynamic=dynamic, window=window, min_scale=1.0)
+    os_ = oracle.Scaler(init, dynamic=dynamic, window=window, min_scale=1.0)
+    for _ in range(200):
+        ovf = 1 if rng.random() < 0.3 else 0
+        z.zero_update_loss_scale(zs, ovf)
+        os_.update(ovf)
+        assert zs.scale == os_.value
+        assert zs.good_steps == os_.good.value
+
+
+def test_argument_errors_before_device_work():
+    lib = _abi.lib
+    h = ctypes.c_void_p()
+    bad_plans = [([4], 0, 0, 1, 1), ([4], 2, 2, 1, 1), ([4], 1, 0, 0, 1), ([4], 1, 0, 1, 0),
+                 ([-3], 1, 0, 1, 1)]
+    for numels, R, r, A, B in bad_plans:
+        arr = (ctypes.c_int64 * 1)(*numels)
+        assert lib.zero_partition_plan(arr, 1, R, r, A, B, ctypes.byref(h)) == _abi.ZERO_EINVAL
+        assert z.zero_last_error() != ""
+    assert lib.zero_partition_plan(None, 1, 1, 0, 1, 1, ctypes.byref(h)) == _abi.ZERO_ENULL
+    assert lib.zero_partition_plan(None, 0, 1, 0, 1, 1, None) == _abi.ZERO_ENULL
+    # total size overflow
+    arr = (ctypes.c_int64 * 2)(1 << 62, 1 << 62)
+    assert lib.zero_partition_plan(arr, 2, 1, 0, 1, 1, ctypes.byref(h)) == _abi.ZERO_EINVAL
+
+    plan = z.zero_partition_plan([1000], 2, 0, 8)
+    hp = z.AdamHParams().to_c()
+    fake = 1 << 20  # 16-byte aligned, never dereferenced on these error paths
+    args = dict(step=1, scale=1.0, g=fake, gdt=z.ZERO_BF16, p=fake, m=fake, v=fake)
+
+    def step(**kw):
+        a = dict(args, **kw)
+        return lib.zero_adam_step(plan.handle, ctypes.byref(hp), a["step"], a["scale"], a["g"],
+                                  a["gdt"], a["p"], a["m"], a["v"], None, 0, 0, 0, None)
+    assert step(step=0) == _abi.ZERO_EINVAL
+    assert step(scale=0.0) == _abi.ZERO_EINVAL
+    assert step(scale=float("inf")) == _abi.ZERO_EINVAL
+    assert step(gdt=7) == _abi.ZERO_EINVAL
+    assert step(g=None) == _abi.ZERO_ENULL
+    assert step(m=fake + 4) == _abi.ZERO_EALIGN
+    bad_hp = z.AdamHParams(beta1=1.0).to_c()
+    assert lib.zero_adam_step(plan.handle, ctypes.byref(bad_hp), 1, 1.0, fake, z.ZERO_BF16, fake,
+                              fake, fake, None, 0, 0, 0, None) == _abi.ZERO_EINVAL
+    # a parameter window that misses the shard
+    assert lib.zero_adam_step(plan.handle, ctypes.byref(hp), 1, 1.0, fake, z.ZERO_BF16, fake,
+                              fake, fake, fake, 10, 100, z.ZERO_BF16, None) == _abi.ZERO_EINVAL
+    assert lib.zero_write_param_shard(plan.handle, fake, fake, 0, 10, z.ZERO_BF16,
+                                      None) == _abi.ZERO_EINVAL
+    assert lib.zero_write_param_shard(plan.handle, fake + 8, fake, 0, 1000, z.ZERO_BF16,
+                                      None) == _abi.ZERO_EALIGN
+    ptrs = (ctypes.c_void_p * 1)(None)
+    assert lib.zero_flatten_grads(plan.handle, 5, ptrs, z.ZERO_BF16, fake,
+                                  None) == _abi.ZERO_EINVAL
+    assert lib.zero_flatten_grads(plan.handle, -1, ptrs, z.ZERO_BF16, fake,
+                                  None) == _abi.ZERO_ENULL
+    ptrs = (ctypes.c_void_p * 1)(fake + 1)
+    assert lib.zero_flatten_grads(plan.handle, -1, ptrs, z.ZERO_BF16, fake,
+                                  None) == _abi.ZERO_EALIGN
+    assert lib.zero_flatten_grads(plan.handle, -1, ptrs, z.ZERO_BF16, fake + 2,
+                                  None) == _abi.ZERO_EALIGN
+    bad = _abi.zero_scaler_t(0.0, 1.0, 0.5, 2.0, 10, 0, 1, 0)
+    assert lib.zero_update_loss_scale(ctypes.byref(bad), 0) == _abi.ZERO_EINVAL
+    assert lib.zero_update_loss_scale(None, 0) == _abi.ZERO_ENULL

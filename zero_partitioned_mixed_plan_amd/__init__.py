@@ -1,0 +1,223 @@
+"""One data-parallel rank's share of ZeRO's partitioned mixed-precision Adam
+step, on an AMD Instinct MI355X.
+
+Every step runs in libzero_mi355x (host planner + HIP kernels for gfx950);
+this module only marshals arguments: torch tensors supply device pointers
+and the stream.  The functions keep the names of the C ABI
+(include/zero_mi355x.h):
+
+    zero_partition_plan(numels, world_size, rank, align_elems, bucket_elems) -> Plan
+    zero_flatten_grads(plan, bucket, grads, flat_grad, stream=None)
+    zero_adam_step(plan, hparams, step, loss_scale, flat_grad, master, exp_avg,
+                   exp_avg_sq, param=None, param_base=0, stream=None) -> 0 | 1
+    zero_update_loss_scale(scaler, overflow)
+    zero_write_param_shard(plan, master, param, param_base=0, stream=None)
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+from . import _abi
+from ._abi import ZERO_BF16, ZERO_F16, ZeroError, check, lib  # noqa: F401
+
+__all__ = ["Plan", "AdamHParams", "LossScaler", "ZeroError", "zero_partition_plan",
+           "zero_flatten_grads", "zero_adam_step", "zero_update_loss_scale",
+           "zero_write_param_shard", "zero_last_error", "ZERO_F16", "ZERO_BF16"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return ZERO_F16
+    if t.dtype == torch.bfloat16:
+        return ZERO_BF16
+    raise TypeError(f"expected a float16 or bfloat16 tensor, got {t.dtype}")
+
+
+def _stream_handle(stream, device) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _require(t, name: str, min_numel: int, dtypes) -> None:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs >= {min_numel}")
+
+
+@dataclass
+class AdamHParams:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+    adamw: bool = True
+
+    def to_c(self) -> _abi.zero_adam_hparams_t:
+        return _abi.zero_adam_hparams_t(self.lr, self.beta1, self.beta2, self.eps,
+                                        self.weight_decay, 1 if self.adamw else 0, 0)
+
+
+class LossScaler:
+    """Host state of the dynamic loss scale; the policy runs in the library."""
+
+    def __init__(self, scale: float = 65536.0, dynamic: bool = True, min_scale: float = 1.0,
+                 backoff: float = 0.5, growth: float = 2.0, window: int = 1000):
+        self.c = _abi.zero_scaler_t(scale, min_scale, backoff, growth, window, 0,
+                                    1 if dynamic else 0, 0)
+
+    @property
+    def scale(self) -> float:
+        return float(self.c.scale)
+
+    @property
+    def good_steps(self) -> int:
+        return int(self.c.good_steps)
+
+
+class Plan:
+    """A partition plan handle (owned; released on garbage collection)."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+        info = _abi.zero_plan_info_t()
+        check(lib.zero_plan_info(self._h, ctypes.byref(info)), "zero_plan_info")
+        self.info = info
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.zero_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    # sizes
+    P = property(lambda self: int(self.info.total_numel))
+    P_pad = property(lambda self: int(self.info.padded_numel))
+    S = property(lambda self: int(self.info.shard_numel))
+    begin = property(lambda self: int(self.info.shard_begin))
+    real = property(lambda self: int(self.info.real_numel))
+    n_buckets = property(lambda self: int(self.info.n_buckets))
+    n_segments = property(lambda self: int(self.info.n_segments))
+    n_tensors = property(lambda self: int(self.info.n_tensors))
+
+    def segments(self) -> List[_abi.zero_segment_t]:
+        n = int(check(lib.zero_plan_segments(self._h, None, 0), "zero_plan_segments"))
+        arr = (_abi.zero_segment_t * max(n, 1))()
+        check(lib.zero_plan_segments(self._h, arr, n), "zero_plan_segments")
+        return list(arr[:n])
+
+    def tensor_buckets(self) -> List[int]:
+        n = self.n_tensors
+        arr = (ctypes.c_int32 * max(n, 1))()
+        check(lib.zero_plan_tensor_buckets(self._h, arr, n), "zero_plan_tensor_buckets")
+        return list(arr[:n])
+
+    def set_timing(self, on: bool) -> None:
+        check(lib.zero_plan_set_timing(self._h, 1 if on else 0), "zero_plan_set_timing")
+
+    def kernel_ms(self, which: int) -> float:
+        """which: 0 flatten, 1 overflow scan, 2 fused Adam, 3 parameter write."""
+        ms = ctypes.c_float(0)
+        check(lib.zero_plan_kernel_ms(self._h, which, ctypes.byref(ms)), "zero_plan_kernel_ms")
+        return float(ms.value)
+
+
+def zero_partition_plan(numels: Sequence[int], world_size: int, rank: int,
+                        align_elems: int = 64, bucket_elems: int = 1 << 25) -> Plan:
+    arr = (ctypes.c_int64 * max(len(numels), 1))(*[int(n) for n in numels])
+    h = ctypes.c_void_p()
+    check(lib.zero_partition_plan(arr, len(numels), world_size, rank, align_elems, bucket_elems,
+                                  ctypes.byref(h)), "zero_partition_plan")
+    plan = Plan(h.value)
+    plan._numels = [int(n) for n in numels]
+    return plan
+
+
+def zero_flatten_grads(plan: Plan, bucket: int, grads: Sequence, flat_grad, stream=None) -> None:
+    """grads: one entry per tensor (a contiguous fp16/bf16 device tensor, or None for a
+    tensor without elements in the requested buckets of this shard)."""
+    torch = _torch()
+    if len(grads) != plan.n_tensors:
+        raise ValueError(f"need {plan.n_tensors} gradient entries, got {len(grads)}")
+    _require(flat_grad, "flat_grad", plan.S, (torch.float16, torch.bfloat16))
+    numels = None
+    ptrs = (ctypes.c_void_p * max(len(grads), 1))()
+    for i, g in enumerate(grads):
+        if g is None:
+            ptrs[i] = None
+            continue
+        if numels is None:
+            numels = [int(n) for n in _plan_numels(plan)]
+        _require(g, f"grads[{i}]", numels[i], (flat_grad.dtype,))
+        ptrs[i] = g.data_ptr()
+    check(lib.zero_flatten_grads(plan.handle, bucket, ptrs, _dtype_code(flat_grad),
+                                 flat_grad.data_ptr(), _stream_handle(stream, flat_grad.device)),
+          "zero_flatten_grads")
+
+
+def _plan_numels(plan: Plan) -> List[int]:
+    cached = getattr(plan, "_numels", None)
+    if cached is None:
+        raise RuntimeError("plan has no recorded tensor sizes")
+    return cached
+
+
+def zero_adam_step(plan: Plan, hparams: AdamHParams, step: int, loss_scale: float, flat_grad,
+                   master, exp_avg, exp_avg_sq, param=None, param_base: int = 0,
+                   stream=None) -> int:
+    """Returns 0 when the update was applied, 1 when an overflow skipped it."""
+    torch = _torch()
+    _require(flat_grad, "flat_grad", plan.S, (torch.float16, torch.bfloat16))
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _require(t, name, plan.S, (torch.float32,))
+    pptr, pnum, pdt = None, 0, 0
+    if param is not None:
+        _require(param, "param", 0, (torch.float16, torch.bfloat16))
+        pptr, pnum, pdt = param.data_ptr(), param.numel(), _dtype_code(param)
+    hp = hparams.to_c()
+    return check(lib.zero_adam_step(plan.handle, ctypes.byref(hp), int(step), float(loss_scale),
+                                    flat_grad.data_ptr(), _dtype_code(flat_grad),
+                                    master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(),
+                                    pptr, int(param_base), pnum, pdt,
+                                    _stream_handle(stream, master.device)), "zero_adam_step")
+
+
+def zero_update_loss_scale(scaler: LossScaler, overflow: int) -> None:
+    check(lib.zero_update_loss_scale(ctypes.byref(scaler.c), int(overflow)),
+          "zero_update_loss_scale")
+
+
+def zero_write_param_shard(plan: Plan, master, param, param_base: int = 0, stream=None) -> None:
+    torch = _torch()
+    _require(master, "master", plan.real, (torch.float32,))
+    _require(param, "param", 0, (torch.float16, torch.bfloat16))
+    check(lib.zero_write_param_shard(plan.handle, master.data_ptr(), param.data_ptr(),
+                                     int(param_base), param.numel(), _dtype_code(param),
+                                     _stream_handle(stream, master.device)),
+          "zero_write_param_shard")
+
+
+def zero_last_error() -> str:
+    return lib.zero_last_error().decode(errors="replace")

@@ -1,0 +1,409 @@
+// C-ABI entry points of libzero_mi355x: argument checks, host scalars,
+// device state of a plan, and kernel launches on the caller's stream.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+namespace zmi {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int fail(int code, const std::string& msg) {
+    set_error(msg);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    set_error(std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")");
+    return ZERO_EHIP;
+}
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int32_t d) { return d == ZERO_F16 || d == ZERO_BF16; }
+
+// Binds the plan to the current device on first use and creates its flag.
+int ensure_device(zero_plan* p) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    DeviceState& d = p->dev;
+    if (d.ready) {
+        if (dev != d.device) {
+            return fail(ZERO_ESTATE, "plan is bound to device " + std::to_string(d.device) +
+                                         " but device " + std::to_string(dev) + " is current");
+        }
+        return ZERO_OK;
+    }
+    e = hipDeviceGetAttribute(&d.cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    e = hipMalloc(reinterpret_cast<void**>(&d.d_flag), 256);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(flag)");
+    e = hipHostMalloc(reinterpret_cast<void**>(&d.h_flag), sizeof(int), hipHostMallocDefault);
+    if (e != hipSuccess) {
+        (void)hipFree(d.d_flag);
+        d.d_flag = nullptr;
+        return hip_fail(e, "hipHostMalloc(flag mirror)");
+    }
+    *d.h_flag = 0;
+    e = hipMemset(d.d_flag, 0, 256);
+    if (e != hipSuccess) return hip_fail(e, "hipMemset(flag)");
+    for (int i = 0; i < kTimers; ++i) {
+        e = hipEventCreate(&d.ev_start[i]);
+        if (e == hipSuccess) e = hipEventCreate(&d.ev_stop[i]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    d.device = dev;
+    d.ready = true;
+    return ZERO_OK;
+}
+
+int timer_start(zero_plan* p, Timer t, hipStream_t s) {
+    if (!p->dev.timing) return ZERO_OK;
+    hipError_t e = hipEventRecord(p->dev.ev_start[t], s);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "hipEventRecord");
+}
+
+int timer_stop(zero_plan* p, Timer t, hipStream_t s) {
+    if (!p->dev.timing) return ZERO_OK;
+    hipError_t e = hipEventRecord(p->dev.ev_stop[t], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    p->dev.timed[t] = true;
+    return ZERO_OK;
+}
+
+// Parameter destination of shard element 0, after checking that the
+// caller's window [base, base + numel) covers the shard's real elements.
+int param_target(const zero_plan* p, void* param, int64_t base, int64_t numel, int32_t dtype,
+                 uint16_t** out) {
+    *out = nullptr;
+    if (param == nullptr) return ZERO_OK;
+    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "param_dtype must be ZERO_F16 or ZERO_BF16");
+    if ((reinterpret_cast<uintptr_t>(param) & 1u) != 0) {
+        return fail(ZERO_EALIGN, "param must be 2-byte aligned");
+    }
+    if (p->real > 0) {
+        if (base < 0 || numel < 0 || p->begin < base || p->begin + p->real - base > numel) {
+            return fail(ZERO_EINVAL, "param window [param_base, param_base + param_numel) must "
+                                     "contain the shard's flat range [shard_begin, shard_begin + "
+                                     "real)");
+        }
+    }
+    *out = static_cast<uint16_t*>(param) + (p->begin - base);
+    return ZERO_OK;
+}
+
+}  // namespace
+}  // namespace zmi
+
+using namespace zmi;
+
+extern "C" {
+
+int zero_partition_plan(const int64_t* numels, int32_t n_tensors, int32_t world_size,
+                        int32_t rank, int64_t align_elems, int64_t bucket_elems,
+                        zero_plan_t** out) {
+    if (out == nullptr) return fail(ZERO_ENULL, "out is NULL");
+    *out = nullptr;
+    zero_plan* p = new (std::nothrow) zero_plan();
+    if (p == nullptr) return fail(ZERO_ENOMEM, "plan allocation failed");
+    int rc;
+    try {
+        rc = build_plan(numels, n_tensors, world_size, rank, align_elems, bucket_elems, p);
+    } catch (const std::bad_alloc&) {
+        rc = fail(ZERO_ENOMEM, "plan tables allocation failed");
+    }
+    if (rc != ZERO_OK) {
+        delete p;
+        return rc;
+    }
+    *out = p;
+    return ZERO_OK;
+}
+
+int zero_plan_info(const zero_plan_t* p, zero_plan_info_t* out) {
+    if (p == nullptr || out == nullptr) return fail(ZERO_ENULL, "plan or out is NULL");
+    std::memset(out, 0, sizeof(*out));
+    out->total_numel = p->P;
+    out->padded_numel = p->P_pad;
+    out->shard_numel = p->S;
+    out->shard_begin = p->begin;
+    out->real_numel = p->real;
+    out->align_elems = p->align;
+    out->bucket_elems = p->bucket_elems;
+    // per-rank model-state bytes: half params 2 B, half grads 2 B, fp32
+    // master + momentum + variance 12 B per element held
+    out->bytes_stage1 = 2 * p->P + 2 * p->P + 12 * p->S;
+    out->bytes_stage2 = 2 * p->P + 2 * p->S + 12 * p->S;
+    out->bytes_stage3 = 2 * p->S + 2 * p->S + 12 * p->S;
+    out->world_size = p->R;
+    out->rank = p->r;
+    out->n_tensors = static_cast<int32_t>(p->numels.size());
+    out->n_segments = static_cast<int32_t>(p->segs.size());
+    out->n_buckets = p->n_buckets;
+    return ZERO_OK;
+}
+
+int64_t zero_plan_segments(const zero_plan_t* p, zero_segment_t* out, int64_t cap) {
+    if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");
+    if (cap < 0) return fail(ZERO_EINVAL, "cap must be >= 0");
+    if (cap > 0 && out == nullptr) return fail(ZERO_ENULL, "out is NULL");
+    const int64_t n = static_cast<int64_t>(p->segs.size());
+    for (int64_t s = 0; s < n && s < cap; ++s) {
+        const Segment& g = p->segs[s];
+        out[s] = zero_segment_t{g.tensor, g.tensor_off, g.shard_off, g.numel, g.bucket, 0};
+    }
+    return n;
+}
+
+int zero_plan_tensor_buckets(const zero_plan_t* p, int32_t* out, int64_t cap) {
+    if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");
+    if (cap < 0) return fail(ZERO_EINVAL, "cap must be >= 0");
+    if (cap > 0 && out == nullptr) return fail(ZERO_ENULL, "out is NULL");
+    const int64_t n = static_cast<int64_t>(p->tensor_bucket.size());
+    for (int64_t i = 0; i < n && i < cap; ++i) out[i] = p->tensor_bucket[i];
+    return ZERO_OK;
+}
+
+void zero_plan_destroy(zero_plan_t* p) {
+    if (p == nullptr) return;
+    DeviceState& d = p->dev;
+    if (d.ready) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        if (cur != d.device) (void)hipSetDevice(d.device);
+        for (int i = 0; i < kTimers; ++i) {
+            if (d.ev_start[i]) (void)hipEventDestroy(d.ev_start[i]);
+            if (d.ev_stop[i]) (void)hipEventDestroy(d.ev_stop[i]);
+        }
+        if (d.d_flag) (void)hipFree(d.d_flag);
+        if (d.h_flag) (void)hipHostFree(d.h_flag);
+        if (cur != d.device && cur >= 0) (void)hipSetDevice(cur);
+    }
+    delete p;
+}
+
+int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
+                       int32_t grad_dtype, void* flat_grad, void* stream) {
+    if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");
+    if (!valid_dtype(grad_dtype)) return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16");
+    if (bucket < -1 || bucket >= p->n_buckets) {
+        return fail(ZERO_EINVAL, "bucket must be -1 or in [0, n_buckets)");
+    }
+    if (p->S > 0 && flat_grad == nullptr) return fail(ZERO_ENULL, "flat_grad is NULL");
+    if (!aligned16(flat_grad)) return fail(ZERO_EALIGN, "flat_grad must be 16-byte aligned");
+    int64_t s_first = 0, s_last = static_cast<int64_t>(p->segs.size());
+    if (bucket >= 0) {
+        s_first = p->bucket_seg_first[bucket];
+        s_last = p->bucket_seg_last[bucket];
+    }
+    if (s_last > s_first && grads == nullptr) return fail(ZERO_ENULL, "grads is NULL");
+    // pieces of this call: the bucket's segments, then the padding tail
+    std::vector<FlatPiece> pieces;
+    pieces.reserve(static_cast<size_t>(s_last - s_first) + 1);
+    for (int64_t s = s_first; s < s_last; ++s) {
+        const Segment& g = p->segs[s];
+        const void* src = grads[g.tensor];
+        if (src == nullptr) {
+            return fail(ZERO_ENULL, "grads[" + std::to_string(g.tensor) +
+                                        "] is NULL but the tensor has elements in this shard");
+        }
+        if ((reinterpret_cast<uintptr_t>(src) & 1u) != 0) {
+            return fail(ZERO_EALIGN, "grads[" + std::to_string(g.tensor) + "] is not 2-byte aligned");
+        }
+        // byte address of the source of flat element 0 (mod 2^64)
+        const uintptr_t base = reinterpret_cast<uintptr_t>(src) +
+                               2u * static_cast<uintptr_t>(g.tensor_off) -
+                               2u * static_cast<uintptr_t>(g.shard_off);
+        pieces.push_back(FlatPiece{g.shard_off, g.shard_off + g.numel, base});
+    }
+    if (p->S > p->real) pieces.push_back(FlatPiece{p->real, p->S, 0});
+    int rc = ensure_device(p);
+    if (rc != ZERO_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = timer_start(p, kTimerFlatten, s)) != ZERO_OK) return rc;
+    // launches of up to kMaxPiecesPerLaunch contiguous pieces each
+    size_t i = 0;
+    while (i < pieces.size()) {
+        size_t j = i + 1;
+        while (j < pieces.size() && j - i < static_cast<size_t>(kMaxPiecesPerLaunch) &&
+               pieces[j].begin == pieces[j - 1].end) {
+            ++j;
+        }
+        hipError_t e = launch_flatten(pieces.data() + i, static_cast<int>(j - i),
+                                      static_cast<uint16_t*>(flat_grad), p->dev.d_flag,
+                                      grad_dtype, p->dev.cu_count, s);
+        if (e != hipSuccess) return hip_fail(e, "flatten launch");
+        i = j;
+    }
+    if ((rc = timer_stop(p, kTimerFlatten, s)) != ZERO_OK) return rc;
+    // bookkeeping for the gate: which buckets reached this flat buffer
+    if (p->flattened_into != flat_grad || p->flattened_dtype != grad_dtype) {
+        std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
+        p->flatten_all_done = false;
+        p->flattened_into = flat_grad;
+        p->flattened_dtype = grad_dtype;
+    }
+    if (bucket < 0) {
+        p->flatten_all_done = true;
+    } else {
+        p->bucket_flattened[bucket] = 1;
+    }
+    return ZERO_OK;
+}
+
+int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, double loss_scale,
+                   const void* flat_grad, int32_t grad_dtype, float* master, float* exp_avg,
+                   float* exp_avg_sq, void* param, int64_t param_base, int64_t param_numel,
+                   int32_t param_dtype, void* stream) {
+    if (p == nullptr || hp == nullptr) return fail(ZERO_ENULL, "plan or hparams is NULL");
+    if (!valid_dtype(grad_dtype)) return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16");
+    if (step < 1) return fail(ZERO_EINVAL, "step must be >= 1");
+    if (!(std::isfinite(loss_scale) && loss_scale > 0)) {
+        return fail(ZERO_EINVAL, "loss_scale must be finite and > 0");
+    }
+    if (!(hp->lr >= 0 && std::isfinite(hp->lr)) || !(hp->beta1 >= 0 && hp->beta1 < 1) ||
+        !(hp->beta2 >= 0 && hp->beta2 < 1) || !(hp->eps > 0 && std::isfinite(hp->eps)) ||
+        !(hp->weight_decay >= 0 && std::isfinite(hp->weight_decay))) {
+        return fail(ZERO_EINVAL, "hyperparameters out of range (lr >= 0, 0 <= betas < 1, eps > 0, "
+                                 "weight_decay >= 0)");
+    }
+    if (p->S > 0 && (flat_grad == nullptr || master == nullptr || exp_avg == nullptr ||
+                     exp_avg_sq == nullptr)) {
+        return fail(ZERO_ENULL, "flat_grad, master, exp_avg and exp_avg_sq must be non-NULL");
+    }
+    if (!aligned16(flat_grad) || !aligned16(master) || !aligned16(exp_avg) ||
+        !aligned16(exp_avg_sq)) {
+        return fail(ZERO_EALIGN, "flat_grad, master, exp_avg and exp_avg_sq must be 16-byte aligned");
+    }
+    uint16_t* param0 = nullptr;
+    int rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
+    if (rc != ZERO_OK) return rc;
+    rc = ensure_device(p);
+    if (rc != ZERO_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    // host scalars: double, each rounded once to fp32
+    const double t = static_cast<double>(step);
+    AdamScalars sc;
+    sc.inv_scale = static_cast<float>(1.0 / loss_scale);
+    sc.b1 = static_cast<float>(hp->beta1);
+    sc.omb1 = static_cast<float>(1.0 - hp->beta1);
+    sc.b2 = static_cast<float>(hp->beta2);
+    sc.omb2 = static_cast<float>(1.0 - hp->beta2);
+    sc.step = static_cast<float>(hp->lr / (1.0 - std::pow(hp->beta1, t)));
+    sc.rsbc2 = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(hp->beta2, t)));
+    sc.eps = static_cast<float>(hp->eps);
+    sc.decay = hp->adamw ? static_cast<float>(1.0 - hp->lr * hp->weight_decay) : 1.0f;
+    sc.wd = static_cast<float>(hp->weight_decay);
+
+    // the gate needs every real gradient of this flat buffer tested
+    bool covered = p->flattened_into == flat_grad && p->flattened_dtype == grad_dtype;
+    if (covered && !p->flatten_all_done) {
+        for (int32_t b = 0; b < p->n_buckets && covered; ++b) {
+            if (p->bucket_seg_last[b] > p->bucket_seg_first[b] && !p->bucket_flattened[b]) {
+                covered = false;
+            }
+        }
+    }
+    if (!covered) {
+        if ((rc = timer_start(p, kTimerScan, s)) != ZERO_OK) return rc;
+        hipError_t e = launch_scan(static_cast<const uint16_t*>(flat_grad), p->S, p->dev.d_flag,
+                                   grad_dtype, p->dev.cu_count, s);
+        if (e != hipSuccess) return hip_fail(e, "scan launch");
+        if ((rc = timer_stop(p, kTimerScan, s)) != ZERO_OK) return rc;
+    }
+    if ((rc = timer_start(p, kTimerAdam, s)) != ZERO_OK) return rc;
+    hipError_t e = launch_adam(static_cast<const uint16_t*>(flat_grad), master, exp_avg,
+                               exp_avg_sq, param0, p->S, p->real, p->dev.d_flag, sc, grad_dtype,
+                               param_dtype, hp->adamw != 0, p->dev.cu_count, s);
+    if (e != hipSuccess) return hip_fail(e, "adam launch");
+    if ((rc = timer_stop(p, kTimerAdam, s)) != ZERO_OK) return rc;
+    e = hipMemcpyAsync(p->dev.h_flag, p->dev.d_flag, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "flag readback");
+    e = launch_flag_clear(p->dev.d_flag, s);
+    if (e != hipSuccess) return hip_fail(e, "flag clear");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
+    p->flatten_all_done = false;
+    p->flattened_into = nullptr;
+    return *p->dev.h_flag != 0 ? 1 : 0;
+}
+
+int zero_update_loss_scale(zero_scaler_t* sc, int32_t overflow) {
+    if (sc == nullptr) return fail(ZERO_ENULL, "scaler is NULL");
+    if (!(std::isfinite(sc->scale) && sc->scale > 0) ||
+        !(std::isfinite(sc->min_scale) && sc->min_scale > 0) ||
+        !(sc->backoff > 0 && sc->backoff <= 1) || !(std::isfinite(sc->growth) && sc->growth >= 1) ||
+        sc->window < 1 || sc->good_steps < 0) {
+        return fail(ZERO_EINVAL, "scaler fields out of range");
+    }
+    if (overflow) {
+        if (sc->dynamic) sc->scale = std::max(sc->scale * sc->backoff, sc->min_scale);
+        sc->good_steps = 0;
+        return ZERO_OK;
+    }
+    sc->good_steps += 1;
+    if (sc->dynamic && sc->good_steps >= sc->window) {
+        sc->scale *= sc->growth;
+        sc->good_steps = 0;
+    }
+    return ZERO_OK;
+}
+
+int zero_write_param_shard(zero_plan_t* p, const float* master, void* param, int64_t param_base,
+                           int64_t param_numel, int32_t param_dtype, void* stream) {
+    if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");
+    if (param == nullptr) return fail(ZERO_ENULL, "param is NULL");
+    if (p->real > 0 && master == nullptr) return fail(ZERO_ENULL, "master is NULL");
+    if (!aligned16(master)) return fail(ZERO_EALIGN, "master must be 16-byte aligned");
+    uint16_t* param0 = nullptr;
+    int rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
+    if (rc != ZERO_OK) return rc;
+    rc = ensure_device(p);
+    if (rc != ZERO_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = timer_start(p, kTimerWrite, s)) != ZERO_OK) return rc;
+    hipError_t e = launch_write_param(master, param0, p->real, param_dtype, p->dev.cu_count, s);
+    if (e != hipSuccess) return hip_fail(e, "write_param launch");
+    return timer_stop(p, kTimerWrite, s);
+}
+
+const char* zero_last_error(void) { return g_last_error.c_str(); }
+
+int zero_plan_set_timing(zero_plan_t* p, int32_t on) {
+    if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");
+    if (on) {
+        int rc = ensure_device(p);
+        if (rc != ZERO_OK) return rc;
+    }
+    p->dev.timing = on != 0;
+    for (int i = 0; i < kTimers; ++i) p->dev.timed[i] = false;
+    return ZERO_OK;
+}
+
+int zero_plan_kernel_ms(zero_plan_t* p, int32_t which, float* ms) {
+    if (p == nullptr || ms == nullptr) return fail(ZERO_ENULL, "plan or ms is NULL");
+    if (which < 0 || which >= kTimers) return fail(ZERO_EINVAL, "which must be in [0, 4)");
+    if (!p->dev.ready || !p->dev.timed[which]) {
+        return fail(ZERO_ESTATE, "that kernel has not run with timing enabled");
+    }
+    hipError_t e = hipEventSynchronize(p->dev.ev_stop[which]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    e = hipEventElapsedTime(ms, p->dev.ev_start[which], p->dev.ev_stop[which]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    return ZERO_OK;
+}
+
+}  // extern "C"
