@@ -184,8 +184,9 @@ int zero_flatten_grads(zero_plan_t* plan, int32_t bucket, const void* const* gra
  * and, if param != NULL, for k < real:
  *   param[shard_begin + k - param_base] = round_to_nearest_even_half(p)
  * step: the bias-correction step t >= 1 (count applied steps only).
- * loss_scale: finite, > 0.  master/exp_avg/exp_avg_sq: device fp32 arrays
- * of >= S elements, 16-byte aligned.  param: device buffer holding flat
+ * loss_scale: finite, > 0.  flat_grad: device, >= S elements, 16-byte
+ * aligned.  master/exp_avg/exp_avg_sq: device fp32 arrays of >= S
+ * elements, 4-byte aligned.  param: device buffer holding flat
  * indices [param_base, param_base + param_numel), which must contain
  * [shard_begin, shard_begin + real); 2-byte aligned.
  * Returns 0 applied, 1 skipped, or a negative error (ZERO_ENULL,

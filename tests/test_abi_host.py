@@ -124,7 +124,8 @@ def test_argument_errors_before_device_work():
     assert step(scale=float("inf")) == _abi.ZERO_EINVAL
     assert step(gdt=7) == _abi.ZERO_EINVAL
     assert step(g=None) == _abi.ZERO_ENULL
-    assert step(m=fake + 4) == _abi.ZERO_EALIGN
+    assert step(m=fake + 2) == _abi.ZERO_EALIGN
+    assert step(g=fake + 8) == _abi.ZERO_EALIGN
     bad_hp = z.AdamHParams(beta1=1.0).to_c()
     assert lib.zero_adam_step(plan.handle, ctypes.byref(bad_hp), 1, 1.0, fake, z.ZERO_BF16, fake,
                               fake, fake, None, 0, 0, 0, None) == _abi.ZERO_EINVAL
@@ -133,7 +134,7 @@ def test_argument_errors_before_device_work():
                               fake, fake, fake, 10, 100, z.ZERO_BF16, None) == _abi.ZERO_EINVAL
     assert lib.zero_write_param_shard(plan.handle, fake, fake, 0, 10, z.ZERO_BF16,
                                       None) == _abi.ZERO_EINVAL
-    assert lib.zero_write_param_shard(plan.handle, fake + 8, fake, 0, 1000, z.ZERO_BF16,
+    assert lib.zero_write_param_shard(plan.handle, fake + 2, fake, 0, 1000, z.ZERO_BF16,
                                       None) == _abi.ZERO_EALIGN
     ptrs = (ctypes.c_void_p * 1)(None)
     assert lib.zero_flatten_grads(plan.handle, 5, ptrs, z.ZERO_BF16, fake,

@@ -1,0 +1,188 @@
+"""GPU vs oracle parity at the workloads' full sizes, on sampled windows.
+
+The GPU runs the whole shard exactly as bench.py does (same library calls,
+same launch shapes).  The oracle recomputes fixed windows of the shard --
+its head and tail, +-2048 elements around every segment edge, +-64 around
+every injected +inf, and seeded random windows -- from the host generator;
+the update is elementwise, so a window evolves exactly as it does inside
+the whole shard.  The overflow decision is global: the windows contain every
+injected position, and the generator's support (|z| <= 2*sqrt(3)) keeps
+every other gradient finite, which the test asserts from the workload's
+constants, so the window's overflow test equals the whole shard's.
+
+Bar, after every step: flags, loss scale and applied-step counter equal;
+the flat gradient shard bit-identical on the windows; master / moments
+within 1e-6 relative error and parameters within 1 ulp on the windows at
+checkpoints (expected: identical bits).
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import zero_partitioned_mixed_plan_amd as z
+from harness import (INF_BITS, REL_TOL, ULP_TOL, Case, flat_offsets, grad_key, log, master_key,
+                     max_rel, torch_dtype, ulp_diff)
+from synth.workloads import get
+
+pytestmark = pytest.mark.gpu
+
+HALF_MAX = {"f16": 65504.0, "bf16": 3.3895313892515355e38}
+
+
+def _windows(op, case, n_random=8, rnd_len=32768, seed=1):
+    S, real = op.S, op.real
+    ranges = [(0, 4096), (max(real - 4096, 0), S)]
+    for so in op.seg_shard_off.tolist():
+        ranges.append((so - 2048, so + 2048))
+    for it in range(1, case.steps + 1):
+        pos = case.injection(it, real)
+        if pos is not None:
+            ranges.append((pos - 64, pos + 64))
+    rng = np.random.default_rng(seed)
+    for _ in range(n_random):
+        a = int(rng.integers(0, max(S - rnd_len, 1)))
+        ranges.append((a, a + rnd_len))
+    ranges = sorted((max(0, a), min(S, b)) for a, b in ranges if min(S, b) > max(0, a))
+    merged = []
+    for a, b in ranges:
+        if merged and a <= merged[-1][1]:
+            merged[-1] = (merged[-1][0], max(merged[-1][1], b))
+        else:
+            merged.append((a, b))
+    idx = np.concatenate([np.arange(a, b, dtype=np.int64) for a, b in merged])
+    return merged, idx
+
+
+def _run_sampled(case, check_at, flatten_mode="all", label=""):
+    import torch
+    dev = torch.device("cuda:0")
+    gdt, pdt = torch_dtype(case.grad_dtype), torch_dtype(case.param_dtype)
+    # finite by construction: the largest gradient the generator can draw
+    bound = case.grad_sigma * 2 * np.sqrt(3) * 1.0001 * max(case.outlier_mult, 1.0) * \
+        max(case.init_scale, 1.0)
+    assert bound < HALF_MAX[case.grad_dtype]
+
+    op = oracle.plan(case.numels, case.world_size, case.rank, case.align, case.bucket_elems)
+    plan = z.zero_partition_plan(case.numels, case.world_size, case.rank, case.align,
+                                 case.bucket_elems)
+    assert (plan.S, plan.begin, plan.real, plan.n_segments) == (op.S, op.begin, op.real,
+                                                               op.n_segments)
+    S, real, begin = op.S, op.real, op.begin
+    windows, idx = _windows(op, case)
+    log(f"[full] {label}: S={S} real={real} segments={op.n_segments} windows={len(windows)} "
+        f"sampled={idx.size}")
+    offs = flat_offsets(case.numels)
+
+    # ---- GPU state (whole shard)
+    master = torch.empty(S, dtype=torch.float32, device=dev)
+    master[real:].zero_()
+    synth.dev_fill_f32(master[:real], master_key(case), begin, case.master_sigma)
+    mom = torch.zeros(S, dtype=torch.float32, device=dev)
+    var = torch.zeros(S, dtype=torch.float32, device=dev)
+    flat = torch.empty(S, dtype=gdt, device=dev)
+    param = torch.full((max(real, 1),), float("nan"), dtype=pdt, device=dev)
+    grads = [None] * len(case.numels)
+    for s in range(op.n_segments):
+        t = int(op.seg_tensor[s])
+        if grads[t] is None:
+            grads[t] = torch.empty(case.numels[t], dtype=gdt, device=dev)
+    hp = z.AdamHParams(case.lr, case.beta1, case.beta2, case.eps, case.weight_decay, case.adamw)
+    g_scaler = z.LossScaler(case.init_scale, dynamic=case.dynamic, window=case.window)
+    tb = plan.tensor_buckets()
+    d_idx = torch.from_numpy(idx).to(dev)
+
+    # ---- oracle state (windows)
+    in_real = idx < real
+    o_master = np.zeros(idx.size, np.float32)
+    o_master[in_real] = synth.host_gather(master_key(case), begin + idx[in_real],
+                                          case.master_sigma)
+    o_m = np.zeros(idx.size, np.float32)
+    o_v = np.zeros(idx.size, np.float32)
+    o_scaler = oracle.Scaler(case.init_scale, dynamic=case.dynamic, window=case.window)
+    g_t = o_t = 0
+    othresh = synth.outlier_thresh(case.outlier_p)
+    skipped = 0
+    for it in range(1, case.steps + 1):
+        scale = o_scaler.value
+        assert g_scaler.scale == scale, f"{label} it={it}: scale {g_scaler.scale} vs {scale}"
+        key = grad_key(case, it)
+        pos = case.injection(it, real)
+        # GPU inputs: every segment of the shard, drawn on the device
+        for s in range(op.n_segments):
+            t, a, n = int(op.seg_tensor[s]), int(op.seg_tensor_off[s]), int(op.seg_numel[s])
+            synth.dev_fill_half(grads[t][a:a + n], key, int(offs[t]) + a, case.grad_sigma, scale,
+                                othresh, case.outlier_mult)
+        if pos is not None:
+            s = int(np.searchsorted(op.seg_shard_off, pos, side="right") - 1)
+            t = int(op.seg_tensor[s])
+            grads[t][int(op.seg_tensor_off[s] + pos - op.seg_shard_off[s])] = float("inf")
+        if flatten_mode == "buckets":
+            for b in range(plan.n_buckets):
+                z.zero_flatten_grads(plan, b, [g if (g is not None and tb[i] == b) else None
+                                               for i, g in enumerate(grads)], flat)
+        else:
+            z.zero_flatten_grads(plan, -1, grads, flat)
+        g_ovf = z.zero_adam_step(plan, hp, g_t + 1, scale, flat, master, mom, var, param, begin)
+        z.zero_update_loss_scale(g_scaler, g_ovf)
+        # oracle inputs: the same values at the window positions, from the host
+        vals = np.zeros(idx.size, np.float32)
+        vals[in_real] = synth.host_gather(key, begin + idx[in_real], case.grad_sigma, scale,
+                                          othresh, case.outlier_mult)
+        o_flat = synth.half_bits(vals, case.grad_dtype)
+        o_flat[~in_real] = 0
+        if pos is not None:
+            o_flat[np.searchsorted(idx, pos)] = INF_BITS[case.grad_dtype]
+        o_ovf = oracle.adam_step(o_t + 1, scale, o_flat, case.grad_dtype, o_master, o_m, o_v,
+                                 **case.hparams())
+        o_scaler.update(o_ovf)
+        assert g_ovf == o_ovf, f"{label} it={it}: overflow {g_ovf} vs oracle {o_ovf}"
+        g_t += 1 - g_ovf
+        o_t += 1 - o_ovf
+        skipped += o_ovf
+        got_flat = flat.index_select(0, d_idx).view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got_flat, o_flat), f"{label} it={it}: flat shard differs"
+        if it in check_at or it == case.steps:
+            gm = master.index_select(0, d_idx).cpu().numpy()
+            gmo = mom.index_select(0, d_idx).cpu().numpy()
+            gv = var.index_select(0, d_idx).cpu().numpy()
+            for name, a, b in (("master", gm, o_master), ("m", gmo, o_m), ("v", gv, o_v)):
+                err = max_rel(a, b)
+                assert err <= REL_TOL, f"{label} it={it}: {name} max rel err {err}"
+                assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), \
+                    f"{label} it={it}: {name} not bit-identical (err {err})"
+            if o_t > 0:
+                ridx = d_idx[torch.from_numpy(in_real).to(dev)]
+                gp = param.index_select(0, ridx).view(torch.int16).cpu().numpy().view(np.uint16)
+                op_bits = oracle.float_to_half(o_master[in_real], case.param_dtype)
+                du = ulp_diff(gp, op_bits)
+                assert du <= ULP_TOL, f"{label} it={it}: params differ by {du} ulp"
+            log(f"[full] {label}: it={it} t={o_t} scale={scale} ok")
+    log(f"[full] {label}: done, skipped {skipped} of {case.steps}")
+    del master, mom, var, flat, param, grads, d_idx
+    gc.collect()
+    torch.cuda.empty_cache()
+    return skipped
+
+
+def test_llama3_8b_rank3_bucketed_flatten():
+    case = Case.from_workload(get("llama3_8b"))
+    _run_sampled(case, check_at={1, 5, 10}, flatten_mode="buckets", label="llama3_8b")
+
+
+def test_dna_20b_rank2_dynamic_scale_with_injected_overflows():
+    case = Case.from_workload(get("dna_20b"))
+    skipped = _run_sampled(case, check_at={1, 10, 25}, label="dna_20b")
+    expect = sum(case.injection(it, 2_498_481_408) is not None for it in range(1, case.steps + 1))
+    assert skipped == expect and skipped >= 1
+
+
+def test_llama2_70b_rank7_full_shard():
+    import torch
+    free, _ = torch.cuda.mem_get_info()
+    if free < 170e9:
+        pytest.skip(f"needs ~160 GB of free device memory, {free / 1e9:.0f} GB free")
+    case = Case.from_workload(get("llama2_70b"))
+    _run_sampled(case, check_at={1, 3}, label="llama2_70b")

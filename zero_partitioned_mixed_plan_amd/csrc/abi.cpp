@@ -30,6 +30,8 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 bool valid_dtype(int32_t d) { return d == ZERO_F16 || d == ZERO_BF16; }
 
 // Binds the plan to the current device on first use and creates its flag.
@@ -45,8 +47,6 @@ int ensure_device(zero_plan* p) {
         }
         return ZERO_OK;
     }
-    e = hipDeviceGetAttribute(&d.cu_count, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     e = hipMalloc(reinterpret_cast<void**>(&d.d_flag), 256);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(flag)");
     e = hipHostMalloc(reinterpret_cast<void**>(&d.h_flag), sizeof(int), hipHostMallocDefault);
@@ -242,7 +242,7 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
         }
         hipError_t e = launch_flatten(pieces.data() + i, static_cast<int>(j - i),
                                       static_cast<uint16_t*>(flat_grad), p->dev.d_flag,
-                                      grad_dtype, p->dev.cu_count, s);
+                                      grad_dtype, s);
         if (e != hipSuccess) return hip_fail(e, "flatten launch");
         i = j;
     }
@@ -282,9 +282,9 @@ int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, 
                      exp_avg_sq == nullptr)) {
         return fail(ZERO_ENULL, "flat_grad, master, exp_avg and exp_avg_sq must be non-NULL");
     }
-    if (!aligned16(flat_grad) || !aligned16(master) || !aligned16(exp_avg) ||
-        !aligned16(exp_avg_sq)) {
-        return fail(ZERO_EALIGN, "flat_grad, master, exp_avg and exp_avg_sq must be 16-byte aligned");
+    if (!aligned16(flat_grad)) return fail(ZERO_EALIGN, "flat_grad must be 16-byte aligned");
+    if (!aligned4(master) || !aligned4(exp_avg) || !aligned4(exp_avg_sq)) {
+        return fail(ZERO_EALIGN, "master, exp_avg and exp_avg_sq must be 4-byte aligned");
     }
     uint16_t* param0 = nullptr;
     int rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
@@ -319,14 +319,14 @@ int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, 
     if (!covered) {
         if ((rc = timer_start(p, kTimerScan, s)) != ZERO_OK) return rc;
         hipError_t e = launch_scan(static_cast<const uint16_t*>(flat_grad), p->S, p->dev.d_flag,
-                                   grad_dtype, p->dev.cu_count, s);
+                                   grad_dtype, s);
         if (e != hipSuccess) return hip_fail(e, "scan launch");
         if ((rc = timer_stop(p, kTimerScan, s)) != ZERO_OK) return rc;
     }
     if ((rc = timer_start(p, kTimerAdam, s)) != ZERO_OK) return rc;
     hipError_t e = launch_adam(static_cast<const uint16_t*>(flat_grad), master, exp_avg,
                                exp_avg_sq, param0, p->S, p->real, p->dev.d_flag, sc, grad_dtype,
-                               param_dtype, hp->adamw != 0, p->dev.cu_count, s);
+                               param_dtype, hp->adamw != 0, s);
     if (e != hipSuccess) return hip_fail(e, "adam launch");
     if ((rc = timer_stop(p, kTimerAdam, s)) != ZERO_OK) return rc;
     e = hipMemcpyAsync(p->dev.h_flag, p->dev.d_flag, sizeof(int), hipMemcpyDeviceToHost, s);
@@ -367,7 +367,7 @@ int zero_write_param_shard(zero_plan_t* p, const float* master, void* param, int
     if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");
     if (param == nullptr) return fail(ZERO_ENULL, "param is NULL");
     if (p->real > 0 && master == nullptr) return fail(ZERO_ENULL, "master is NULL");
-    if (!aligned16(master)) return fail(ZERO_EALIGN, "master must be 16-byte aligned");
+    if (!aligned4(master)) return fail(ZERO_EALIGN, "master must be 4-byte aligned");
     uint16_t* param0 = nullptr;
     int rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
     if (rc != ZERO_OK) return rc;
@@ -375,7 +375,7 @@ int zero_write_param_shard(zero_plan_t* p, const float* master, void* param, int
     if (rc != ZERO_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = timer_start(p, kTimerWrite, s)) != ZERO_OK) return rc;
-    hipError_t e = launch_write_param(master, param0, p->real, param_dtype, p->dev.cu_count, s);
+    hipError_t e = launch_write_param(master, param0, p->real, param_dtype, s);
     if (e != hipSuccess) return hip_fail(e, "write_param launch");
     return timer_stop(p, kTimerWrite, s);
 }

@@ -31,7 +31,6 @@ enum Timer { kTimerFlatten = 0, kTimerScan = 1, kTimerAdam = 2, kTimerWrite = 3,
 struct DeviceState {
     bool ready = false;
     int device = -1;
-    int cu_count = 0;
     int* d_flag = nullptr;      // device overflow flag (256 B allocation)
     int* h_flag = nullptr;      // pinned host mirror
     bool timing = false;
@@ -84,14 +83,13 @@ struct AdamScalars {
 };
 
 hipError_t launch_flatten(const FlatPiece* pieces, int n, uint16_t* flat, int* flag,
-                          int grad_dtype, int cu_count, hipStream_t s);
-hipError_t launch_scan(const uint16_t* flat, int64_t n, int* flag, int grad_dtype, int cu_count,
-                       hipStream_t s);
+                          int grad_dtype, hipStream_t s);
+hipError_t launch_scan(const uint16_t* flat, int64_t n, int* flag, int grad_dtype, hipStream_t s);
 hipError_t launch_adam(const uint16_t* g, float* master, float* m, float* v, uint16_t* param_at_0,
                        int64_t S, int64_t real, const int* flag, const AdamScalars& sc,
-                       int grad_dtype, int param_dtype, bool adamw, int cu_count, hipStream_t s);
+                       int grad_dtype, int param_dtype, bool adamw, hipStream_t s);
 hipError_t launch_write_param(const float* master, uint16_t* param_at_0, int64_t real,
-                              int param_dtype, int cu_count, hipStream_t s);
+                              int param_dtype, hipStream_t s);
 hipError_t launch_flag_clear(int* flag, hipStream_t s);
 
 }  // namespace zmi
