@@ -12,8 +12,10 @@ Prints one JSON line.  ``value`` is shard parameters updated per second over
 the timed steps (wall clock, synchronized on both sides).  ``roofline``
 prices the fused Adam kernel at 28 algorithmic bytes per shard element
 against 8 TB/s, from HIP events recorded around the kernel on its launch
-stream.  ``cpu_baseline`` times the oracle (single thread) on a bounded
-window of the same shard.
+stream; its ``traffic`` is the counter-measured HBM bytes per launch from
+the committed rocprofv3 summary under profiles/, reported only while the
+kernel source is the one that summary measured.  ``cpu_baseline`` times the
+oracle (single thread) on a bounded window of the same shard.
 """
 from __future__ import annotations
 
@@ -171,6 +173,29 @@ def cpu_baseline(w, plan_S, plan_begin, target_s=12.0, window=1 << 24):
             "gbps_equiv": rate * (ADAM_BYTES_PER_ELEM + FLATTEN_BYTES_PER_ELEM) / 1e9}
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "adam_fused_llama2_70b_rank7_hbm_counters.md")
+KERNELS_SRC = os.path.join(ROOT, "zero_partitioned_mixed_plan_amd", "csrc", "kernels.hip")
+
+
+def counted_traffic(workload_name):
+    """HBM bytes per launch of the update kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (copy-calibrated), or None when that
+    summary is for another workload or the kernels have changed since."""
+    import hashlib
+    import re
+    try:
+        text = open(COUNTERS_FILE).read()
+        src = open(KERNELS_SRC, "rb").read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^(\w+) = (\S+)$", text, flags=re.M))
+    if vals.get("workload") != workload_name:
+        return None
+    if vals.get("kernels_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
 def copy_probe(nbytes, reps, device):
     """A plain device copy of known size (for scaling the HBM byte counters)."""
     import torch
@@ -247,7 +272,7 @@ def main(argv=None):
         },
         "skipped_steps": state["skipped"],
         "roofline": {"bound": "hbm", "achieved": adam_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": adam_gbs / HBM_PEAK_GBS, "traffic": None},
+                     "frac": adam_gbs / HBM_PEAK_GBS, "traffic": counted_traffic(w.name)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

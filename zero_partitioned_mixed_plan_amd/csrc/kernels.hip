@@ -2,17 +2,33 @@
 // fused unscale + Adam/AdamW + half cast, and the standalone parameter cast.
 //
 // All four are streaming, memory-bound kernels (no contraction, so no
-// MFMA).  Launch shape, chosen by measurement on MI355X:
-//   * exact-cover grids: every 256-thread workgroup (four 64-wide waves)
-//     handles one fixed piece of the shard and exits, so the hardware
-//     dispatcher walks memory in address order.  Grid-stride loops over a
-//     CU-sized grid reached ~5.0 TB/s on the update; exact cover ~6.3 TB/s.
-//   * the update and the parameter cast take ONE element per thread (2- and
-//     4-byte accesses, 128-256 contiguous bytes per wave instruction): with
-//     four read and four write streams this beat 8 elements per thread with
-//     16-byte accesses by ~15% (5.3 -> 6.2 TB/s on random data).
-//   * flatten and scan (one read and at most one write stream) take one
-//     16-byte vector (8 halves) per thread, like a plain copy.
+// MFMA).  Launch shape and cache policy, chosen by measurement on MI355X
+// (2^31-element buffers, HIP events):
+//   * exact-cover grids: every workgroup handles one fixed piece of the
+//     shard and exits, so the hardware dispatcher walks memory in address
+//     order.  Grid-stride loops over a CU-sized grid reached ~5.0 TB/s on
+//     the update; exact cover ~6.2 TB/s.  Remapping workgroups so that each
+//     XCD streams its own contiguous range (whole-range or 16..4096-block
+//     chunks) was 1-10% slower than plain address order.
+//   * the update uses 2- and 4-byte accesses (128-256 contiguous bytes per
+//     wave instruction), not 8- or 16-byte vectors: with four read and four
+//     write streams, vector accesses were 5-15% slower.  On a 70B-class
+//     shard (8.6e9 elements) the best shape was 128-thread workgroups with
+//     two elements per thread, t and t + 128, both loaded before the math:
+//     36.9 ms vs 37.5 ms for 256 threads x 1 element and 38.2 ms for
+//     64 x 2 or 256 x 4.
+//   * non-temporal loads and stores (the streaming cache policy) on the
+//     three fp32 state arrays, plain accesses for the half gradient and
+//     parameter: +3-6% on the update.  Every byte of the state is touched
+//     exactly once per step, so nothing is lost by not keeping it cached.
+//   * flatten and scan (one read and at most one write stream) move 16-byte
+//     vectors (8 halves), like a plain copy, with non-temporal stores, and
+//     non-temporal loads where the source is 16-byte aligned (copy 6.19 ->
+//     6.44 TB/s, read 6.81 -> 7.07).  A flatten workgroup first searches
+//     the launch's piece table for its tile (a short chain of dependent
+//     scalar loads); two vectors per thread (4096-element tiles) amortise
+//     that better than one or four (-3% flatten time on a 70B-class shard,
+//     -5% on a shard of 300 mostly misaligned pieces).
 //   * grids are 2-D (x up to 65536 workgroups) because a 1-D grid is limited
 //     to 2^32 work-items and a 70B-class shard has more elements than that;
 //     workgroup id = blockIdx.y * gridDim.x + blockIdx.x keeps address order.
@@ -25,11 +41,20 @@
 namespace zmi {
 namespace {
 
+// 16 bytes as a native vector (the non-temporal builtins take these, not
+// HIP's uint4 wrapper struct).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kVec = 8;                     // halves per 16-byte access
-constexpr int64_t kTile = kThreads * kVec;  // flatten / scan tile: 2048 elements
+constexpr int64_t kTile = kThreads * kVec;  // scan tile: 2048 elements
+constexpr int kFlatV = 2;                   // 16-byte vectors per thread in flatten
+constexpr int64_t kFlatTile = kTile * kFlatV;  // flatten tile: 4096 elements
 constexpr int64_t kGridX = 65536;           // x extent of the 2-D grids
+constexpr int kAdamThreads = 128;           // update: two waves per workgroup,
+constexpr int kAdamPer = 2;                 // two elements per thread,
+constexpr int64_t kAdamSpan = kAdamThreads * kAdamPer;  // 256 elements per workgroup
 
 __device__ __forceinline__ int64_t block_id() {
     return static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
@@ -58,7 +83,7 @@ __device__ __forceinline__ int word_nonfinite(uint32_t w) {
 }
 
 template <int DT>
-__device__ __forceinline__ bool vec_nonfinite(const uint4& q) {
+__device__ __forceinline__ bool vec_nonfinite(const u32x4& q) {
     return (word_nonfinite<DT>(q.x) | word_nonfinite<DT>(q.y) | word_nonfinite<DT>(q.z) |
             word_nonfinite<DT>(q.w)) != 0;
 }
@@ -94,7 +119,7 @@ __device__ __forceinline__ void raise_flag_if_any(bool bad, int* flag) {
 
 // ------------------------------------------------------------ flatten
 struct FlattenArgs {
-    int64_t tile_first;  // tile t covers flat [t*kTile, (t+1)*kTile)
+    int64_t tile_first;  // tile t covers flat [t*kFlatTile, (t+1)*kFlatTile)
     int64_t n_tiles;
     int32_t n;           // pieces, sorted by begin, disjoint
     int32_t _pad;
@@ -106,7 +131,7 @@ struct FlattenArgs {
 
 // 16 source bytes starting MIS bytes into the aligned pair (a, b).
 template <int MIS>
-__device__ __forceinline__ uint4 realign(const uint4& a, const uint4& b) {
+__device__ __forceinline__ u32x4 realign(const u32x4& a, const u32x4& b) {
     const uint32_t c[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     constexpr int q = MIS / 4;
     constexpr int r = MIS % 4;
@@ -115,37 +140,65 @@ __device__ __forceinline__ uint4 realign(const uint4& a, const uint4& b) {
     for (int j = 0; j < 4; ++j) {
         o[j] = r == 0 ? c[q + j] : __builtin_amdgcn_alignbyte(c[q + j + 1], c[q + j], r);
     }
-    return make_uint4(o[0], o[1], o[2], o[3]);
+    return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-__device__ __forceinline__ uint4 load_src16(uint64_t addr) {
-    const uint32_t mis = static_cast<uint32_t>(addr & 15u);  // uniform per piece
-    const uint4* p = reinterpret_cast<const uint4*>(addr - mis);
-    if (mis == 0) return p[0];
-    // Both aligned 16-byte blocks hold wanted elements, so neither read
-    // leaves the source allocation.
-    const uint4 a = p[0];
-    const uint4 b = p[1];
+// Pointers into global memory built from byte addresses (the compiler
+// cannot infer the address space of an integer, and generic "flat"
+// accesses cost more than global ones).
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* global_ptr(uint64_t addr) {
+    return reinterpret_cast<const __attribute__((address_space(1))) T*>(addr);
+}
+
+// The kFlatV 16-byte source vectors of this lane in a full tile whose
+// element 0 is read from byte address src0 (uniform over the workgroup);
+// vector j of lane t starts at src0 + 16 (t + j * kThreads).  An aligned
+// source is read with the streaming (non-temporal) policy.  A misaligned
+// one is read as two aligned blocks per vector, each block also read by the
+// neighbouring lane: plain loads keep that second read a cache hit
+// (non-temporal loads cost ~9% there).  Both blocks hold wanted elements of
+// the tile, so no read leaves the source allocation.
+template <int MIS>
+__device__ __forceinline__ void load_tile_mis(const __attribute__((address_space(1))) u32x4* blk,
+                                              u32x4 (&q)[kFlatV]) {
+    u32x4 lo[kFlatV], hi[kFlatV];
+#pragma unroll
+    for (int j = 0; j < kFlatV; ++j) {
+        lo[j] = blk[j * kThreads];
+        hi[j] = blk[j * kThreads + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kFlatV; ++j) q[j] = realign<MIS>(lo[j], hi[j]);
+}
+
+__device__ __forceinline__ void load_tile(uint64_t src0, u32x4 (&q)[kFlatV]) {
+    const uint32_t mis = static_cast<uint32_t>(src0 & 15u);
+    const auto* blk = global_ptr<u32x4>(src0 - mis) + threadIdx.x;
     switch (mis) {
-        case 2: return realign<2>(a, b);
-        case 4: return realign<4>(a, b);
-        case 6: return realign<6>(a, b);
-        case 8: return realign<8>(a, b);
-        case 10: return realign<10>(a, b);
-        case 12: return realign<12>(a, b);
-        default: return realign<14>(a, b);
+        case 0:
+#pragma unroll
+            for (int j = 0; j < kFlatV; ++j) q[j] = __builtin_nontemporal_load(blk + j * kThreads);
+            return;
+        case 2: return load_tile_mis<2>(blk, q);
+        case 4: return load_tile_mis<4>(blk, q);
+        case 6: return load_tile_mis<6>(blk, q);
+        case 8: return load_tile_mis<8>(blk, q);
+        case 10: return load_tile_mis<10>(blk, q);
+        case 12: return load_tile_mis<12>(blk, q);
+        default: return load_tile_mis<14>(blk, q);
     }
 }
 
-// One workgroup per 2048-element tile of the flat shard.
+// One workgroup per kFlatTile-element tile of the flat shard.
 template <int DT>
 __global__ void __launch_bounds__(kThreads)
 flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict__ flag) {
     const int64_t blk = block_id();
     if (blk >= a.n_tiles) return;  // the whole workgroup leaves together
     bool bad = false;
-    const int64_t lo = (a.tile_first + blk) * kTile;
-    const int64_t hi = lo + kTile;
+    const int64_t lo = (a.tile_first + blk) * kFlatTile;
+    const int64_t hi = lo + kFlatTile;
     // first piece ending after lo
     int pl = 0, ph = a.n;
     while (pl < ph) {
@@ -154,15 +207,20 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
     }
     int p = pl;
     if (p < a.n && a.begin[p] <= lo && a.end[p] >= hi) {
-        // whole tile inside one piece: 8 elements per thread, 16-byte
-        // aligned stores, realigned 16-byte loads
-        const int64_t d0 = lo + static_cast<int64_t>(threadIdx.x) * kVec;
-        uint4 q = make_uint4(0u, 0u, 0u, 0u);
+        // whole tile inside one piece: kFlatV x 8 elements per thread,
+        // 16-byte aligned stores, realigned 16-byte loads
+        u32x4 q[kFlatV];
         if (!((a.zero_mask >> p) & 1ull)) {
-            q = load_src16(a.src[p] + 2ull * static_cast<uint64_t>(d0));
-            bad = vec_nonfinite<DT>(q);
+            load_tile(a.src[p] + 2ull * static_cast<uint64_t>(lo), q);
+#pragma unroll
+            for (int j = 0; j < kFlatV; ++j) bad |= vec_nonfinite<DT>(q[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kFlatV; ++j) q[j] = u32x4{0u, 0u, 0u, 0u};
         }
-        *reinterpret_cast<uint4*>(flat + d0) = q;
+        auto* dst = reinterpret_cast<u32x4*>(flat + lo) + threadIdx.x;
+#pragma unroll
+        for (int j = 0; j < kFlatV; ++j) __builtin_nontemporal_store(q[j], dst + j * kThreads);
     } else {
         // tile crosses piece edges: element-wise, coalesced per piece
         for (; p < a.n && a.begin[p] < hi; ++p) {
@@ -172,8 +230,7 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
             for (int64_t d = s0 + threadIdx.x; d < s1; d += kThreads) {
                 uint32_t h = 0;
                 if (!zero) {
-                    h = *reinterpret_cast<const uint16_t*>(a.src[p] +
-                                                           2ull * static_cast<uint64_t>(d));
+                    h = *global_ptr<uint16_t>(a.src[p] + 2ull * static_cast<uint64_t>(d));
                     bad |= half_nonfinite<DT>(h);
                 }
                 flat[d] = static_cast<uint16_t>(h);
@@ -193,7 +250,8 @@ scan_kernel(const uint16_t* __restrict__ flat, int64_t n, int* __restrict__ flag
     const int64_t k0 = blk * kTile + static_cast<int64_t>(threadIdx.x) * kVec;
     bool bad = false;
     if (k0 + kVec <= n) {
-        bad = vec_nonfinite<DT>(*reinterpret_cast<const uint4*>(flat + k0));
+        bad = vec_nonfinite<DT>(
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(flat + k0)));
     } else {
         for (int64_t k = k0; k < n; ++k) bad |= half_nonfinite<DT>(flat[k]);
     }
@@ -217,21 +275,39 @@ __device__ __forceinline__ void adam_elem(float g, float& p, float& m, float& v,
 }
 
 // GDT: gradient dtype.  PDT: parameter dtype, 0 = no parameter write.
-// One shard element per thread.
+// A 128-thread workgroup (two waves) updates kAdamSpan = 256 consecutive
+// elements; thread t takes elements t and t + 128 and issues the loads of
+// both before any arithmetic.
 template <int GDT, int PDT, bool ADAMW>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kAdamThreads)
 adam_kernel(const uint16_t* __restrict__ g, float* __restrict__ master, float* __restrict__ mom,
             float* __restrict__ var, uint16_t* __restrict__ param, int64_t S, int64_t real,
             const int* __restrict__ flag, const AdamScalars c) {
     if (*flag != 0) return;  // overflow: the step is skipped, nothing is written
-    const int64_t k = block_id() * kThreads + threadIdx.x;
-    if (k >= S) return;
-    float p = master[k], m = mom[k], v = var[k];
-    adam_elem<ADAMW>(half_to_f32<GDT>(g[k]), p, m, v, c);
-    master[k] = p;
-    mom[k] = m;
-    var[k] = v;
-    if (PDT != 0 && k < real) param[k] = f32_to_half<PDT>(p);
+    const int64_t k0 = block_id() * kAdamSpan + threadIdx.x;
+    float p[kAdamPer], m[kAdamPer], v[kAdamPer];
+    uint32_t h[kAdamPer];
+#pragma unroll
+    for (int j = 0; j < kAdamPer; ++j) {
+        const int64_t k = k0 + j * kAdamThreads;
+        if (k < S) {
+            p[j] = __builtin_nontemporal_load(master + k);
+            m[j] = __builtin_nontemporal_load(mom + k);
+            v[j] = __builtin_nontemporal_load(var + k);
+            h[j] = g[k];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kAdamPer; ++j) {
+        const int64_t k = k0 + j * kAdamThreads;
+        if (k < S) {
+            adam_elem<ADAMW>(half_to_f32<GDT>(h[j]), p[j], m[j], v[j], c);
+            __builtin_nontemporal_store(p[j], master + k);
+            __builtin_nontemporal_store(m[j], mom + k);
+            __builtin_nontemporal_store(v[j], var + k);
+            if (PDT != 0 && k < real) param[k] = f32_to_half<PDT>(p[j]);
+        }
+    }
 }
 
 // ------------------------------------------------------------ param cast
@@ -239,7 +315,7 @@ template <int PDT>
 __global__ void __launch_bounds__(kThreads)
 write_param_kernel(const float* __restrict__ master, uint16_t* __restrict__ param, int64_t real) {
     const int64_t k = block_id() * kThreads + threadIdx.x;
-    if (k < real) param[k] = f32_to_half<PDT>(master[k]);
+    if (k < real) param[k] = f32_to_half<PDT>(__builtin_nontemporal_load(master + k));
 }
 
 __global__ void flag_clear_kernel(int* flag) { *flag = 0; }
@@ -249,10 +325,10 @@ hipError_t adam_dispatch_w(bool adamw, dim3 grid, hipStream_t s, const uint16_t*
                            float* m, float* v, uint16_t* param, int64_t S, int64_t real,
                            const int* flag, const AdamScalars& sc) {
     if (adamw) {
-        hipLaunchKernelGGL((adam_kernel<GDT, PDT, true>), grid, dim3(kThreads), 0, s, g, master,
+        hipLaunchKernelGGL((adam_kernel<GDT, PDT, true>), grid, dim3(kAdamThreads), 0, s, g, master,
                            m, v, param, S, real, flag, sc);
     } else {
-        hipLaunchKernelGGL((adam_kernel<GDT, PDT, false>), grid, dim3(kThreads), 0, s, g, master,
+        hipLaunchKernelGGL((adam_kernel<GDT, PDT, false>), grid, dim3(kAdamThreads), 0, s, g, master,
                            m, v, param, S, real, flag, sc);
     }
     return hipGetLastError();
@@ -289,8 +365,8 @@ hipError_t launch_flatten(const FlatPiece* pieces, int n, uint16_t* flat, int* f
         if (pieces[i].src_base == 0) a.zero_mask |= 1ull << i;
     }
     const int64_t lo = pieces[0].begin, hi = pieces[n - 1].end;
-    a.tile_first = lo / kTile;
-    a.n_tiles = (hi + kTile - 1) / kTile - a.tile_first;
+    a.tile_first = lo / kFlatTile;
+    a.n_tiles = (hi + kFlatTile - 1) / kFlatTile - a.tile_first;
     if (a.n_tiles <= 0) return hipSuccess;
     const dim3 grid = grid_2d(a.n_tiles);
     if (grad_dtype == ZERO_F16) {
@@ -316,7 +392,7 @@ hipError_t launch_adam(const uint16_t* g, float* master, float* m, float* v, uin
                        int64_t S, int64_t real, const int* flag, const AdamScalars& sc,
                        int grad_dtype, int param_dtype, bool adamw, hipStream_t s) {
     if (S <= 0) return hipSuccess;
-    const dim3 grid = grid_2d((S + kThreads - 1) / kThreads);
+    const dim3 grid = grid_2d((S + kAdamSpan - 1) / kAdamSpan);
     if (grad_dtype == ZERO_F16) {
         return adam_dispatch_p<ZERO_F16>(param_dtype, adamw, grid, s, g, master, m, v, param_at_0,
                                          S, real, flag, sc);
