@@ -18,20 +18,29 @@
  *   zero_update_loss_scale  dynamic loss-scale policy (host only)
  *   zero_write_param_shard  fp32 master shard -> half params at its offset
  *
+ * and the same step without host round trips, for HIP graph capture:
+ *   zero_state_upload       step count and loss scaler -> device state
+ *   zero_adam_step_async    gated update + cast + loss-scale policy, all on
+ *                           the device state; never waits
+ *   zero_state_download     device state -> host (waits)
+ *   zero_state_device_scale device address of the current loss scale
+ *
  * Conventions
  *   Errors   every call returns an int: 0 (ZERO_OK) or a negative ZERO_E*
  *            code; zero_adam_step returns 0 (applied) or 1 (overflow,
  *            skipped).  A message for the last error of the calling thread
  *            is available from zero_last_error().
  *   Memory   the caller allocates and owns every device buffer and stream.
- *            The plan owns only its host tables, a 4-byte device overflow
- *            flag and a 4-byte pinned host mirror, created on the first
- *            device call and released by zero_plan_destroy.  Buffers are
- *            not retained between calls.
+ *            The plan owns only its host tables, a 256-byte device block
+ *            (overflow flag, asynchronous step state, update scalars) and
+ *            its pinned host mirror, created on the first device call and
+ *            released by zero_plan_destroy.  Buffers are not retained
+ *            between calls.
  *   Streams  all device work is enqueued on the caller's stream (a
  *            hipStream_t passed as void*; NULL means the default stream).
- *            Only zero_adam_step waits, and only for its own stream, to read
- *            the flag back.
+ *            zero_adam_step waits for its own stream to read the flag back,
+ *            and so do zero_state_upload and zero_state_download; nothing
+ *            else waits.
  *   Devices  a plan binds to the device that is current at its first device
  *            call; later device calls must run with that device current.
  *   Threads  a plan is not thread safe; distinct plans are independent.
@@ -145,7 +154,7 @@ int64_t zero_plan_segments(const zero_plan_t* plan, zero_segment_t* out, int64_t
 /* Writes the bucket id of each of the first min(cap, n_tensors) tensors. */
 int zero_plan_tensor_buckets(const zero_plan_t* plan, int32_t* out, int64_t cap);
 
-/* Releases the plan and its device flag (NULL is a no-op). */
+/* Releases the plan, its device block and pinned mirror (NULL is a no-op). */
 void zero_plan_destroy(zero_plan_t* plan);
 
 /* Bucketed flatten of half gradients into the rank's flat shard.
@@ -216,11 +225,64 @@ int zero_write_param_shard(zero_plan_t* plan, const float* master, void* param,
                            int64_t param_base, int64_t param_numel, int32_t param_dtype,
                            void* stream);
 
+/* ------------------------------------------------------------------------
+ * The step without host round trips.  The step count t and the loss scaler
+ * live in the plan's device block, so that zero_flatten_grads followed by
+ * zero_adam_step_async can be recorded once into a HIP graph (stream
+ * capture) and replayed every step: nothing in them allocates, waits or
+ * issues a memset.  The arithmetic is that of zero_adam_step and
+ * zero_update_loss_scale; only the bias-correction scalars are formed on
+ * the device (in double, rounded once to fp32, with the device's pow and
+ * sqrt instead of the host C library's).
+ * ---------------------------------------------------------------------- */
+
+/* Loads the device state: applied_steps = steps applied so far (the next
+ * applied step uses t = applied_steps + 1), the scaler's fields, and zero
+ * skipped steps.  Creates the plan's device block if needed.  Waits for
+ * `stream`.  Call it before capturing a graph that contains the plan.
+ * Errors: ZERO_ENULL, ZERO_EINVAL (negative count, scaler fields out of
+ * range), ZERO_EHIP, ZERO_ESTATE. */
+int zero_state_upload(zero_plan_t* plan, int64_t applied_steps, const zero_scaler_t* scaler,
+                      void* stream);
+
+/* Reads the device state back after the work queued on `stream` (waits):
+ * applied steps, the scaler (all fields), the flag of the last asynchronous
+ * step (1 = skipped) and the number of skipped steps since the upload.  Any
+ * output pointer may be NULL.  Errors: ZERO_ENULL, ZERO_ESTATE (no upload
+ * yet), ZERO_EHIP. */
+int zero_state_download(zero_plan_t* plan, int64_t* applied_steps, zero_scaler_t* scaler,
+                        int32_t* last_flag, int64_t* skipped_steps, void* stream);
+
+/* Device address of the current loss scale (a double in the plan's device
+ * block), for scaling the loss on the device before backward ([instr]
+ * loss-scaling bullet).  It changes only inside zero_adam_step_async.
+ * Errors: ZERO_ENULL, ZERO_ESTATE (no upload yet). */
+int zero_state_device_scale(zero_plan_t* plan, const double** out);
+
+/* zero_adam_step with the step count and the loss scale taken from the
+ * device state, followed on the device by the policy of
+ * zero_update_loss_scale:
+ *   flag clear: scalars of step t + 1 at the current scale, the update and
+ *               cast exactly as zero_adam_step, then t += 1 and the
+ *               clean-step count / growth rule;
+ *   flag set:   nothing written, scale = max(scale * backoff, min_scale)
+ *               when dynamic, clean-step count reset, skipped += 1;
+ * then the flag is cleared.  The scan of flat_grad runs first under the
+ * same rule as in zero_adam_step.  Arguments as in zero_adam_step.  Never
+ * waits and never allocates; returns 0 once the work is enqueued.  Calls
+ * on one plan must be ordered (one stream).  Errors: ZERO_ENULL,
+ * ZERO_EINVAL, ZERO_EALIGN, ZERO_EHIP, ZERO_ESTATE (no zero_state_upload
+ * yet, or wrong device). */
+int zero_adam_step_async(zero_plan_t* plan, const zero_adam_hparams_t* hp, const void* flat_grad,
+                         int32_t grad_dtype, float* master, float* exp_avg, float* exp_avg_sq,
+                         void* param, int64_t param_base, int64_t param_numel,
+                         int32_t param_dtype, void* stream);
+
 /* Message of the calling thread's last error ("" if none). */
 const char* zero_last_error(void);
 
 /* Kernel timing with HIP events recorded on the launch stream around each
- * kernel (off by default).  which: 0 flatten (all launches of the last
+ * kernel (off by default; skipped while the stream is being captured).  which: 0 flatten (all launches of the last
  * call), 1 overflow scan, 2 fused Adam, 3 parameter write.  *ms receives
  * the last launch's duration; the call waits for that launch to finish.
  * Errors: ZERO_ESTATE if that kernel has not run since timing was enabled. */

@@ -206,9 +206,13 @@ class OracleRun:
 
 
 class GpuRun:
-    """The GPU side of a case (small and medium sizes: inputs copied from host)."""
+    """The GPU side of a case (small and medium sizes: inputs copied from host).
 
-    def __init__(self, case: Case, device="cuda:0"):
+    mode "sync":  zero_adam_step returns the flag; the host runs the scaler.
+    mode "async": zero_adam_step_async on the device state; the test reads
+                  the state back after every step to compare it."""
+
+    def __init__(self, case: Case, device="cuda:0", mode: str = "sync"):
         import torch
         self.case = case
         self.dev = torch.device(device)
@@ -227,6 +231,9 @@ class GpuRun:
         self.scaler = z.LossScaler(case.init_scale, dynamic=case.dynamic, window=case.window)
         self.t = 0
         self.rng = np.random.default_rng(case.seed + 17)
+        self.mode = mode
+        if mode == "async":
+            z.zero_state_upload(p, 0, self.scaler)
 
     def _param_args(self):
         p, c = self.plan, self.case
@@ -264,6 +271,13 @@ class GpuRun:
             raise ValueError(c.flatten_mode)
         param, base = self._param_args()
         scale = self.scaler.scale
+        if self.mode == "async":
+            z.zero_adam_step_async(p, self.hp, self.flat, self.master, self.m, self.v, param, base)
+            st = z.zero_state_download(p, scaler=self.scaler)
+            ovf = st.last_flag
+            assert st.applied_steps == self.t + (1 - ovf)
+            self.t = st.applied_steps
+            return ovf, scale
         ovf = z.zero_adam_step(p, self.hp, self.t + 1, scale, self.flat, self.master, self.m,
                                self.v, param, base)
         if not ovf:
@@ -281,12 +295,12 @@ class GpuRun:
 
 
 def compare_full(case: Case, steps: Optional[int] = None, check_every: int = 1,
-                 label: str = "") -> dict:
+                 label: str = "", mode: str = "sync") -> dict:
     """Run a case on both sides and compare after every (check_every-th) step.
     Returns a summary (exact-match flags and the max errors seen)."""
     steps = case.steps if steps is None else steps
     orc = OracleRun(case)
-    gpu = GpuRun(case)
+    gpu = GpuRun(case, mode=mode)
     assert (gpu.plan.S, gpu.plan.begin, gpu.plan.real) == (orc.plan.S, orc.plan.begin,
                                                            orc.plan.real)
     worst = dict(master=0.0, m=0.0, v=0.0, param_ulp=0, bit_exact=True, skipped=0)
@@ -296,23 +310,31 @@ def compare_full(case: Case, steps: Optional[int] = None, check_every: int = 1,
         assert g_scale == o_scale, f"{label} it={it}: loss scale {g_scale} vs oracle {o_scale}"
         assert g_ovf == o_ovf, f"{label} it={it}: overflow flag {g_ovf} vs oracle {o_ovf}"
         assert gpu.t == orc.t
+        assert gpu.scaler.scale == orc.scaler.value
         worst["skipped"] += o_ovf
         if it % check_every and it != steps:
             continue
-        gm, gmo, gv, gp, gf = gpu.state_host()
-        S, real = orc.plan.S, orc.plan.real
-        assert np.array_equal(gf, orc.flat), f"{label} it={it}: flat gradient shard differs"
-        for name, a, b in (("master", gm[:S], orc.master), ("m", gmo[:S], orc.m),
-                           ("v", gv[:S], orc.v)):
-            err = max_rel(a, b)
-            worst[name] = max(worst[name], err)
-            if not np.array_equal(a.view(np.uint32), b.view(np.uint32)):
-                worst["bit_exact"] = False
-            assert err <= REL_TOL, f"{label} it={it}: {name} max rel err {err}"
-        if case.param_mode != "none":
-            du = ulp_diff(gp, orc.params())
-            worst["param_ulp"] = max(worst["param_ulp"], du)
-            if du:
-                worst["bit_exact"] = False
-            assert du <= ULP_TOL, f"{label} it={it}: params differ by {du} ulp"
+        compare_state(gpu, orc, worst, f"{label} it={it}")
     return worst
+
+
+def compare_state(gpu: "GpuRun", orc: OracleRun, worst: dict, where: str) -> None:
+    """Compare the GPU's flat shard, master, moments and parameters with the
+    oracle's after the same steps; update the worst-error summary."""
+    case = orc.case
+    gm, gmo, gv, gp, gf = gpu.state_host()
+    S = orc.plan.S
+    assert np.array_equal(gf[:S], orc.flat), f"{where}: flat gradient shard differs"
+    for name, a, b in (("master", gm[:S], orc.master), ("m", gmo[:S], orc.m),
+                       ("v", gv[:S], orc.v)):
+        err = max_rel(a, b)
+        worst[name] = max(worst[name], err)
+        if not np.array_equal(a.view(np.uint32), b.view(np.uint32)):
+            worst["bit_exact"] = False
+        assert err <= REL_TOL, f"{where}: {name} max rel err {err}"
+    if case.param_mode != "none":
+        du = ulp_diff(gp, orc.params())
+        worst["param_ulp"] = max(worst["param_ulp"], du)
+        if du:
+            worst["bit_exact"] = False
+        assert du <= ULP_TOL, f"{where}: params differ by {du} ulp"

@@ -149,3 +149,34 @@ def test_argument_errors_before_device_work():
     bad = _abi.zero_scaler_t(0.0, 1.0, 0.5, 2.0, 10, 0, 1, 0)
     assert lib.zero_update_loss_scale(ctypes.byref(bad), 0) == _abi.ZERO_EINVAL
     assert lib.zero_update_loss_scale(None, 0) == _abi.ZERO_ENULL
+
+
+def test_async_step_argument_errors_before_device_work():
+    """The asynchronous step validates its arguments, then refuses to run on a
+    plan whose device state was never uploaded -- all before any device call."""
+    lib = _abi.lib
+    plan = z.zero_partition_plan([1000], 2, 0, 8)
+    hp = z.AdamHParams().to_c()
+    fake = 1 << 20  # 16-byte aligned, never dereferenced on these error paths
+
+    def step(g=fake, gdt=z.ZERO_BF16, m=fake, hpp=hp, param=None, base=0, numel=0, pdt=0):
+        return lib.zero_adam_step_async(plan.handle, ctypes.byref(hpp), g, gdt, fake, m, fake,
+                                        param, base, numel, pdt, None)
+    assert step(gdt=3) == _abi.ZERO_EINVAL
+    assert step(g=None) == _abi.ZERO_ENULL
+    assert step(g=fake + 4) == _abi.ZERO_EALIGN
+    assert step(m=fake + 1) == _abi.ZERO_EALIGN
+    assert step(hpp=z.AdamHParams(eps=0.0).to_c()) == _abi.ZERO_EINVAL
+    assert step(param=fake, base=10, numel=100, pdt=z.ZERO_BF16) == _abi.ZERO_EINVAL
+    assert step() == _abi.ZERO_ESTATE
+    assert "zero_state_upload" in z.zero_last_error()
+    assert lib.zero_adam_step_async(None, ctypes.byref(hp), fake, z.ZERO_BF16, fake, fake, fake,
+                                    None, 0, 0, 0, None) == _abi.ZERO_ENULL
+    out = ctypes.c_void_p()
+    assert lib.zero_state_device_scale(plan.handle, ctypes.byref(out)) == _abi.ZERO_ESTATE
+    assert lib.zero_state_download(plan.handle, None, None, None, None, None) == _abi.ZERO_ESTATE
+    sc = _abi.zero_scaler_t(1024.0, 1.0, 0.5, 2.0, 0, 0, 1, 0)        # window 0
+    assert lib.zero_state_upload(plan.handle, 0, ctypes.byref(sc), None) == _abi.ZERO_EINVAL
+    sc = _abi.zero_scaler_t(1024.0, 1.0, 0.5, 2.0, 10, 0, 1, 0)
+    assert lib.zero_state_upload(plan.handle, -1, ctypes.byref(sc), None) == _abi.ZERO_EINVAL
+    assert lib.zero_state_upload(None, 0, ctypes.byref(sc), None) == _abi.ZERO_ENULL

@@ -12,6 +12,14 @@ and the stream.  The functions keep the names of the C ABI
                    exp_avg_sq, param=None, param_base=0, stream=None) -> 0 | 1
     zero_update_loss_scale(scaler, overflow)
     zero_write_param_shard(plan, master, param, param_base=0, stream=None)
+
+and the step without host round trips (graph-capturable):
+
+    zero_state_upload(plan, applied_steps, scaler, stream=None)
+    zero_adam_step_async(plan, hparams, flat_grad, master, exp_avg, exp_avg_sq,
+                         param=None, param_base=0, stream=None)
+    zero_state_download(plan, stream=None) -> DeviceStepState
+    zero_state_device_scale(plan) -> device address of the loss scale (double)
 """
 from __future__ import annotations
 
@@ -22,9 +30,11 @@ from typing import List, Optional, Sequence
 from . import _abi
 from ._abi import ZERO_BF16, ZERO_F16, ZeroError, check, lib  # noqa: F401
 
-__all__ = ["Plan", "AdamHParams", "LossScaler", "ZeroError", "zero_partition_plan",
-           "zero_flatten_grads", "zero_adam_step", "zero_update_loss_scale",
-           "zero_write_param_shard", "zero_last_error", "ZERO_F16", "ZERO_BF16"]
+__all__ = ["Plan", "AdamHParams", "LossScaler", "DeviceStepState", "ZeroError",
+           "zero_partition_plan", "zero_flatten_grads", "zero_adam_step",
+           "zero_update_loss_scale", "zero_write_param_shard", "zero_state_upload",
+           "zero_adam_step_async", "zero_state_download", "zero_state_device_scale",
+           "zero_last_error", "ZERO_F16", "ZERO_BF16"]
 
 
 def _torch():
@@ -217,6 +227,70 @@ def zero_write_param_shard(plan: Plan, master, param, param_base: int = 0, strea
                                      int(param_base), param.numel(), _dtype_code(param),
                                      _stream_handle(stream, master.device)),
           "zero_write_param_shard")
+
+
+@dataclass
+class DeviceStepState:
+    """The device state of the asynchronous step, as read back."""
+    applied_steps: int
+    skipped_steps: int
+    last_flag: int
+    scale: float
+    good_steps: int
+
+
+def zero_state_upload(plan: Plan, applied_steps: int, scaler: LossScaler, stream=None) -> None:
+    """Load t (= applied_steps) and the scaler into the plan's device state (waits)."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device())
+    check(lib.zero_state_upload(plan.handle, int(applied_steps), ctypes.byref(scaler.c),
+                                _stream_handle(stream, dev)), "zero_state_upload")
+
+
+def zero_state_download(plan: Plan, stream=None, scaler: Optional[LossScaler] = None
+                        ) -> DeviceStepState:
+    """Read the device state back (waits); also refreshes `scaler` when given."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device())
+    t = ctypes.c_int64(0)
+    skipped = ctypes.c_int64(0)
+    last = ctypes.c_int32(0)
+    sc = _abi.zero_scaler_t()
+    check(lib.zero_state_download(plan.handle, ctypes.byref(t), ctypes.byref(sc),
+                                  ctypes.byref(last), ctypes.byref(skipped),
+                                  _stream_handle(stream, dev)), "zero_state_download")
+    if scaler is not None:
+        ctypes.memmove(ctypes.byref(scaler.c), ctypes.byref(sc), ctypes.sizeof(sc))
+    return DeviceStepState(int(t.value), int(skipped.value), int(last.value), float(sc.scale),
+                           int(sc.good_steps))
+
+
+def zero_state_device_scale(plan: Plan) -> int:
+    """Device address of the current loss scale (a double)."""
+    out = ctypes.c_void_p()
+    check(lib.zero_state_device_scale(plan.handle, ctypes.byref(out)), "zero_state_device_scale")
+    return int(out.value)
+
+
+def zero_adam_step_async(plan: Plan, hparams: AdamHParams, flat_grad, master, exp_avg,
+                         exp_avg_sq, param=None, param_base: int = 0, stream=None) -> None:
+    """Enqueue the gated update and the loss-scale policy on the device state;
+    returns at once (nothing waits, nothing is allocated)."""
+    torch = _torch()
+    _require(flat_grad, "flat_grad", plan.S, (torch.float16, torch.bfloat16))
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _require(t, name, plan.S, (torch.float32,))
+    pptr, pnum, pdt = None, 0, 0
+    if param is not None:
+        _require(param, "param", 0, (torch.float16, torch.bfloat16))
+        pptr, pnum, pdt = param.data_ptr(), param.numel(), _dtype_code(param)
+    hp = hparams.to_c()
+    check(lib.zero_adam_step_async(plan.handle, ctypes.byref(hp), flat_grad.data_ptr(),
+                                   _dtype_code(flat_grad), master.data_ptr(),
+                                   exp_avg.data_ptr(), exp_avg_sq.data_ptr(), pptr,
+                                   int(param_base), pnum, pdt,
+                                   _stream_handle(stream, master.device)),
+          "zero_adam_step_async")
 
 
 def zero_last_error() -> str:

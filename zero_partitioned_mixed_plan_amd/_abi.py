@@ -73,6 +73,12 @@ SIGNATURES = {
                                       _I32, _VP]),
     "zero_update_loss_scale": (ctypes.c_int, [ctypes.POINTER(zero_scaler_t), _I32]),
     "zero_write_param_shard": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _I32, _VP]),
+    "zero_state_upload": (ctypes.c_int, [_VP, _I64, ctypes.POINTER(zero_scaler_t), _VP]),
+    "zero_state_download": (ctypes.c_int, [_VP, ctypes.POINTER(_I64), ctypes.POINTER(zero_scaler_t),
+                                           ctypes.POINTER(_I32), ctypes.POINTER(_I64), _VP]),
+    "zero_state_device_scale": (ctypes.c_int, [_VP, ctypes.POINTER(_VP)]),
+    "zero_adam_step_async": (ctypes.c_int, [_VP, ctypes.POINTER(zero_adam_hparams_t), _VP, _I32,
+                                            _VP, _VP, _VP, _VP, _I64, _I64, _I32, _VP]),
     "zero_last_error": (ctypes.c_char_p, []),
     "zero_plan_set_timing": (ctypes.c_int, [_VP, _I32]),
     "zero_plan_kernel_ms": (ctypes.c_int, [_VP, _I32, ctypes.POINTER(ctypes.c_float)]),

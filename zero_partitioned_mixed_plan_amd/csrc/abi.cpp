@@ -47,17 +47,17 @@ int ensure_device(zero_plan* p) {
         }
         return ZERO_OK;
     }
-    e = hipMalloc(reinterpret_cast<void**>(&d.d_flag), 256);
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(flag)");
-    e = hipHostMalloc(reinterpret_cast<void**>(&d.h_flag), sizeof(int), hipHostMallocDefault);
+    e = hipMalloc(reinterpret_cast<void**>(&d.d_flag), kBlockBytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(device block)");
+    e = hipHostMalloc(reinterpret_cast<void**>(&d.h_flag), kBlockBytes, hipHostMallocDefault);
     if (e != hipSuccess) {
         (void)hipFree(d.d_flag);
         d.d_flag = nullptr;
-        return hip_fail(e, "hipHostMalloc(flag mirror)");
+        return hip_fail(e, "hipHostMalloc(device block mirror)");
     }
-    *d.h_flag = 0;
-    e = hipMemset(d.d_flag, 0, 256);
-    if (e != hipSuccess) return hip_fail(e, "hipMemset(flag)");
+    std::memset(d.h_flag, 0, kBlockBytes);
+    e = hipMemset(d.d_flag, 0, kBlockBytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMemset(device block)");
     for (int i = 0; i < kTimers; ++i) {
         e = hipEventCreate(&d.ev_start[i]);
         if (e == hipSuccess) e = hipEventCreate(&d.ev_stop[i]);
@@ -68,14 +68,20 @@ int ensure_device(zero_plan* p) {
     return ZERO_OK;
 }
 
+// Event timing is skipped while the stream is being captured into a graph.
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
 int timer_start(zero_plan* p, Timer t, hipStream_t s) {
-    if (!p->dev.timing) return ZERO_OK;
+    if (!p->dev.timing || capturing(s)) return ZERO_OK;
     hipError_t e = hipEventRecord(p->dev.ev_start[t], s);
     return e == hipSuccess ? ZERO_OK : hip_fail(e, "hipEventRecord");
 }
 
 int timer_stop(zero_plan* p, Timer t, hipStream_t s) {
-    if (!p->dev.timing) return ZERO_OK;
+    if (!p->dev.timing || capturing(s)) return ZERO_OK;
     hipError_t e = hipEventRecord(p->dev.ev_stop[t], s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     p->dev.timed[t] = true;
@@ -101,6 +107,70 @@ int param_target(const zero_plan* p, void* param, int64_t base, int64_t numel, i
     }
     *out = static_cast<uint16_t*>(param) + (p->begin - base);
     return ZERO_OK;
+}
+
+DeviceStep* device_step(zero_plan* p) {
+    return reinterpret_cast<DeviceStep*>(reinterpret_cast<char*>(p->dev.d_flag) + kStateOffset);
+}
+
+AdamScalars* device_scalars(zero_plan* p) {
+    return reinterpret_cast<AdamScalars*>(reinterpret_cast<char*>(p->dev.d_flag) +
+                                          kScalarsOffset);
+}
+
+int check_hparams(const zero_adam_hparams_t* hp) {
+    if (!(hp->lr >= 0 && std::isfinite(hp->lr)) || !(hp->beta1 >= 0 && hp->beta1 < 1) ||
+        !(hp->beta2 >= 0 && hp->beta2 < 1) || !(hp->eps > 0 && std::isfinite(hp->eps)) ||
+        !(hp->weight_decay >= 0 && std::isfinite(hp->weight_decay))) {
+        return fail(ZERO_EINVAL, "hyperparameters out of range (lr >= 0, 0 <= betas < 1, eps > 0, "
+                                 "weight_decay >= 0)");
+    }
+    return ZERO_OK;
+}
+
+int check_scaler(const zero_scaler_t* sc) {
+    if (!(std::isfinite(sc->scale) && sc->scale > 0) ||
+        !(std::isfinite(sc->min_scale) && sc->min_scale > 0) ||
+        !(sc->backoff > 0 && sc->backoff <= 1) || !(std::isfinite(sc->growth) && sc->growth >= 1) ||
+        sc->window < 1 || sc->good_steps < 0) {
+        return fail(ZERO_EINVAL, "scaler fields out of range");
+    }
+    return ZERO_OK;
+}
+
+// Checks shared by the synchronous and asynchronous steps.
+int check_step_buffers(const zero_plan* p, const void* flat_grad, int32_t grad_dtype,
+                       const float* master, const float* exp_avg, const float* exp_avg_sq) {
+    if (!valid_dtype(grad_dtype)) return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16");
+    if (p->S > 0 && (flat_grad == nullptr || master == nullptr || exp_avg == nullptr ||
+                     exp_avg_sq == nullptr)) {
+        return fail(ZERO_ENULL, "flat_grad, master, exp_avg and exp_avg_sq must be non-NULL");
+    }
+    if (!aligned16(flat_grad)) return fail(ZERO_EALIGN, "flat_grad must be 16-byte aligned");
+    if (!aligned4(master) || !aligned4(exp_avg) || !aligned4(exp_avg_sq)) {
+        return fail(ZERO_EALIGN, "master, exp_avg and exp_avg_sq must be 4-byte aligned");
+    }
+    return ZERO_OK;
+}
+
+// Whether every real gradient of flat_grad went through the flatten (and so
+// through its overflow test) since the last step; if not, the step scans.
+bool flatten_covered(const zero_plan* p, const void* flat_grad, int32_t grad_dtype) {
+    bool covered = p->flattened_into == flat_grad && p->flattened_dtype == grad_dtype;
+    if (covered && !p->flatten_all_done) {
+        for (int32_t b = 0; b < p->n_buckets && covered; ++b) {
+            if (p->bucket_seg_last[b] > p->bucket_seg_first[b] && !p->bucket_flattened[b]) {
+                covered = false;
+            }
+        }
+    }
+    return covered;
+}
+
+void reset_flatten_bookkeeping(zero_plan* p) {
+    std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
+    p->flatten_all_done = false;
+    p->flattened_into = nullptr;
 }
 
 }  // namespace
@@ -272,51 +342,23 @@ int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, 
     if (!(std::isfinite(loss_scale) && loss_scale > 0)) {
         return fail(ZERO_EINVAL, "loss_scale must be finite and > 0");
     }
-    if (!(hp->lr >= 0 && std::isfinite(hp->lr)) || !(hp->beta1 >= 0 && hp->beta1 < 1) ||
-        !(hp->beta2 >= 0 && hp->beta2 < 1) || !(hp->eps > 0 && std::isfinite(hp->eps)) ||
-        !(hp->weight_decay >= 0 && std::isfinite(hp->weight_decay))) {
-        return fail(ZERO_EINVAL, "hyperparameters out of range (lr >= 0, 0 <= betas < 1, eps > 0, "
-                                 "weight_decay >= 0)");
-    }
-    if (p->S > 0 && (flat_grad == nullptr || master == nullptr || exp_avg == nullptr ||
-                     exp_avg_sq == nullptr)) {
-        return fail(ZERO_ENULL, "flat_grad, master, exp_avg and exp_avg_sq must be non-NULL");
-    }
-    if (!aligned16(flat_grad)) return fail(ZERO_EALIGN, "flat_grad must be 16-byte aligned");
-    if (!aligned4(master) || !aligned4(exp_avg) || !aligned4(exp_avg_sq)) {
-        return fail(ZERO_EALIGN, "master, exp_avg and exp_avg_sq must be 4-byte aligned");
-    }
+    int rc = check_hparams(hp);
+    if (rc != ZERO_OK) return rc;
+    rc = check_step_buffers(p, flat_grad, grad_dtype, master, exp_avg, exp_avg_sq);
+    if (rc != ZERO_OK) return rc;
     uint16_t* param0 = nullptr;
-    int rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
+    rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
     if (rc != ZERO_OK) return rc;
     rc = ensure_device(p);
     if (rc != ZERO_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // host scalars: double, each rounded once to fp32
-    const double t = static_cast<double>(step);
-    AdamScalars sc;
-    sc.inv_scale = static_cast<float>(1.0 / loss_scale);
-    sc.b1 = static_cast<float>(hp->beta1);
-    sc.omb1 = static_cast<float>(1.0 - hp->beta1);
-    sc.b2 = static_cast<float>(hp->beta2);
-    sc.omb2 = static_cast<float>(1.0 - hp->beta2);
-    sc.step = static_cast<float>(hp->lr / (1.0 - std::pow(hp->beta1, t)));
-    sc.rsbc2 = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(hp->beta2, t)));
-    sc.eps = static_cast<float>(hp->eps);
-    sc.decay = hp->adamw ? static_cast<float>(1.0 - hp->lr * hp->weight_decay) : 1.0f;
-    sc.wd = static_cast<float>(hp->weight_decay);
+    const AdamScalars sc = make_scalars(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay,
+                                        hp->adamw, static_cast<double>(step), loss_scale);
 
     // the gate needs every real gradient of this flat buffer tested
-    bool covered = p->flattened_into == flat_grad && p->flattened_dtype == grad_dtype;
-    if (covered && !p->flatten_all_done) {
-        for (int32_t b = 0; b < p->n_buckets && covered; ++b) {
-            if (p->bucket_seg_last[b] > p->bucket_seg_first[b] && !p->bucket_flattened[b]) {
-                covered = false;
-            }
-        }
-    }
-    if (!covered) {
+    if (!flatten_covered(p, flat_grad, grad_dtype)) {
         if ((rc = timer_start(p, kTimerScan, s)) != ZERO_OK) return rc;
         hipError_t e = launch_scan(static_cast<const uint16_t*>(flat_grad), p->S, p->dev.d_flag,
                                    grad_dtype, s);
@@ -325,8 +367,8 @@ int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, 
     }
     if ((rc = timer_start(p, kTimerAdam, s)) != ZERO_OK) return rc;
     hipError_t e = launch_adam(static_cast<const uint16_t*>(flat_grad), master, exp_avg,
-                               exp_avg_sq, param0, p->S, p->real, p->dev.d_flag, sc, grad_dtype,
-                               param_dtype, hp->adamw != 0, s);
+                               exp_avg_sq, param0, p->S, p->real, p->dev.d_flag, sc, nullptr,
+                               grad_dtype, param_dtype, hp->adamw != 0, s);
     if (e != hipSuccess) return hip_fail(e, "adam launch");
     if ((rc = timer_stop(p, kTimerAdam, s)) != ZERO_OK) return rc;
     e = hipMemcpyAsync(p->dev.h_flag, p->dev.d_flag, sizeof(int), hipMemcpyDeviceToHost, s);
@@ -335,20 +377,131 @@ int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, 
     if (e != hipSuccess) return hip_fail(e, "flag clear");
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
-    p->flatten_all_done = false;
-    p->flattened_into = nullptr;
+    reset_flatten_bookkeeping(p);
     return *p->dev.h_flag != 0 ? 1 : 0;
+}
+
+int zero_state_upload(zero_plan_t* p, int64_t applied_steps, const zero_scaler_t* scaler,
+                      void* stream) {
+    if (p == nullptr || scaler == nullptr) return fail(ZERO_ENULL, "plan or scaler is NULL");
+    if (applied_steps < 0) return fail(ZERO_EINVAL, "applied_steps must be >= 0");
+    int rc = check_scaler(scaler);
+    if (rc != ZERO_OK) return rc;
+    rc = ensure_device(p);
+    if (rc != ZERO_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // stage in the pinned mirror; the stream is drained before returning, so
+    // the mirror is free again afterwards
+    DeviceStep d{};
+    d.t = applied_steps;
+    d.skipped = 0;
+    d.scale = scaler->scale;
+    d.min_scale = scaler->min_scale;
+    d.backoff = scaler->backoff;
+    d.growth = scaler->growth;
+    d.window = scaler->window;
+    d.good_steps = scaler->good_steps;
+    d.dynamic = scaler->dynamic != 0;
+    d.last_flag = 0;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    char* mirror = reinterpret_cast<char*>(p->dev.h_flag);
+    std::memcpy(mirror + kStateOffset, &d, sizeof(d));
+    e = hipMemcpyAsync(device_step(p), mirror + kStateOffset, sizeof(d), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "state upload");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    p->dev.state_ready = true;
+    return ZERO_OK;
+}
+
+int zero_state_download(zero_plan_t* p, int64_t* applied_steps, zero_scaler_t* scaler,
+                        int32_t* last_flag, int64_t* skipped_steps, void* stream) {
+    if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");
+    if (!p->dev.ready || !p->dev.state_ready) {
+        return fail(ZERO_ESTATE, "no device state: call zero_state_upload first");
+    }
+    int rc = ensure_device(p);
+    if (rc != ZERO_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* mirror = reinterpret_cast<char*>(p->dev.h_flag);
+    hipError_t e = hipMemcpyAsync(mirror + kStateOffset, device_step(p), sizeof(DeviceStep),
+                                  hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "state download");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    DeviceStep d;
+    std::memcpy(&d, mirror + kStateOffset, sizeof(d));
+    if (applied_steps) *applied_steps = d.t;
+    if (skipped_steps) *skipped_steps = d.skipped;
+    if (last_flag) *last_flag = d.last_flag;
+    if (scaler) {
+        scaler->scale = d.scale;
+        scaler->min_scale = d.min_scale;
+        scaler->backoff = d.backoff;
+        scaler->growth = d.growth;
+        scaler->window = d.window;
+        scaler->good_steps = d.good_steps;
+        scaler->dynamic = d.dynamic;
+    }
+    return ZERO_OK;
+}
+
+int zero_state_device_scale(zero_plan_t* p, const double** out) {
+    if (p == nullptr || out == nullptr) return fail(ZERO_ENULL, "plan or out is NULL");
+    if (!p->dev.ready || !p->dev.state_ready) {
+        return fail(ZERO_ESTATE, "no device state: call zero_state_upload first");
+    }
+    *out = &device_step(p)->scale;
+    return ZERO_OK;
+}
+
+int zero_adam_step_async(zero_plan_t* p, const zero_adam_hparams_t* hp, const void* flat_grad,
+                         int32_t grad_dtype, float* master, float* exp_avg, float* exp_avg_sq,
+                         void* param, int64_t param_base, int64_t param_numel,
+                         int32_t param_dtype, void* stream) {
+    if (p == nullptr || hp == nullptr) return fail(ZERO_ENULL, "plan or hparams is NULL");
+    int rc = check_hparams(hp);
+    if (rc != ZERO_OK) return rc;
+    rc = check_step_buffers(p, flat_grad, grad_dtype, master, exp_avg, exp_avg_sq);
+    if (rc != ZERO_OK) return rc;
+    uint16_t* param0 = nullptr;
+    rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
+    if (rc != ZERO_OK) return rc;
+    // allocation happens at zero_state_upload, never here: this call may be
+    // captured into a graph
+    if (!p->dev.ready || !p->dev.state_ready) {
+        return fail(ZERO_ESTATE, "no device state: call zero_state_upload first");
+    }
+    rc = ensure_device(p);
+    if (rc != ZERO_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!flatten_covered(p, flat_grad, grad_dtype)) {
+        if ((rc = timer_start(p, kTimerScan, s)) != ZERO_OK) return rc;
+        hipError_t e = launch_scan(static_cast<const uint16_t*>(flat_grad), p->S, p->dev.d_flag,
+                                   grad_dtype, s);
+        if (e != hipSuccess) return hip_fail(e, "scan launch");
+        if ((rc = timer_stop(p, kTimerScan, s)) != ZERO_OK) return rc;
+    }
+    hipError_t e = launch_step_prologue(p->dev.d_flag, device_step(p), device_scalars(p), *hp, s);
+    if (e != hipSuccess) return hip_fail(e, "step prologue launch");
+    if ((rc = timer_start(p, kTimerAdam, s)) != ZERO_OK) return rc;
+    const AdamScalars unused{};
+    e = launch_adam(static_cast<const uint16_t*>(flat_grad), master, exp_avg, exp_avg_sq, param0,
+                    p->S, p->real, p->dev.d_flag, unused, device_scalars(p), grad_dtype,
+                    param_dtype, hp->adamw != 0, s);
+    if (e != hipSuccess) return hip_fail(e, "adam launch");
+    if ((rc = timer_stop(p, kTimerAdam, s)) != ZERO_OK) return rc;
+    e = launch_step_epilogue(p->dev.d_flag, device_step(p), s);
+    if (e != hipSuccess) return hip_fail(e, "step epilogue launch");
+    reset_flatten_bookkeeping(p);
+    return ZERO_OK;
 }
 
 int zero_update_loss_scale(zero_scaler_t* sc, int32_t overflow) {
     if (sc == nullptr) return fail(ZERO_ENULL, "scaler is NULL");
-    if (!(std::isfinite(sc->scale) && sc->scale > 0) ||
-        !(std::isfinite(sc->min_scale) && sc->min_scale > 0) ||
-        !(sc->backoff > 0 && sc->backoff <= 1) || !(std::isfinite(sc->growth) && sc->growth >= 1) ||
-        sc->window < 1 || sc->good_steps < 0) {
-        return fail(ZERO_EINVAL, "scaler fields out of range");
-    }
+    int rc = check_scaler(sc);
+    if (rc != ZERO_OK) return rc;
     if (overflow) {
         if (sc->dynamic) sc->scale = std::max(sc->scale * sc->backoff, sc->min_scale);
         sc->good_steps = 0;

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -28,11 +29,59 @@ struct Segment {
 
 enum Timer { kTimerFlatten = 0, kTimerScan = 1, kTimerAdam = 2, kTimerWrite = 3, kTimers = 4 };
 
+// Loss-scale and step-count state of the asynchronous step, kept in device
+// memory so that a whole step needs no host round trip.
+struct DeviceStep {
+    int64_t t;        // applied (not skipped) steps so far
+    int64_t skipped;  // skipped steps so far
+    double scale;
+    double min_scale;
+    double backoff;
+    double growth;
+    int32_t window;
+    int32_t good_steps;
+    int32_t dynamic;
+    int32_t last_flag;  // flag of the last asynchronous step (1 = skipped)
+};
+
+struct AdamScalars {
+    float inv_scale, b1, omb1, b2, omb2, step, rsbc2, eps, decay, wd;
+};
+
+// The plan's device block (one 256-byte allocation): the overflow flag, the
+// asynchronous step state and the update scalars formed on the device.
+constexpr size_t kBlockBytes = 256;
+constexpr size_t kStateOffset = 64;
+constexpr size_t kScalarsOffset = 128;
+static_assert(kStateOffset + sizeof(DeviceStep) <= kScalarsOffset, "device block layout");
+static_assert(kScalarsOffset + sizeof(AdamScalars) <= kBlockBytes, "device block layout");
+
+// The update's fp32 scalars for bias-correction step t and loss scale
+// `scale`: formed in double, each rounded once to fp32.  The same function
+// serves the host (synchronous step) and the device (asynchronous step).
+__host__ __device__ inline AdamScalars make_scalars(double lr, double beta1, double beta2,
+                                                    double eps, double weight_decay, int adamw,
+                                                    double t, double scale) {
+    AdamScalars sc;
+    sc.inv_scale = static_cast<float>(1.0 / scale);
+    sc.b1 = static_cast<float>(beta1);
+    sc.omb1 = static_cast<float>(1.0 - beta1);
+    sc.b2 = static_cast<float>(beta2);
+    sc.omb2 = static_cast<float>(1.0 - beta2);
+    sc.step = static_cast<float>(lr / (1.0 - pow(beta1, t)));
+    sc.rsbc2 = static_cast<float>(1.0 / sqrt(1.0 - pow(beta2, t)));
+    sc.eps = static_cast<float>(eps);
+    sc.decay = adamw ? static_cast<float>(1.0 - lr * weight_decay) : 1.0f;
+    sc.wd = static_cast<float>(weight_decay);
+    return sc;
+}
+
 struct DeviceState {
     bool ready = false;
+    bool state_ready = false;   // zero_state_upload has run
     int device = -1;
-    int* d_flag = nullptr;      // device overflow flag (256 B allocation)
-    int* h_flag = nullptr;      // pinned host mirror
+    int* d_flag = nullptr;      // device block: overflow flag at offset 0
+    int* h_flag = nullptr;      // pinned host mirror of the device block
     bool timing = false;
     hipEvent_t ev_start[kTimers] = {};
     hipEvent_t ev_stop[kTimers] = {};
@@ -78,18 +127,23 @@ struct FlatPiece {
 
 constexpr int kMaxPiecesPerLaunch = 64;
 
-struct AdamScalars {
-    float inv_scale, b1, omb1, b2, omb2, step, rsbc2, eps, decay, wd;
-};
-
 hipError_t launch_flatten(const FlatPiece* pieces, int n, uint16_t* flat, int* flag,
                           int grad_dtype, hipStream_t s);
 hipError_t launch_scan(const uint16_t* flat, int64_t n, int* flag, int grad_dtype, hipStream_t s);
+// sc_dev == nullptr: the update uses the scalars passed by value in sc;
+// otherwise it reads them from device memory at sc_dev.
 hipError_t launch_adam(const uint16_t* g, float* master, float* m, float* v, uint16_t* param_at_0,
                        int64_t S, int64_t real, const int* flag, const AdamScalars& sc,
-                       int grad_dtype, int param_dtype, bool adamw, hipStream_t s);
+                       const AdamScalars* sc_dev, int grad_dtype, int param_dtype, bool adamw,
+                       hipStream_t s);
 hipError_t launch_write_param(const float* master, uint16_t* param_at_0, int64_t real,
                               int param_dtype, hipStream_t s);
 hipError_t launch_flag_clear(int* flag, hipStream_t s);
+// Asynchronous step: the prologue forms the scalars of step t + 1 from the
+// device state (skipped when the flag is raised); the epilogue applies the
+// loss-scale policy, advances t or the skip count, and clears the flag.
+hipError_t launch_step_prologue(const int* flag, const DeviceStep* st, AdamScalars* out,
+                                const zero_adam_hparams_t& hp, hipStream_t s);
+hipError_t launch_step_epilogue(int* flag, DeviceStep* st, hipStream_t s);
 
 }  // namespace zmi

@@ -275,15 +275,18 @@ __device__ __forceinline__ void adam_elem(float g, float& p, float& m, float& v,
 }
 
 // GDT: gradient dtype.  PDT: parameter dtype, 0 = no parameter write.
-// A 128-thread workgroup (two waves) updates kAdamSpan = 256 consecutive
-// elements; thread t takes elements t and t + 128 and issues the loads of
-// both before any arithmetic.
-template <int GDT, int PDT, bool ADAMW>
+// DEVSC: the scalars come from device memory (asynchronous step) instead of
+// the kernel arguments.  A 128-thread workgroup (two waves) updates
+// kAdamSpan = 256 consecutive elements; thread t takes elements t and
+// t + 128 and issues the loads of both before any arithmetic.
+template <int GDT, int PDT, bool ADAMW, bool DEVSC>
 __global__ void __launch_bounds__(kAdamThreads)
 adam_kernel(const uint16_t* __restrict__ g, float* __restrict__ master, float* __restrict__ mom,
             float* __restrict__ var, uint16_t* __restrict__ param, int64_t S, int64_t real,
-            const int* __restrict__ flag, const AdamScalars c) {
+            const int* __restrict__ flag, const AdamScalars c_arg,
+            const AdamScalars* __restrict__ c_dev) {
     if (*flag != 0) return;  // overflow: the step is skipped, nothing is written
+    const AdamScalars c = DEVSC ? *c_dev : c_arg;
     const int64_t k0 = block_id() * kAdamSpan + threadIdx.x;
     float p[kAdamPer], m[kAdamPer], v[kAdamPer];
     uint32_t h[kAdamPer];
@@ -320,33 +323,82 @@ write_param_kernel(const float* __restrict__ master, uint16_t* __restrict__ para
 
 __global__ void flag_clear_kernel(int* flag) { *flag = 0; }
 
-template <int GDT, int PDT>
-hipError_t adam_dispatch_w(bool adamw, dim3 grid, hipStream_t s, const uint16_t* g, float* master,
-                           float* m, float* v, uint16_t* param, int64_t S, int64_t real,
-                           const int* flag, const AdamScalars& sc) {
-    if (adamw) {
-        hipLaunchKernelGGL((adam_kernel<GDT, PDT, true>), grid, dim3(kAdamThreads), 0, s, g, master,
-                           m, v, param, S, real, flag, sc);
+// One thread: the fp32 scalars of step t + 1 at the current loss scale, in
+// double and rounded once each (make_scalars), unless the flag says this
+// step is skipped.
+__global__ void step_prologue_kernel(const int* __restrict__ flag,
+                                     const DeviceStep* __restrict__ st,
+                                     AdamScalars* __restrict__ out, const zero_adam_hparams_t hp) {
+    if (*flag != 0) return;
+    *out = make_scalars(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.adamw,
+                        static_cast<double>(st->t + 1), st->scale);
+}
+
+// One thread: the loss-scale policy of zero_update_loss_scale on the device
+// state, then the flag is cleared for the next step.
+__global__ void step_epilogue_kernel(int* __restrict__ flag, DeviceStep* __restrict__ st) {
+    const int overflow = *flag != 0;
+    DeviceStep d = *st;
+    if (overflow) {
+        if (d.dynamic) {
+            const double s = d.scale * d.backoff;
+            d.scale = s < d.min_scale ? d.min_scale : s;
+        }
+        d.good_steps = 0;
+        d.skipped += 1;
     } else {
-        hipLaunchKernelGGL((adam_kernel<GDT, PDT, false>), grid, dim3(kAdamThreads), 0, s, g, master,
-                           m, v, param, S, real, flag, sc);
+        d.t += 1;
+        d.good_steps += 1;
+        if (d.dynamic && d.good_steps >= d.window) {
+            d.scale *= d.growth;
+            d.good_steps = 0;
+        }
+    }
+    d.last_flag = overflow;
+    *st = d;
+    *flag = 0;
+}
+
+template <int GDT, int PDT, bool ADAMW>
+hipError_t adam_dispatch_d(const AdamScalars* dsc, dim3 grid, hipStream_t s, const uint16_t* g,
+                           float* master, float* m, float* v, uint16_t* param, int64_t S,
+                           int64_t real, const int* flag, const AdamScalars& sc) {
+    if (dsc != nullptr) {
+        hipLaunchKernelGGL((adam_kernel<GDT, PDT, ADAMW, true>), grid, dim3(kAdamThreads), 0, s, g,
+                           master, m, v, param, S, real, flag, sc, dsc);
+    } else {
+        hipLaunchKernelGGL((adam_kernel<GDT, PDT, ADAMW, false>), grid, dim3(kAdamThreads), 0, s,
+                           g, master, m, v, param, S, real, flag, sc, dsc);
     }
     return hipGetLastError();
 }
 
+template <int GDT, int PDT>
+hipError_t adam_dispatch_w(bool adamw, const AdamScalars* dsc, dim3 grid, hipStream_t s,
+                           const uint16_t* g, float* master, float* m, float* v, uint16_t* param,
+                           int64_t S, int64_t real, const int* flag, const AdamScalars& sc) {
+    if (adamw) {
+        return adam_dispatch_d<GDT, PDT, true>(dsc, grid, s, g, master, m, v, param, S, real,
+                                               flag, sc);
+    }
+    return adam_dispatch_d<GDT, PDT, false>(dsc, grid, s, g, master, m, v, param, S, real, flag,
+                                            sc);
+}
+
 template <int GDT>
-hipError_t adam_dispatch_p(int pdt, bool adamw, dim3 grid, hipStream_t s, const uint16_t* g,
-                           float* master, float* m, float* v, uint16_t* param, int64_t S,
-                           int64_t real, const int* flag, const AdamScalars& sc) {
+hipError_t adam_dispatch_p(int pdt, bool adamw, const AdamScalars* dsc, dim3 grid, hipStream_t s,
+                           const uint16_t* g, float* master, float* m, float* v, uint16_t* param,
+                           int64_t S, int64_t real, const int* flag, const AdamScalars& sc) {
     if (param == nullptr) {
-        return adam_dispatch_w<GDT, 0>(adamw, grid, s, g, master, m, v, param, S, real, flag, sc);
+        return adam_dispatch_w<GDT, 0>(adamw, dsc, grid, s, g, master, m, v, param, S, real, flag,
+                                       sc);
     }
     if (pdt == ZERO_F16) {
-        return adam_dispatch_w<GDT, ZERO_F16>(adamw, grid, s, g, master, m, v, param, S, real,
-                                              flag, sc);
+        return adam_dispatch_w<GDT, ZERO_F16>(adamw, dsc, grid, s, g, master, m, v, param, S,
+                                              real, flag, sc);
     }
-    return adam_dispatch_w<GDT, ZERO_BF16>(adamw, grid, s, g, master, m, v, param, S, real, flag,
-                                           sc);
+    return adam_dispatch_w<GDT, ZERO_BF16>(adamw, dsc, grid, s, g, master, m, v, param, S, real,
+                                           flag, sc);
 }
 
 }  // namespace
@@ -390,15 +442,16 @@ hipError_t launch_scan(const uint16_t* flat, int64_t n, int* flag, int grad_dtyp
 
 hipError_t launch_adam(const uint16_t* g, float* master, float* m, float* v, uint16_t* param_at_0,
                        int64_t S, int64_t real, const int* flag, const AdamScalars& sc,
-                       int grad_dtype, int param_dtype, bool adamw, hipStream_t s) {
+                       const AdamScalars* sc_dev, int grad_dtype, int param_dtype, bool adamw,
+                       hipStream_t s) {
     if (S <= 0) return hipSuccess;
     const dim3 grid = grid_2d((S + kAdamSpan - 1) / kAdamSpan);
     if (grad_dtype == ZERO_F16) {
-        return adam_dispatch_p<ZERO_F16>(param_dtype, adamw, grid, s, g, master, m, v, param_at_0,
-                                         S, real, flag, sc);
+        return adam_dispatch_p<ZERO_F16>(param_dtype, adamw, sc_dev, grid, s, g, master, m, v,
+                                         param_at_0, S, real, flag, sc);
     }
-    return adam_dispatch_p<ZERO_BF16>(param_dtype, adamw, grid, s, g, master, m, v, param_at_0, S,
-                                      real, flag, sc);
+    return adam_dispatch_p<ZERO_BF16>(param_dtype, adamw, sc_dev, grid, s, g, master, m, v,
+                                      param_at_0, S, real, flag, sc);
 }
 
 hipError_t launch_write_param(const float* master, uint16_t* param_at_0, int64_t real,
@@ -417,6 +470,17 @@ hipError_t launch_write_param(const float* master, uint16_t* param_at_0, int64_t
 
 hipError_t launch_flag_clear(int* flag, hipStream_t s) {
     hipLaunchKernelGGL(flag_clear_kernel, dim3(1), dim3(1), 0, s, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_prologue(const int* flag, const DeviceStep* st, AdamScalars* out,
+                                const zero_adam_hparams_t& hp, hipStream_t s) {
+    hipLaunchKernelGGL(step_prologue_kernel, dim3(1), dim3(1), 0, s, flag, st, out, hp);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_epilogue(int* flag, DeviceStep* st, hipStream_t s) {
+    hipLaunchKernelGGL(step_epilogue_kernel, dim3(1), dim3(1), 0, s, flag, st);
     return hipGetLastError();
 }
 
