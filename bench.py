@@ -170,6 +170,57 @@ def run_graph(bufs, steps, warmup, device):
     return wall
 
 
+def run_offload(w, steps, warmup, device, n_threads):
+    """ZeRO-Offload: fp32 master / moments in host memory, the update on the
+    host cores, gradients and parameters crossing PCIe; timed with the
+    one-step delayed update (lag 1) and serialised (lag 0)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import zero_partitioned_mixed_plan_amd as z
+
+    plan, dmaster, dm, dv, flat, param, grads = setup(w, device)
+    del dm, dv
+    S, real, begin = plan.S, plan.real, plan.begin
+    master = np.zeros(S, np.float32)
+    master[:real] = dmaster[:real].cpu().numpy()
+    del dmaster
+    torch.cuda.empty_cache()
+    hp = z.AdamHParams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.adamw)
+    out = {"isa": z.zero_cpu_isa(), "host_threads": n_threads}
+    for lag in (1, 0):
+        m = np.zeros(S, np.float32)
+        v = np.zeros(S, np.float32)
+        scaler = z.LossScaler(w.init_scale if w.dynamic_scale else 1.0, dynamic=w.dynamic_scale)
+        z.zero_state_upload(plan, 0, scaler)
+        off = z.Offload(plan, hp, w.grad_dtype, w.param_dtype, master, m, v, n_threads=n_threads)
+
+        def step():
+            off.wait_params(lag)
+            z.zero_flatten_grads(plan, -1, grads, flat)
+            off.submit(flat, param, begin)
+
+        for _ in range(warmup):
+            step()
+        off.drain()
+        h0 = off.stats()["host_ms_total"]
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        off.drain()
+        wall = time.perf_counter() - t0
+        st = off.stats()
+        host_ms = (st["host_ms_total"] - h0) / steps
+        off.close()
+        out[f"lag{lag}"] = {"ms_per_step": wall * 1000.0 / steps, "host_update_ms": host_ms,
+                            "value": real / (wall / steps),
+                            "host_update_params_per_s": S / (host_ms * 1e-3),
+                            "host_update_gbps": ADAM_BYTES_PER_ELEM * S / (host_ms * 1e-3) / 1e9}
+        log(f"[bench] offload lag={lag}: {out[f'lag{lag}']}")
+    return plan, out
+
+
 def cpu_baseline(w, plan_S, plan_begin, target_s=12.0, window=1 << 24):
     """The oracle (single thread, as it stands) on a bounded window of the same
     shard: flatten + overflow test + AdamW + half cast, repeated until about
@@ -255,6 +306,11 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay measurement of the same step")
+    ap.add_argument("--mode", choices=["device", "offload"], default="device",
+                    help="device: the whole step on the GPU (default); offload: ZeRO-Offload "
+                         "(host-resident state, host update, one-step delayed update)")
+    ap.add_argument("--host-threads", type=int,
+                    default=int(os.environ.get("OMP_NUM_THREADS", "16")))
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run only a plain copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
@@ -275,6 +331,18 @@ def main(argv=None):
 
     from synth.workloads import get
     w = get(args.workload)
+    if args.mode == "offload":
+        plan, res = run_offload(w, args.steps, args.warmup, device, args.host_threads)
+        print(json.dumps({
+            "metric": METRIC, "value": res["lag1"]["value"], "unit": "params/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["lag1"]["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": w.description, "mode": "offload (ZeRO-Offload, host update, "
+                       "one-step delayed parameter update)", "shard_elems": plan.S,
+                       "real_elems": plan.real},
+            "offload": res}), flush=True)
+        return 0
     plan, wall, times, state, bufs = run_gpu(w, args.steps, args.warmup, device)
     graph_wall = None if args.no_graph else run_graph(bufs, args.steps, args.warmup, device)
     S, real, begin = plan.S, plan.real, plan.begin

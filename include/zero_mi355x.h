@@ -278,6 +278,104 @@ int zero_adam_step_async(zero_plan_t* plan, const zero_adam_hparams_t* hp, const
                          void* param, int64_t param_base, int64_t param_numel,
                          int32_t param_dtype, void* stream);
 
+/* ------------------------------------------------------------------------
+ * ZeRO-Offload: the rank's optimizer state in host memory, the update on
+ * the host cores ([legal] offload list, CPU-offload bullet: optimizer states
+ * in CPU DRAM, Adam on the CPU while the GPU runs forward and backward;
+ * [genomic] offload list, CPU-offload bullet: fp32 master weights and
+ * optimizer states in CPU RAM, half parameters and gradients on the GPU).
+ * ---------------------------------------------------------------------- */
+
+/* The update of zero_adam_step, run on the host over HOST buffers: same
+ * scalars, same operation order, same rounding, so the result is bit for
+ * bit that of the device update.  flat_grad: S half gradients (2-byte
+ * aligned); master / exp_avg / exp_avg_sq: S floats each (4-byte aligned);
+ * param (may be NULL): host buffer holding flat indices [param_base,
+ * param_base + param_numel), which must contain the shard's real range.
+ * overflow: 1 = skip (nothing written), 0 = apply, -1 = test flat_grad for
+ * inf/NaN here first.  n_threads (1..1024): host threads; the result does
+ * not depend on it.  Returns 0 applied, 1 skipped, or a negative error
+ * (ZERO_ENULL, ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOMEM).  Needs no GPU. */
+int zero_cpu_adam_step(const zero_plan_t* plan, const zero_adam_hparams_t* hp, int64_t step,
+                       double loss_scale, const void* flat_grad, int32_t grad_dtype,
+                       float* master, float* exp_avg, float* exp_avg_sq, void* param,
+                       int64_t param_base, int64_t param_numel, int32_t param_dtype,
+                       int32_t overflow, int32_t n_threads);
+
+/* Name of the host instruction set the update uses: "avx512", "avx2" or
+ * "scalar" (environment variable ZERO_CPU_ISA may force a narrower one). */
+const char* zero_cpu_isa(void);
+
+/* The offloaded step as a pipeline, with the one-step delayed parameter
+ * update ([legal] offload list, DPU bullet: the CPU optimizer step of one
+ * iteration overlaps the next iteration's forward pass; [genomic] offload
+ * list, DPU bullet).  Per step, after zero_flatten_grads on the caller's
+ * stream, zero_offload_submit enqueues there a one-thread snapshot (the
+ * flag, t + 1 and the scale of this step; then the loss-scale policy on the
+ * device state, flag cleared) and the copy of the flat gradient shard into
+ * one of two pinned host buffers, and returns.  A library thread then runs
+ * the host update of that step (zero_cpu_adam_step's arithmetic) and copies
+ * the half parameters to the rank's offset on its own stream, ordered after
+ * the caller's release of the previous parameters: the next submit, a
+ * zero_offload_wait_params or zero_offload_drain.  At most two steps are in
+ * flight; a submit waits (host) for the older one when needed.
+ *
+ * A training loop with the delayed update:
+ *   for each step: zero_offload_wait_params(o, 1, s);   forward(s); backward(s);
+ *                  zero_flatten_grads(..., s);  zero_offload_submit(o, ..., s);
+ *   zero_offload_drain(o, s);
+ * With lag 0 instead of 1 the step is serialised (no overlap). */
+typedef struct zero_offload zero_offload_t;
+
+typedef struct {
+    int64_t submitted;      /* steps submitted */
+    int64_t processed;      /* steps whose host part is done */
+    int64_t applied;        /* of those, updates applied */
+    int64_t skipped;        /* of those, overflow-skipped */
+    int32_t last_flag;      /* flag of the last processed step */
+    int32_t _pad;
+    double host_ms_last;    /* host update time of the last applied step */
+    double host_ms_total;
+} zero_offload_stats_t;
+
+/* Creates the pipeline for `plan`, whose device state must already hold t
+ * and the scaler (zero_state_upload).  master / exp_avg / exp_avg_sq: HOST
+ * fp32 arrays of S elements, owned by the caller and touched only by the
+ * library's thread until zero_offload_drain returns.  param_dtype: 0 for no
+ * parameter write-back.  Allocates two pinned gradient buffers (2 S bytes
+ * each), two pinned parameter buffers (2 real bytes each), a transfer
+ * stream and a worker thread.  Errors: ZERO_ENULL, ZERO_EINVAL, ZERO_ESTATE,
+ * ZERO_EHIP, ZERO_ENOMEM. */
+int zero_offload_create(zero_plan_t* plan, const zero_adam_hparams_t* hp, int32_t grad_dtype,
+                        int32_t param_dtype, float* master, float* exp_avg, float* exp_avg_sq,
+                        int32_t n_threads, zero_offload_t** out);
+
+/* Submits one step: flat_grad is the device flat gradient shard just
+ * flattened on `stream`; param the device parameter buffer holding flat
+ * indices [param_base, param_base + param_numel) (may be NULL when
+ * param_dtype is 0).  Errors: ZERO_ENULL, ZERO_EINVAL, ZERO_EALIGN,
+ * ZERO_EHIP, ZERO_ESTATE, or the worker's error. */
+int zero_offload_submit(zero_offload_t* off, const void* flat_grad, void* param,
+                        int64_t param_base, int64_t param_numel, void* stream);
+
+/* Makes `stream` wait (on the device) until the parameters of every
+ * submitted step except the last `lag` are in the device buffer; the host
+ * waits only for the host update of those steps.  lag is 1 (the one-step
+ * delayed update) or 0 (serialised).  Call it before each forward: the
+ * parameters it releases are overwritten only after the next submit.
+ * Errors: ZERO_ENULL, ZERO_EINVAL, ZERO_ESTATE, ZERO_EHIP, or the worker's. */
+int zero_offload_wait_params(zero_offload_t* off, int32_t lag, void* stream);
+
+/* Waits (host) until every submitted step is complete, parameters copied. */
+int zero_offload_drain(zero_offload_t* off, void* stream);
+
+/* Counters of the pipeline; returns the worker's error, if any. */
+int zero_offload_stats(zero_offload_t* off, zero_offload_stats_t* out);
+
+/* Completes the submitted steps, then releases the thread, stream and
+ * buffers (NULL is a no-op). */
+void zero_offload_destroy(zero_offload_t* off);
+
 /* Message of the calling thread's last error ("" if none). */
 const char* zero_last_error(void);
 

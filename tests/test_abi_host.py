@@ -180,3 +180,30 @@ def test_async_step_argument_errors_before_device_work():
     sc = _abi.zero_scaler_t(1024.0, 1.0, 0.5, 2.0, 10, 0, 1, 0)
     assert lib.zero_state_upload(plan.handle, -1, ctypes.byref(sc), None) == _abi.ZERO_EINVAL
     assert lib.zero_state_upload(None, 0, ctypes.byref(sc), None) == _abi.ZERO_ENULL
+
+
+def test_offload_argument_errors_before_device_work():
+    lib = _abi.lib
+    plan = z.zero_partition_plan([1000], 2, 0, 8)
+    hp = z.AdamHParams().to_c()
+    fake = 1 << 20
+    out = ctypes.c_void_p()
+    create = lib.zero_offload_create
+    assert create(plan.handle, ctypes.byref(hp), z.ZERO_BF16, z.ZERO_BF16, fake, fake, fake, 4,
+                  None) == _abi.ZERO_ENULL
+    assert create(plan.handle, ctypes.byref(hp), 9, z.ZERO_BF16, fake, fake, fake, 4,
+                  ctypes.byref(out)) == _abi.ZERO_EINVAL
+    assert create(plan.handle, ctypes.byref(hp), z.ZERO_BF16, 7, fake, fake, fake, 4,
+                  ctypes.byref(out)) == _abi.ZERO_EINVAL
+    assert create(plan.handle, ctypes.byref(hp), z.ZERO_BF16, z.ZERO_BF16, fake, fake, fake, 0,
+                  ctypes.byref(out)) == _abi.ZERO_EINVAL
+    assert create(plan.handle, ctypes.byref(hp), z.ZERO_BF16, z.ZERO_BF16, None, fake, fake, 4,
+                  ctypes.byref(out)) == _abi.ZERO_ENULL
+    # the device state must be uploaded first
+    assert create(plan.handle, ctypes.byref(hp), z.ZERO_BF16, z.ZERO_BF16, fake, fake, fake, 4,
+                  ctypes.byref(out)) == _abi.ZERO_ESTATE
+    assert out.value is None
+    assert lib.zero_offload_submit(None, fake, fake, 0, 1, None) == _abi.ZERO_ENULL
+    assert lib.zero_offload_wait_params(None, 1, None) == _abi.ZERO_ENULL
+    assert lib.zero_offload_drain(None, None) == _abi.ZERO_ENULL
+    lib.zero_offload_destroy(None)

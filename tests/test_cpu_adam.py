@@ -1,0 +1,134 @@
+"""ZeRO-Offload's host-side update (zero_cpu_adam_step) against the oracle,
+on the CPU: every instruction-set path (forced with ZERO_CPU_ISA), several
+thread counts, fp16 and bf16, Adam-L2 and AdamW, padding, skipped steps and
+a sweep of fp32 patterns through the parameter cast.  Bar: bit-identical
+master / moments / parameters (the same arithmetic as the device update)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import zero_partitioned_mixed_plan_amd as z
+
+ISAS = ["avx512", "avx2", "scalar"]
+
+
+@pytest.fixture(params=ISAS)
+def isa(request, monkeypatch):
+    monkeypatch.setenv("ZERO_CPU_ISA", request.param)
+    if request.param != "scalar" and z.zero_cpu_isa() != request.param:
+        pytest.skip(f"this host has no {request.param}")
+    assert z.zero_cpu_isa() == request.param
+    return request.param
+
+
+def _grads(rng, n, dt, scale, sigma=1e-2):
+    vals = (rng.normal(0, sigma, n) * scale).astype(np.float32)
+    if dt == "f16":
+        return vals.astype(np.float16).view(np.uint16)
+    import torch
+    return torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("gdt,pdt,adamw", [("f16", "f16", True), ("bf16", "bf16", True),
+                                           ("bf16", "f16", False), ("f16", "bf16", False)])
+@pytest.mark.parametrize("threads", [1, 3, 8])
+def test_host_update_equals_oracle(isa, gdt, pdt, adamw, threads):
+    numels = [1000, 37, 5, 2049, 1]          # P = 3092; R = 3, A = 8 -> S = 1032, padding on rank 2
+    rng = np.random.default_rng(7)
+    for r in range(3):
+        plan = z.zero_partition_plan(numels, 3, r, 8)
+        S, real, begin = plan.S, plan.real, plan.begin
+        master = np.zeros(S, np.float32)
+        master[:real] = rng.normal(0, 0.02, real).astype(np.float32)
+        om, omo, ov = master.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32)
+        gm, gmo, gv = master.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32)
+        P = sum(numels)
+        oparam = np.full(P, 0xABCD, np.uint16)
+        gparam = oparam.copy()
+        hp = z.AdamHParams(weight_decay=0.05, adamw=adamw)
+        scale = 1024.0 if gdt == "f16" else 1.0
+        for t in range(1, 5):
+            flat = np.zeros(S, np.uint16)
+            flat[:real] = _grads(rng, real, gdt, scale)
+            o = oracle.adam_step(t, scale, flat, gdt, om, omo, ov, lr=hp.lr, b1=hp.beta1,
+                                 b2=hp.beta2, eps=hp.eps, wd=hp.weight_decay, adamw=adamw)
+            oracle.write_param(om, real, begin, 0, oparam, pdt)
+            g = z.zero_cpu_adam_step(plan, hp, t, scale, flat, gm, gmo, gv, gparam, 0,
+                                     grad_dtype=gdt, param_dtype=pdt, n_threads=threads)
+            assert g == o == 0
+            for a, b in ((gm, om), (gmo, omo), (gv, ov)):
+                assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (isa, r, t)
+            assert np.array_equal(gparam, oparam), (isa, r, t)
+
+
+def test_overflow_skips_and_leaves_state_untouched(isa):
+    plan = z.zero_partition_plan([5000], 1, 0, 1)
+    rng = np.random.default_rng(1)
+    for bad in (0x7C00, 0xFC00, 0x7E00, 0x7C01):
+        for pos in (0, 17, 4095, 4999):
+            flat = _grads(rng, 5000, "f16", 1.0)
+            flat[pos] = bad
+            m0 = rng.normal(0, 0.02, 5000).astype(np.float32)
+            master, mo, v = m0.copy(), np.ones(5000, np.float32), np.ones(5000, np.float32)
+            param = np.zeros(5000, np.uint16)
+            assert z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, flat, master, mo, v, param,
+                                        grad_dtype="f16", param_dtype="f16") == 1
+            assert np.array_equal(master, m0) and np.all(mo == 1) and np.all(v == 1)
+            assert not param.any()
+    # a known flag overrides the test; the largest finite value does not trip
+    flat = np.full(5000, 0x7BFF, np.uint16)
+    master = np.zeros(5000, np.float32)
+    z1, z2 = np.zeros(5000, np.float32), np.zeros(5000, np.float32)
+    assert z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, flat, master, z1, z2,
+                                grad_dtype="f16", overflow=1) == 1
+    assert z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, flat, master, z1, z2,
+                                grad_dtype="f16") == 0
+
+
+@pytest.mark.parametrize("pdt", ["f16", "bf16"])
+def test_parameter_cast_sweep(isa, pdt):
+    """lr = 0 and zero gradients leave the master unchanged, so the written
+    parameters are the cast of the master: every fp32 exponent, both
+    parities of the last kept bit, ties and their neighbours."""
+    lows = []
+    for b in range(8):
+        for lo in (0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x0ABC, 0x1555):
+            lows.append((b << 13) | lo)
+    lows = np.array(sorted(set(lows)), dtype=np.uint32)
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    x = (hi[:, None] | lows[None, :]).ravel().view(np.float32)
+    n = x.size
+    plan = z.zero_partition_plan([n], 1, 0, 1)
+    master = x.copy()
+    param = np.zeros(n, np.uint16)
+    flat = np.zeros(n, np.uint16)
+    hp = z.AdamHParams(lr=0.0, weight_decay=0.0)
+    assert z.zero_cpu_adam_step(plan, hp, 1, 1.0, flat, master, np.zeros(n, np.float32),
+                                np.zeros(n, np.float32), param, grad_dtype="bf16",
+                                param_dtype=pdt, overflow=0, n_threads=4) == 0
+    nan = np.isnan(x)
+    assert np.array_equal(master[~nan].view(np.uint32), x[~nan].view(np.uint32))
+    exp = oracle.float_to_half(x, pdt)
+    assert np.array_equal(param[~nan], exp[~nan])
+    emask, frac = (0x7C00, 0x03FF) if pdt == "f16" else (0x7F80, 0x007F)
+    assert np.all((param[nan] & emask) == emask) and np.all((param[nan] & frac) != 0)
+
+
+def test_argument_errors():
+    plan = z.zero_partition_plan([100], 1, 0, 1)
+    f = np.zeros(100, np.float32)
+    g = np.zeros(100, np.uint16)
+    with pytest.raises(z.ZeroError):
+        z.zero_cpu_adam_step(plan, z.AdamHParams(), 0, 1.0, g, f, f.copy(), f.copy(),
+                             grad_dtype="bf16")
+    with pytest.raises(z.ZeroError):
+        z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, g, f, f.copy(), f.copy(),
+                             grad_dtype="bf16", overflow=2)
+    with pytest.raises(z.ZeroError):
+        z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, g, f, f.copy(), f.copy(),
+                             np.zeros(10, np.uint16), grad_dtype="bf16", param_dtype="bf16")
+    with pytest.raises(ValueError):
+        z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, g[:10], f, f.copy(), f.copy(),
+                             grad_dtype="bf16")

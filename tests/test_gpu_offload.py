@@ -1,0 +1,111 @@
+"""ZeRO-Offload pipeline (zero_offload_*) on the GPU against the oracle.
+
+Each iteration: wait_params(lag), a stand-in "forward" that copies the
+device parameter buffer, the gradients of the iteration copied to the
+device, zero_flatten_grads, submit.  Checked:
+  * what the forward of iteration it sees is exactly the oracle's parameters
+    after iteration it - 1 - lag (lag 1: the one-step delayed update; lag 0:
+    the serialised step) -- so the parameter copy never lands early or late;
+  * the device loss scale before each iteration equals the oracle's;
+  * after drain: host master / moments and the device parameters equal the
+    oracle's bit for bit, and the applied / skipped counts match.
+"""
+import numpy as np
+import pytest
+
+import zero_partitioned_mixed_plan_amd as z
+from harness import Case, OracleRun, host_model_grads, init_master_host, init_param_host, log, \
+    torch_dtype
+from synth.workloads import get
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [3000, 1, 7, 100003, 65, 2048, 511, 300000, 13, 0, 4099, 77777]
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _offload_run(case, lag, label, write_params=True, n_threads=4):
+    import torch
+    dev = torch.device("cuda:0")
+    orc = OracleRun(case)
+    op = orc.plan
+    plan = z.zero_partition_plan(case.numels, case.world_size, case.rank, case.align,
+                                 case.bucket_elems)
+    S, real, begin = plan.S, plan.real, plan.begin
+    hp = z.AdamHParams(case.lr, case.beta1, case.beta2, case.eps, case.weight_decay, case.adamw)
+    scaler = z.LossScaler(case.init_scale, dynamic=case.dynamic, window=case.window)
+    z.zero_state_upload(plan, 0, scaler)
+    master = init_master_host(case, begin, real, S)
+    mom = np.zeros(S, np.float32)
+    var = np.zeros(S, np.float32)
+    gdt = torch_dtype(case.grad_dtype)
+    param = torch.from_numpy(init_param_host(case, op.P).view(np.int16)).to(dev).view(
+        torch_dtype(case.param_dtype))
+    flat = torch.empty(max(S, 1), dtype=gdt, device=dev)
+    off = z.Offload(plan, hp, case.grad_dtype, case.param_dtype if write_params else None,
+                    master, mom, var, n_threads=n_threads)
+    hist = [orc.params().copy()]       # oracle parameters after iteration k
+    skipped = 0
+    log(f"[offload] {label}: S={S} real={real} lag={lag} steps={case.steps}")
+    for it in range(1, case.steps + 1):
+        off.wait_params(lag)
+        seen = param.clone()          # the forward of this iteration reads the parameters
+        st = z.zero_state_download(plan)
+        o_ovf, grads, o_scale = orc.step(it)
+        assert st.scale == o_scale, f"{label} it={it}: device scale {st.scale} vs {o_scale}"
+        grads_dev = [None if g is None else torch.from_numpy(g.view(np.int16)).to(dev).view(gdt)
+                     for g in grads]
+        z.zero_flatten_grads(plan, -1, grads_dev, flat)
+        off.submit(flat, param if write_params else None, 0)
+        skipped += o_ovf
+        hist.append(orc.params().copy())
+        if write_params:
+            want = hist[max(it - 1 - lag, 0)]
+            assert np.array_equal(_bits(seen), want), \
+                f"{label} it={it}: the forward saw other parameters than iteration {it - 1 - lag}'s"
+    off.drain()
+    stats = off.stats()
+    assert stats["applied"] == orc.t and stats["skipped"] == skipped, stats
+    st = z.zero_state_download(plan)
+    assert (st.applied_steps, st.skipped_steps, st.scale) == (orc.t, skipped, orc.scaler.value)
+    for name, a, b in (("master", master, orc.master), ("m", mom, orc.m), ("v", var, orc.v)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{label}: {name} differs"
+    final = _bits(param)
+    if write_params:
+        assert np.array_equal(final, hist[-1]), f"{label}: final parameters differ"
+    else:
+        assert np.array_equal(final, hist[0]), f"{label}: parameters written without param_dtype"
+    off.close()
+    log(f"[offload] {label}: ok, applied {orc.t}, skipped {skipped}, "
+        f"host ms last {stats['host_ms_last']:.2f}")
+    return skipped
+
+
+@pytest.mark.parametrize("lag", [1, 0])
+def test_offload_tiny_with_overflow_at_step_four(lag):
+    case = Case.from_workload(get("tiny"), inject={4: 2624 // 2})
+    assert _offload_run(case, lag, f"tiny lag={lag}") == 1
+
+
+@pytest.mark.parametrize("lag", [1, 0])
+def test_offload_ragged_scaler_growth_and_backoff(lag):
+    case = Case(numels=RAGGED, world_size=2, rank=1, grad_dtype="f16", param_dtype="f16",
+                steps=10, dynamic=True, init_scale=512.0, window=2,
+                inject={2: 5, 3: 100000, 7: 1})
+    assert _offload_run(case, lag, f"ragged lag={lag}") == 3
+
+
+def test_offload_bf16_padding_rank_and_no_param_write():
+    case = Case(numels=RAGGED, world_size=3, rank=2, grad_dtype="bf16", param_dtype="bf16",
+                steps=4, grad_sigma=1e-2, adamw=False, weight_decay=0.1)
+    _offload_run(case, 1, "bf16 adam-l2")
+    _offload_run(case, 1, "bf16 no param write", write_params=False)
+
+
+def test_offload_gpt2_small():
+    case = Case.from_workload(get("gpt2_small"), steps=6)
+    _offload_run(case, 1, "gpt2_small", n_threads=8)

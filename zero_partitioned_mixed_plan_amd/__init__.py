@@ -20,6 +20,17 @@ and the step without host round trips (graph-capturable):
                          param=None, param_base=0, stream=None)
     zero_state_download(plan, stream=None) -> DeviceStepState
     zero_state_device_scale(plan) -> device address of the loss scale (double)
+
+and ZeRO-Offload's host-side update (host buffers: numpy arrays or CPU tensors):
+
+    zero_cpu_adam_step(plan, hparams, step, loss_scale, flat_grad, master, exp_avg,
+                       exp_avg_sq, param=None, param_base=0, grad_dtype=None,
+                       param_dtype=None, overflow=-1, n_threads=None) -> 0 | 1
+    zero_cpu_isa() -> "avx512" | "avx2" | "scalar"
+    Offload(plan, hparams, grad_dtype, param_dtype, master, exp_avg, exp_avg_sq,
+            n_threads=None)     .submit / .wait_params / .drain / .stats / .close
+                                (zero_offload_* : the pipelined offloaded step with the
+                                 one-step delayed parameter update)
 """
 from __future__ import annotations
 
@@ -34,7 +45,8 @@ __all__ = ["Plan", "AdamHParams", "LossScaler", "DeviceStepState", "ZeroError",
            "zero_partition_plan", "zero_flatten_grads", "zero_adam_step",
            "zero_update_loss_scale", "zero_write_param_shard", "zero_state_upload",
            "zero_adam_step_async", "zero_state_download", "zero_state_device_scale",
-           "zero_last_error", "ZERO_F16", "ZERO_BF16"]
+           "zero_cpu_adam_step", "zero_cpu_isa", "Offload", "zero_last_error", "ZERO_F16",
+           "ZERO_BF16"]
 
 
 def _torch():
@@ -291,6 +303,126 @@ def zero_adam_step_async(plan: Plan, hparams: AdamHParams, flat_grad, master, ex
                                    int(param_base), pnum, pdt,
                                    _stream_handle(stream, master.device)),
           "zero_adam_step_async")
+
+
+_HALF_CODES = {"f16": ZERO_F16, "bf16": ZERO_BF16, ZERO_F16: ZERO_F16, ZERO_BF16: ZERO_BF16}
+
+
+def _host_buffer(x, name: str, min_numel: int, itemsize: int):
+    """(address, numel) of a contiguous host buffer: a numpy array or a CPU tensor."""
+    torch = _torch()
+    if isinstance(x, torch.Tensor):
+        if x.is_cuda:
+            raise ValueError(f"{name} must be host memory")
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        addr, n, isz = x.data_ptr(), x.numel(), x.element_size()
+    else:
+        import numpy as np
+        if not isinstance(x, np.ndarray) or not x.flags.c_contiguous:
+            raise ValueError(f"{name} must be a contiguous numpy array or CPU tensor")
+        addr, n, isz = x.ctypes.data, x.size, x.itemsize
+    if isz != itemsize:
+        raise TypeError(f"{name} has {isz}-byte elements, expected {itemsize}")
+    if n < min_numel:
+        raise ValueError(f"{name} holds {n} elements, needs >= {min_numel}")
+    return addr, n
+
+
+def _half_code(x, given):
+    if given is not None:
+        return _HALF_CODES[given]
+    torch = _torch()
+    if isinstance(x, torch.Tensor) and x.dtype in (torch.float16, torch.bfloat16):
+        return _dtype_code(x)
+    raise TypeError("pass grad_dtype / param_dtype ('f16' or 'bf16') for raw 16-bit buffers")
+
+
+def zero_cpu_adam_step(plan: Plan, hparams: AdamHParams, step: int, loss_scale: float, flat_grad,
+                       master, exp_avg, exp_avg_sq, param=None, param_base: int = 0,
+                       grad_dtype=None, param_dtype=None, overflow: int = -1,
+                       n_threads: Optional[int] = None) -> int:
+    """ZeRO-Offload's update on host buffers; returns 0 applied, 1 skipped.
+    overflow: -1 tests flat_grad here, 0 / 1 pass a known flag."""
+    import os
+    g, _ = _host_buffer(flat_grad, "flat_grad", plan.S, 2)
+    ptrs = [_host_buffer(t, name, plan.S, 4)[0] for name, t in
+            (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq))]
+    pptr, pnum, pdt = None, 0, 0
+    if param is not None:
+        pptr, pnum = _host_buffer(param, "param", 0, 2)
+        pdt = _half_code(param, param_dtype)
+    if n_threads is None:
+        n_threads = max(1, min(16, os.cpu_count() or 1))
+    hp = hparams.to_c()
+    return check(lib.zero_cpu_adam_step(plan.handle, ctypes.byref(hp), int(step),
+                                        float(loss_scale), g, _half_code(flat_grad, grad_dtype),
+                                        *ptrs, pptr, int(param_base), pnum, pdt, int(overflow),
+                                        int(n_threads)), "zero_cpu_adam_step")
+
+
+def zero_cpu_isa() -> str:
+    return lib.zero_cpu_isa().decode()
+
+
+class Offload:
+    """ZeRO-Offload pipeline of one rank (zero_offload_*): host-resident fp32
+    master / moments, host update on a library thread, parameters copied
+    back with the one-step delayed update.  The plan's device state must be
+    uploaded first (zero_state_upload).  The host arrays must stay alive and
+    untouched until drain() returns."""
+
+    def __init__(self, plan: Plan, hparams: AdamHParams, grad_dtype, param_dtype, master,
+                 exp_avg, exp_avg_sq, n_threads: Optional[int] = None):
+        import os
+        self.plan = plan
+        self._keep = (master, exp_avg, exp_avg_sq)
+        ptrs = [_host_buffer(t, name, plan.S, 4)[0] for name, t in
+                (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq))]
+        if n_threads is None:
+            n_threads = max(1, min(16, os.cpu_count() or 1))
+        pdt = 0 if param_dtype is None else _HALF_CODES[param_dtype]
+        hp = hparams.to_c()
+        h = ctypes.c_void_p()
+        check(lib.zero_offload_create(plan.handle, ctypes.byref(hp), _HALF_CODES[grad_dtype], pdt,
+                                      *ptrs, int(n_threads), ctypes.byref(h)),
+              "zero_offload_create")
+        self._h = h
+
+    def _stream(self, stream):
+        torch = _torch()
+        return _stream_handle(stream, torch.device("cuda", torch.cuda.current_device()))
+
+    def submit(self, flat_grad, param=None, param_base: int = 0, stream=None) -> None:
+        torch = _torch()
+        _require(flat_grad, "flat_grad", self.plan.S, (torch.float16, torch.bfloat16))
+        pptr, pnum = None, 0
+        if param is not None:
+            _require(param, "param", 0, (torch.float16, torch.bfloat16))
+            pptr, pnum = param.data_ptr(), param.numel()
+        check(lib.zero_offload_submit(self._h, flat_grad.data_ptr(), pptr, int(param_base), pnum,
+                                      self._stream(stream)), "zero_offload_submit")
+
+    def wait_params(self, lag: int = 1, stream=None) -> None:
+        check(lib.zero_offload_wait_params(self._h, int(lag), self._stream(stream)),
+              "zero_offload_wait_params")
+
+    def drain(self, stream=None) -> None:
+        check(lib.zero_offload_drain(self._h, self._stream(stream)), "zero_offload_drain")
+
+    def stats(self) -> dict:
+        st = _abi.zero_offload_stats_t()
+        check(lib.zero_offload_stats(self._h, ctypes.byref(st)), "zero_offload_stats")
+        return {k: getattr(st, k) for k, _ in st._fields_ if k != "_pad"}
+
+    def close(self) -> None:
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.zero_offload_destroy(h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
 
 
 def zero_last_error() -> str:

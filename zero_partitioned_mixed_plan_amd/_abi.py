@@ -48,6 +48,13 @@ class zero_adam_hparams_t(ctypes.Structure):
                 ("adamw", ctypes.c_int32), ("_pad", ctypes.c_int32)]
 
 
+class zero_offload_stats_t(ctypes.Structure):
+    _fields_ = [("submitted", ctypes.c_int64), ("processed", ctypes.c_int64),
+                ("applied", ctypes.c_int64), ("skipped", ctypes.c_int64),
+                ("last_flag", ctypes.c_int32), ("_pad", ctypes.c_int32),
+                ("host_ms_last", ctypes.c_double), ("host_ms_total", ctypes.c_double)]
+
+
 class zero_scaler_t(ctypes.Structure):
     _fields_ = [("scale", ctypes.c_double), ("min_scale", ctypes.c_double),
                 ("backoff", ctypes.c_double), ("growth", ctypes.c_double),
@@ -79,6 +86,17 @@ SIGNATURES = {
     "zero_state_device_scale": (ctypes.c_int, [_VP, ctypes.POINTER(_VP)]),
     "zero_adam_step_async": (ctypes.c_int, [_VP, ctypes.POINTER(zero_adam_hparams_t), _VP, _I32,
                                             _VP, _VP, _VP, _VP, _I64, _I64, _I32, _VP]),
+    "zero_cpu_adam_step": (ctypes.c_int, [_VP, ctypes.POINTER(zero_adam_hparams_t), _I64,
+                                          ctypes.c_double, _VP, _I32, _VP, _VP, _VP, _VP, _I64,
+                                          _I64, _I32, _I32, _I32]),
+    "zero_cpu_isa": (ctypes.c_char_p, []),
+    "zero_offload_create": (ctypes.c_int, [_VP, ctypes.POINTER(zero_adam_hparams_t), _I32, _I32,
+                                           _VP, _VP, _VP, _I32, ctypes.POINTER(_VP)]),
+    "zero_offload_submit": (ctypes.c_int, [_VP, _VP, _VP, _I64, _I64, _VP]),
+    "zero_offload_wait_params": (ctypes.c_int, [_VP, _I32, _VP]),
+    "zero_offload_drain": (ctypes.c_int, [_VP, _VP]),
+    "zero_offload_stats": (ctypes.c_int, [_VP, ctypes.POINTER(zero_offload_stats_t)]),
+    "zero_offload_destroy": (None, [_VP]),
     "zero_last_error": (ctypes.c_char_p, []),
     "zero_plan_set_timing": (ctypes.c_int, [_VP, _I32]),
     "zero_plan_kernel_ms": (ctypes.c_int, [_VP, _I32, ctypes.POINTER(ctypes.c_float)]),

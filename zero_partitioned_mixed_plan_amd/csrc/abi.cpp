@@ -533,6 +533,58 @@ int zero_write_param_shard(zero_plan_t* p, const float* master, void* param, int
     return timer_stop(p, kTimerWrite, s);
 }
 
+int zero_cpu_adam_step(const zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step,
+                       double loss_scale, const void* flat_grad, int32_t grad_dtype,
+                       float* master, float* exp_avg, float* exp_avg_sq, void* param,
+                       int64_t param_base, int64_t param_numel, int32_t param_dtype,
+                       int32_t overflow, int32_t n_threads) {
+    if (p == nullptr || hp == nullptr) return fail(ZERO_ENULL, "plan or hparams is NULL");
+    if (!valid_dtype(grad_dtype)) return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16");
+    if (step < 1) return fail(ZERO_EINVAL, "step must be >= 1");
+    if (!(std::isfinite(loss_scale) && loss_scale > 0)) {
+        return fail(ZERO_EINVAL, "loss_scale must be finite and > 0");
+    }
+    if (overflow < -1 || overflow > 1) return fail(ZERO_EINVAL, "overflow must be -1, 0 or 1");
+    if (n_threads < 1 || n_threads > 1024) return fail(ZERO_EINVAL, "n_threads must be in [1, 1024]");
+    int rc = check_hparams(hp);
+    if (rc != ZERO_OK) return rc;
+    if (p->S > 0 && (flat_grad == nullptr || master == nullptr || exp_avg == nullptr ||
+                     exp_avg_sq == nullptr)) {
+        return fail(ZERO_ENULL, "flat_grad, master, exp_avg and exp_avg_sq must be non-NULL");
+    }
+    if ((reinterpret_cast<uintptr_t>(flat_grad) & 1u) != 0 || !aligned4(master) ||
+        !aligned4(exp_avg) || !aligned4(exp_avg_sq)) {
+        return fail(ZERO_EALIGN, "flat_grad must be 2-byte and the fp32 arrays 4-byte aligned");
+    }
+    uint16_t* param0 = nullptr;
+    rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
+    if (rc != ZERO_OK) return rc;
+    const uint16_t* g = static_cast<const uint16_t*>(flat_grad);
+    const bool skip = overflow < 0 ? cpu_nonfinite(g, p->S, grad_dtype, n_threads) : overflow != 0;
+    if (skip) return 1;
+    CpuAdamArgs a;
+    a.g = g;
+    a.p = master;
+    a.m = exp_avg;
+    a.v = exp_avg_sq;
+    a.param = param0;
+    a.n = p->S;
+    a.real = p->real;
+    a.sc = make_scalars(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->adamw,
+                        static_cast<double>(step), loss_scale);
+    a.gdt = grad_dtype;
+    a.pdt = param_dtype;
+    a.adamw = hp->adamw != 0;
+    try {
+        cpu_adam(a, n_threads);
+    } catch (const std::exception& ex) {
+        return fail(ZERO_ENOMEM, std::string("host update failed: ") + ex.what());
+    }
+    return 0;
+}
+
+const char* zero_cpu_isa(void) { return cpu_isa_name(cpu_isa()); }
+
 const char* zero_last_error(void) { return g_last_error.c_str(); }
 
 int zero_plan_set_timing(zero_plan_t* p, int32_t on) {

@@ -1,0 +1,403 @@
+// Host-side Adam/AdamW over a rank's shard, for ZeRO-Offload: the fp32
+// master weights, momentum and variance live in host memory and the update
+// runs on the host cores ("ZeRO Optimization", inferensys glossary, legal
+// pre-training page, offload list, CPU-offload bullet; genomic MLOps page,
+// offload list, CPU-offload bullet).
+//
+// The arithmetic is the device update's, element for element: the same
+// fp32 scalars (make_scalars), the same operation order, one rounding per
+// operation (no FMA contraction: built with -ffp-contract=off and written
+// with separate multiply and add), IEEE division and square root (the
+// vector DIVPS / SQRTPS instructions are correctly rounded), and
+// round-to-nearest-even casts to fp16 (F16C conversion) or bf16 (integer
+// rounding on the fp32 bits).  The result therefore does not depend on the
+// instruction set or on the number of threads.
+//
+// Three code paths, picked at run time: AVX-512 (16 lanes), AVX2 + F16C
+// (8 lanes) and scalar.  ZERO_CPU_ISA=avx512|avx2|scalar forces one (tests
+// use it to cover every path on one machine).
+#include <immintrin.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+
+namespace zmi {
+namespace {
+
+constexpr uint32_t kF16ExpMask = 0x7C00u;
+constexpr uint32_t kBf16ExpMask = 0x7F80u;
+
+// ------------------------------------------------------------ scalar path
+// binary16 -> binary32, exact (integer decode).
+float f16_bits_to_f32(uint32_t h) {
+    const uint32_t sign = (h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 0x1Fu;
+    uint32_t f = h & 0x3FFu;
+    uint32_t out;
+    if (e == 0x1Fu) {
+        out = sign | 0x7F800000u | (f << 13) | (f ? 0x00400000u : 0u);  // inf / quiet NaN
+    } else if (e != 0) {
+        out = sign | ((e + 112u) << 23) | (f << 13);                   // normal: bias 15 -> 127
+    } else if (f == 0) {
+        out = sign;                                                    // +-0
+    } else {
+        // subnormal: normalise the fraction
+        int shift = 0;
+        while ((f & 0x400u) == 0) {
+            f <<= 1;
+            ++shift;
+        }
+        f &= 0x3FFu;
+        out = sign | ((113u - static_cast<uint32_t>(shift)) << 23) | (f << 13);
+    }
+    float x;
+    std::memcpy(&x, &out, 4);
+    return x;
+}
+
+// binary32 -> binary16, round to nearest even, on the integer bits.
+uint16_t f32_to_f16_bits(float x) {
+    uint32_t u;
+    std::memcpy(&u, &x, 4);
+    const uint32_t sign = (u >> 16) & 0x8000u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return static_cast<uint16_t>(sign | 0x7E00u | ((a >> 13) & 0x3FFu));
+    if (a >= 0x477FF000u) return static_cast<uint16_t>(sign | 0x7C00u);  // rounds past 65504
+    if (a >= 0x38800000u) {                                               // normal result
+        const uint32_t r = a + 0x0FFFu + ((a >> 13) & 1u);                // RNE at bit 13
+        return static_cast<uint16_t>(sign | ((r - 0x38000000u) >> 13));
+    }
+    // subnormal or zero result: value = a as fp32, quantum 2^-24
+    const uint32_t e = a >> 23;
+    if (e < 102) return static_cast<uint16_t>(sign);  // below half the smallest subnormal
+    const uint32_t mant = (a & 0x7FFFFFu) | 0x800000u;
+    const uint32_t shift = 126 - e;                   // 14..24
+    uint32_t q = mant >> shift;
+    const uint32_t rem = mant & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u))) ++q;
+    return static_cast<uint16_t>(sign | q);
+}
+
+// binary32 -> bfloat16, round to nearest even on the integer bits.
+uint16_t f32_to_bf16_bits(float x) {
+    uint32_t u;
+    std::memcpy(&u, &x, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+    return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+float bf16_bits_to_f32(uint32_t h) {
+    const uint32_t u = h << 16;
+    float x;
+    std::memcpy(&x, &u, 4);
+    return x;
+}
+
+template <int GDT, int PDT, bool ADAMW>
+void adam_scalar(const CpuAdamArgs& a, int64_t lo, int64_t hi) {
+    const AdamScalars& c = a.sc;
+    for (int64_t k = lo; k < hi; ++k) {
+        const float g = GDT == ZERO_F16 ? f16_bits_to_f32(a.g[k]) : bf16_bits_to_f32(a.g[k]);
+        float p = a.p[k];
+        float gu = g * c.inv_scale;
+        if (!ADAMW) gu = gu + c.wd * p;
+        const float m = c.b1 * a.m[k] + c.omb1 * gu;
+        const float v = c.b2 * a.v[k] + c.omb2 * (gu * gu);
+        const float d = __builtin_sqrtf(v) * c.rsbc2 + c.eps;
+        const float u = m / d;
+        p = p * c.decay - c.step * u;
+        a.p[k] = p;
+        a.m[k] = m;
+        a.v[k] = v;
+        if (PDT != 0 && k < a.real) {
+            a.param[k] = PDT == ZERO_F16 ? f32_to_f16_bits(p) : f32_to_bf16_bits(p);
+        }
+    }
+}
+
+bool nonfinite_scalar(const uint16_t* g, int64_t lo, int64_t hi, uint32_t mask) {
+    uint32_t any = 0;
+    for (int64_t k = lo; k < hi; ++k) any |= (g[k] & mask) == mask;
+    return any != 0;
+}
+
+// ------------------------------------------------------------ AVX2 + F16C
+#define ZMI_AVX2 __attribute__((target("avx2,f16c")))
+
+ZMI_AVX2 inline __m256i bf16_rne_avx2(__m256 p) {
+    const __m256i u = _mm256_castps_si256(p);
+    const __m256i lsb = _mm256_and_si256(_mm256_srli_epi32(u, 16), _mm256_set1_epi32(1));
+    __m256i r = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(u, _mm256_set1_epi32(0x7FFF)),
+                                                   lsb), 16);
+    const __m256i nan_bits = _mm256_or_si256(_mm256_srli_epi32(u, 16), _mm256_set1_epi32(0x40));
+    const __m256 isnan = _mm256_cmp_ps(p, p, _CMP_UNORD_Q);
+    return _mm256_blendv_epi8(r, nan_bits, _mm256_castps_si256(isnan));
+}
+
+// 8 uint32 (each <= 0xFFFF) -> 8 uint16
+ZMI_AVX2 inline __m128i narrow16_avx2(__m256i x) {
+    const __m256i packed = _mm256_packus_epi32(x, x);  // per 128-bit lane: x0..3 x0..3 | x4..7 x4..7
+    return _mm256_castsi256_si128(_mm256_permute4x64_epi64(packed, 0x08));
+}
+
+template <int GDT, int PDT, bool ADAMW>
+ZMI_AVX2 void adam_block_avx2(const uint16_t* g, float* pp, float* mp, float* vp, uint16_t* par,
+                              int n_param, const AdamScalars& c) {
+    const __m128i h = _mm_loadu_si128(reinterpret_cast<const __m128i*>(g));
+    __m256 gf;
+    if (GDT == ZERO_F16) {
+        gf = _mm256_cvtph_ps(h);
+    } else {
+        gf = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(h), 16));
+    }
+    __m256 p = _mm256_loadu_ps(pp);
+    __m256 gu = _mm256_mul_ps(gf, _mm256_set1_ps(c.inv_scale));
+    if (!ADAMW) gu = _mm256_add_ps(gu, _mm256_mul_ps(_mm256_set1_ps(c.wd), p));
+    const __m256 m = _mm256_add_ps(_mm256_mul_ps(_mm256_set1_ps(c.b1), _mm256_loadu_ps(mp)),
+                                   _mm256_mul_ps(_mm256_set1_ps(c.omb1), gu));
+    const __m256 v = _mm256_add_ps(_mm256_mul_ps(_mm256_set1_ps(c.b2), _mm256_loadu_ps(vp)),
+                                   _mm256_mul_ps(_mm256_set1_ps(c.omb2), _mm256_mul_ps(gu, gu)));
+    const __m256 d = _mm256_add_ps(_mm256_mul_ps(_mm256_sqrt_ps(v), _mm256_set1_ps(c.rsbc2)),
+                                   _mm256_set1_ps(c.eps));
+    const __m256 u = _mm256_div_ps(m, d);
+    p = _mm256_sub_ps(_mm256_mul_ps(p, _mm256_set1_ps(c.decay)),
+                      _mm256_mul_ps(_mm256_set1_ps(c.step), u));
+    _mm256_storeu_ps(pp, p);
+    _mm256_storeu_ps(mp, m);
+    _mm256_storeu_ps(vp, v);
+    if (PDT != 0 && n_param > 0) {
+        __m128i out;
+        if (PDT == ZERO_F16) {
+            out = _mm256_cvtps_ph(p, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
+        } else {
+            out = narrow16_avx2(bf16_rne_avx2(p));
+        }
+        if (n_param >= 8) {
+            _mm_storeu_si128(reinterpret_cast<__m128i*>(par), out);
+        } else {
+            alignas(16) uint16_t tmp[8];
+            _mm_store_si128(reinterpret_cast<__m128i*>(tmp), out);
+            std::memcpy(par, tmp, static_cast<size_t>(n_param) * 2);
+        }
+    }
+}
+
+template <int GDT, int PDT, bool ADAMW>
+ZMI_AVX2 void adam_avx2(const CpuAdamArgs& a, int64_t lo, int64_t hi) {
+    int64_t k = lo;
+    for (; k + 8 <= hi; k += 8) {
+        const int64_t np = std::min<int64_t>(8, std::max<int64_t>(0, a.real - k));
+        adam_block_avx2<GDT, PDT, ADAMW>(a.g + k, a.p + k, a.m + k, a.v + k,
+                                         a.param ? a.param + k : nullptr, static_cast<int>(np),
+                                         a.sc);
+    }
+    if (k < hi) {  // tail: through zero-padded copies
+        const int n = static_cast<int>(hi - k);
+        alignas(32) uint16_t g[8] = {0};
+        alignas(32) float p[8] = {0}, m[8] = {0}, v[8] = {0};
+        alignas(32) uint16_t par[8];
+        std::memcpy(g, a.g + k, n * 2);
+        std::memcpy(p, a.p + k, n * 4);
+        std::memcpy(m, a.m + k, n * 4);
+        std::memcpy(v, a.v + k, n * 4);
+        const int np = static_cast<int>(std::min<int64_t>(n, std::max<int64_t>(0, a.real - k)));
+        adam_block_avx2<GDT, PDT, ADAMW>(g, p, m, v, par, np, a.sc);
+        std::memcpy(a.p + k, p, n * 4);
+        std::memcpy(a.m + k, m, n * 4);
+        std::memcpy(a.v + k, v, n * 4);
+        if (PDT != 0 && np > 0) std::memcpy(a.param + k, par, np * 2);
+    }
+}
+
+ZMI_AVX2 bool nonfinite_avx2(const uint16_t* g, int64_t lo, int64_t hi, uint32_t mask) {
+    const __m256i mk = _mm256_set1_epi16(static_cast<short>(mask));
+    __m256i acc = _mm256_setzero_si256();
+    int64_t k = lo;
+    for (; k + 16 <= hi; k += 16) {
+        const __m256i x = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(g + k));
+        acc = _mm256_or_si256(acc, _mm256_cmpeq_epi16(_mm256_and_si256(x, mk), mk));
+    }
+    return !_mm256_testz_si256(acc, acc) || nonfinite_scalar(g, k, hi, mask);
+}
+
+// ------------------------------------------------------------ AVX-512
+#define ZMI_AVX512 __attribute__((target("avx512f,avx512bw,avx512vl,avx2,f16c")))
+
+template <int GDT, int PDT, bool ADAMW>
+ZMI_AVX512 void adam_avx512(const CpuAdamArgs& a, int64_t lo, int64_t hi) {
+    const AdamScalars& c = a.sc;
+    const __m512 inv = _mm512_set1_ps(c.inv_scale), b1 = _mm512_set1_ps(c.b1),
+                 omb1 = _mm512_set1_ps(c.omb1), b2 = _mm512_set1_ps(c.b2),
+                 omb2 = _mm512_set1_ps(c.omb2), step = _mm512_set1_ps(c.step),
+                 rsbc2 = _mm512_set1_ps(c.rsbc2), eps = _mm512_set1_ps(c.eps),
+                 decay = _mm512_set1_ps(c.decay), wd = _mm512_set1_ps(c.wd);
+    for (int64_t k = lo; k < hi; k += 16) {
+        const int64_t left = hi - k;
+        const __mmask16 mk = left >= 16 ? static_cast<__mmask16>(0xFFFF)
+                                        : static_cast<__mmask16>((1u << left) - 1u);
+        const __m256i h = _mm256_maskz_loadu_epi16(mk, a.g + k);
+        __m512 gf;
+        if (GDT == ZERO_F16) {
+            gf = _mm512_cvtph_ps(h);
+        } else {
+            gf = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(h), 16));
+        }
+        __m512 p = _mm512_maskz_loadu_ps(mk, a.p + k);
+        __m512 gu = _mm512_mul_ps(gf, inv);
+        if (!ADAMW) gu = _mm512_add_ps(gu, _mm512_mul_ps(wd, p));
+        const __m512 m = _mm512_add_ps(_mm512_mul_ps(b1, _mm512_maskz_loadu_ps(mk, a.m + k)),
+                                       _mm512_mul_ps(omb1, gu));
+        const __m512 v = _mm512_add_ps(_mm512_mul_ps(b2, _mm512_maskz_loadu_ps(mk, a.v + k)),
+                                       _mm512_mul_ps(omb2, _mm512_mul_ps(gu, gu)));
+        const __m512 d = _mm512_add_ps(_mm512_mul_ps(_mm512_sqrt_ps(v), rsbc2), eps);
+        const __m512 u = _mm512_div_ps(m, d);
+        p = _mm512_sub_ps(_mm512_mul_ps(p, decay), _mm512_mul_ps(step, u));
+        _mm512_mask_storeu_ps(a.p + k, mk, p);
+        _mm512_mask_storeu_ps(a.m + k, mk, m);
+        _mm512_mask_storeu_ps(a.v + k, mk, v);
+        if (PDT != 0 && k < a.real) {
+            const int64_t rl = a.real - k;
+            const __mmask16 mp =
+                mk & (rl >= 16 ? static_cast<__mmask16>(0xFFFF)
+                               : static_cast<__mmask16>((1u << rl) - 1u));
+            __m256i out;
+            if (PDT == ZERO_F16) {
+                out = _mm512_cvtps_ph(p, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
+            } else {
+                const __m512i u32 = _mm512_castps_si512(p);
+                const __m512i lsb = _mm512_and_si512(_mm512_srli_epi32(u32, 16),
+                                                     _mm512_set1_epi32(1));
+                __m512i r = _mm512_srli_epi32(
+                    _mm512_add_epi32(_mm512_add_epi32(u32, _mm512_set1_epi32(0x7FFF)), lsb), 16);
+                const __mmask16 isnan = _mm512_cmp_ps_mask(p, p, _CMP_UNORD_Q);
+                r = _mm512_mask_or_epi32(r, isnan, _mm512_srli_epi32(u32, 16),
+                                         _mm512_set1_epi32(0x40));
+                out = _mm512_cvtepi32_epi16(r);
+            }
+            _mm256_mask_storeu_epi16(a.param + k, mp, out);
+        }
+    }
+}
+
+ZMI_AVX512 bool nonfinite_avx512(const uint16_t* g, int64_t lo, int64_t hi, uint32_t mask) {
+    const __m512i mk = _mm512_set1_epi16(static_cast<short>(mask));
+    __mmask32 acc = 0;
+    for (int64_t k = lo; k < hi; k += 32) {
+        const int64_t left = hi - k;
+        const __mmask32 lm = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
+        const __m512i x = _mm512_maskz_loadu_epi16(lm, g + k);
+        acc |= _mm512_mask_cmpeq_epi16_mask(lm, _mm512_and_si512(x, mk), mk);
+    }
+    return acc != 0;
+}
+
+// ------------------------------------------------------------ dispatch
+CpuIsa detect_isa() {
+    const char* force = std::getenv("ZERO_CPU_ISA");
+    const bool has512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                        __builtin_cpu_supports("avx512vl");
+    const bool has2 = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("f16c");
+    if (force != nullptr) {
+        const std::string f(force);
+        if (f == "scalar") return CpuIsa::kScalar;
+        if (f == "avx2" && has2) return CpuIsa::kAvx2;
+        if (f == "avx512" && has512) return CpuIsa::kAvx512;
+    }
+    if (has512) return CpuIsa::kAvx512;
+    if (has2) return CpuIsa::kAvx2;
+    return CpuIsa::kScalar;
+}
+
+using RangeFn = void (*)(const CpuAdamArgs&, int64_t, int64_t);
+
+template <CpuIsa ISA, int GDT, int PDT, bool ADAMW>
+RangeFn pick3() {
+    if (ISA == CpuIsa::kAvx512) return adam_avx512<GDT, PDT, ADAMW>;
+    if (ISA == CpuIsa::kAvx2) return adam_avx2<GDT, PDT, ADAMW>;
+    return adam_scalar<GDT, PDT, ADAMW>;
+}
+
+template <CpuIsa ISA, int GDT>
+RangeFn pick2(int pdt, bool adamw) {
+    if (pdt == 0) return adamw ? pick3<ISA, GDT, 0, true>() : pick3<ISA, GDT, 0, false>();
+    if (pdt == ZERO_F16) {
+        return adamw ? pick3<ISA, GDT, ZERO_F16, true>() : pick3<ISA, GDT, ZERO_F16, false>();
+    }
+    return adamw ? pick3<ISA, GDT, ZERO_BF16, true>() : pick3<ISA, GDT, ZERO_BF16, false>();
+}
+
+template <CpuIsa ISA>
+RangeFn pick1(int gdt, int pdt, bool adamw) {
+    return gdt == ZERO_F16 ? pick2<ISA, ZERO_F16>(pdt, adamw) : pick2<ISA, ZERO_BF16>(pdt, adamw);
+}
+
+RangeFn pick(CpuIsa isa, int gdt, int pdt, bool adamw) {
+    switch (isa) {
+        case CpuIsa::kAvx512: return pick1<CpuIsa::kAvx512>(gdt, pdt, adamw);
+        case CpuIsa::kAvx2: return pick1<CpuIsa::kAvx2>(gdt, pdt, adamw);
+        default: return pick1<CpuIsa::kScalar>(gdt, pdt, adamw);
+    }
+}
+
+// Runs fn over [0, n) split into n_threads contiguous chunks (multiples of
+// 64 elements); the calling thread takes the first chunk.
+template <typename Fn>
+void parallel_ranges(int64_t n, int n_threads, Fn fn) {
+    if (n_threads < 1) n_threads = 1;
+    int64_t chunk = (n + n_threads - 1) / n_threads;
+    chunk = (chunk + 63) / 64 * 64;
+    if (chunk < 64) chunk = 64;
+    std::vector<std::thread> pool;
+    for (int t = 1; t < n_threads; ++t) {
+        const int64_t lo = t * chunk;
+        if (lo >= n) break;
+        const int64_t hi = std::min(n, lo + chunk);
+        pool.emplace_back([=] { fn(lo, hi); });
+    }
+    fn(0, std::min(n, chunk));
+    for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+const char* cpu_isa_name(CpuIsa isa) {
+    switch (isa) {
+        case CpuIsa::kAvx512: return "avx512";
+        case CpuIsa::kAvx2: return "avx2";
+        default: return "scalar";
+    }
+}
+
+CpuIsa cpu_isa() { return detect_isa(); }
+
+bool cpu_nonfinite(const uint16_t* g, int64_t n, int gdt, int n_threads) {
+    if (n <= 0) return false;
+    const uint32_t mask = gdt == ZERO_F16 ? kF16ExpMask : kBf16ExpMask;
+    const CpuIsa isa = detect_isa();
+    std::vector<char> hit(static_cast<size_t>(std::max(n_threads, 1)) + 1, 0);
+    int64_t chunk = (n + std::max(n_threads, 1) - 1) / std::max(n_threads, 1);
+    chunk = std::max<int64_t>(64, (chunk + 63) / 64 * 64);
+    parallel_ranges(n, n_threads, [&](int64_t lo, int64_t hi) {
+        bool bad;
+        if (isa == CpuIsa::kAvx512) bad = nonfinite_avx512(g, lo, hi, mask);
+        else if (isa == CpuIsa::kAvx2) bad = nonfinite_avx2(g, lo, hi, mask);
+        else bad = nonfinite_scalar(g, lo, hi, mask);
+        hit[static_cast<size_t>(lo / chunk)] = bad ? 1 : 0;
+    });
+    return std::any_of(hit.begin(), hit.end(), [](char c) { return c != 0; });
+}
+
+void cpu_adam(const CpuAdamArgs& a, int n_threads) {
+    if (a.n <= 0) return;
+    const RangeFn fn = pick(detect_isa(), a.gdt, a.param ? a.pdt : 0, a.adamw);
+    parallel_ranges(a.n, n_threads, [&](int64_t lo, int64_t hi) { fn(a, lo, hi); });
+}
+
+}  // namespace zmi

@@ -48,6 +48,36 @@ struct AdamScalars {
     float inv_scale, b1, omb1, b2, omb2, step, rsbc2, eps, decay, wd;
 };
 
+// What an offloaded step needs from the device: its overflow flag, its
+// bias-correction step and the loss scale its gradients carry.
+struct OffloadSlot {
+    int32_t flag;
+    int32_t _pad;
+    int64_t t;
+    double scale;
+};
+
+// The loss-scale policy of zero_update_loss_scale on the device state
+// (also advances t or the skip count).
+__host__ __device__ inline void apply_scale_policy(DeviceStep& d, int overflow) {
+    if (overflow) {
+        if (d.dynamic) {
+            const double s = d.scale * d.backoff;
+            d.scale = s < d.min_scale ? d.min_scale : s;
+        }
+        d.good_steps = 0;
+        d.skipped += 1;
+    } else {
+        d.t += 1;
+        d.good_steps += 1;
+        if (d.dynamic && d.good_steps >= d.window) {
+            d.scale *= d.growth;
+            d.good_steps = 0;
+        }
+    }
+    d.last_flag = overflow;
+}
+
 // The plan's device block (one 256-byte allocation): the overflow flag, the
 // asynchronous step state and the update scalars formed on the device.
 constexpr size_t kBlockBytes = 256;
@@ -145,5 +175,33 @@ hipError_t launch_flag_clear(int* flag, hipStream_t s);
 hipError_t launch_step_prologue(const int* flag, const DeviceStep* st, AdamScalars* out,
                                 const zero_adam_hparams_t& hp, hipStream_t s);
 hipError_t launch_step_epilogue(int* flag, DeviceStep* st, hipStream_t s);
+// Offloaded step: snapshot (flag, t + 1, scale) into *slot, apply the
+// loss-scale policy to the device state, clear the flag.
+hipError_t launch_offload_snapshot(int* flag, DeviceStep* st, OffloadSlot* slot, hipStream_t s);
+
+// ---------------------------------------------------------------- host Adam
+enum class CpuIsa { kScalar = 0, kAvx2 = 1, kAvx512 = 2 };
+
+// One host update over shard elements [0, n): the arithmetic of the device
+// update.  param points at shard element 0's destination (nullptr: no
+// parameter write); elements k >= real are never written to it.
+struct CpuAdamArgs {
+    const uint16_t* g;
+    float* p;
+    float* m;
+    float* v;
+    uint16_t* param;
+    int64_t n;
+    int64_t real;
+    AdamScalars sc;
+    int gdt;
+    int pdt;
+    bool adamw;
+};
+
+CpuIsa cpu_isa();
+const char* cpu_isa_name(CpuIsa isa);
+void cpu_adam(const CpuAdamArgs& a, int n_threads);
+bool cpu_nonfinite(const uint16_t* g, int64_t n, int gdt, int n_threads);
 
 }  // namespace zmi

@@ -337,24 +337,25 @@ __global__ void step_prologue_kernel(const int* __restrict__ flag,
 // One thread: the loss-scale policy of zero_update_loss_scale on the device
 // state, then the flag is cleared for the next step.
 __global__ void step_epilogue_kernel(int* __restrict__ flag, DeviceStep* __restrict__ st) {
+    DeviceStep d = *st;
+    apply_scale_policy(d, *flag != 0);
+    *st = d;
+    *flag = 0;
+}
+
+// One thread: what the host update of an offloaded step needs (its flag,
+// t + 1 and the scale its gradients carry), then the policy as above.
+__global__ void offload_snapshot_kernel(int* __restrict__ flag, DeviceStep* __restrict__ st,
+                                        OffloadSlot* __restrict__ slot) {
     const int overflow = *flag != 0;
     DeviceStep d = *st;
-    if (overflow) {
-        if (d.dynamic) {
-            const double s = d.scale * d.backoff;
-            d.scale = s < d.min_scale ? d.min_scale : s;
-        }
-        d.good_steps = 0;
-        d.skipped += 1;
-    } else {
-        d.t += 1;
-        d.good_steps += 1;
-        if (d.dynamic && d.good_steps >= d.window) {
-            d.scale *= d.growth;
-            d.good_steps = 0;
-        }
-    }
-    d.last_flag = overflow;
+    OffloadSlot o;
+    o.flag = overflow;
+    o._pad = 0;
+    o.t = d.t + 1;
+    o.scale = d.scale;
+    *slot = o;
+    apply_scale_policy(d, overflow);
     *st = d;
     *flag = 0;
 }
@@ -481,6 +482,11 @@ hipError_t launch_step_prologue(const int* flag, const DeviceStep* st, AdamScala
 
 hipError_t launch_step_epilogue(int* flag, DeviceStep* st, hipStream_t s) {
     hipLaunchKernelGGL(step_epilogue_kernel, dim3(1), dim3(1), 0, s, flag, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_offload_snapshot(int* flag, DeviceStep* st, OffloadSlot* slot, hipStream_t s) {
+    hipLaunchKernelGGL(offload_snapshot_kernel, dim3(1), dim3(1), 0, s, flag, st, slot);
     return hipGetLastError();
 }
 

@@ -1,0 +1,461 @@
+// ZeRO-Offload for one rank, with the one-step delayed parameter update.
+//
+// "ZeRO Optimization", inferensys glossary: the legal pre-training page,
+// offload list (CPU-offload bullet: optimizer states in CPU DRAM, Adam on the
+// CPU while the GPU runs forward and backward; DPU bullet: the CPU optimizer
+// step of one iteration overlaps the next iteration's forward pass), and the
+// genomic MLOps page, offload list (fp32 master weights and optimizer states
+// in CPU RAM, half parameters and gradients on the GPU; DPU overlaps CPU and
+// GPU computation).
+//
+// Per submitted step i (caller's stream, after zero_flatten_grads):
+//   snapshot kernel   flag, t + 1 and the scale of step i -> device slot i%2;
+//                     loss-scale policy applied to the device state; flag
+//                     cleared (so the next backward already sees the new scale)
+//   D2H               flat gradient shard -> pinned host buffer i%2, slot -> host
+// Worker thread, steps in order:
+//   wait for the D2H; skipped step: nothing else.  Otherwise the host update
+//   (cpu_adam, same arithmetic as the device update) writes master / moments
+//   in host memory and the half parameters into pinned buffer i%2; then, on
+//   the library's transfer stream, once the caller has released the device
+//   parameters of step i (event recorded by the next submit, by
+//   zero_offload_wait_params or by zero_offload_drain), H2D of the parameters
+//   to the rank's offset.
+// zero_offload_wait_params(lag) makes the caller's stream wait until the
+// parameters of every submitted step but the last `lag` are on the device:
+// lag = 1 is the one-step delayed update (the host work of step i runs while
+// the GPU computes step i + 1), lag = 0 the plain, serialised step.
+#include <chrono>
+#include <condition_variable>
+#include <cstring>
+#include <exception>
+#include <mutex>
+#include <new>
+#include <string>
+#include <thread>
+
+#include "internal.h"
+
+namespace zmi {
+namespace {
+
+struct Pending {
+    int64_t idx = -1;
+    uint16_t* param_dst = nullptr;  // device address of shard element 0's parameter
+    bool free_recorded = false;     // ev_free[b] holds the release point
+    bool processed = false;         // host part done, H2D enqueued (or step skipped)
+    bool applied = false;
+};
+
+}  // namespace
+}  // namespace zmi
+
+using namespace zmi;
+
+struct zero_offload {
+    zero_plan* plan = nullptr;
+    zero_adam_hparams_t hp{};
+    int gdt = 0, pdt = 0;
+    float* master = nullptr;
+    float* m = nullptr;
+    float* v = nullptr;
+    int n_threads = 1;
+    int device = -1;
+    // library-owned buffers
+    uint16_t* hgrad[2] = {nullptr, nullptr};   // pinned, S each
+    uint16_t* hparam[2] = {nullptr, nullptr};  // pinned, max(real, 1) each
+    OffloadSlot* hslot = nullptr;              // pinned, 2 slots
+    OffloadSlot* dslot = nullptr;              // device, 2 slots
+    hipStream_t xfer = nullptr;
+    hipEvent_t ev_d2h[2] = {}, ev_free[2] = {}, ev_h2d[2] = {};
+    bool h2d_recorded[2] = {false, false};  // written under mu; the worker also reads it unlocked
+    // steps
+    Pending rec[2];
+    int64_t submitted = 0;
+    int64_t processed = 0;
+    // worker
+    std::thread worker;
+    std::mutex mu;
+    std::condition_variable cv;
+    bool stop = false;
+    // stats (under mu)
+    int64_t applied = 0, skipped = 0;
+    int32_t last_flag = 0;
+    double host_ms_last = 0, host_ms_total = 0;
+    int err = ZERO_OK;
+    std::string err_msg;
+};
+
+namespace {
+
+void set_worker_error(zero_offload* o, int code, const std::string& msg) {
+    std::lock_guard<std::mutex> g(o->mu);
+    if (o->err == ZERO_OK) {
+        o->err = code;
+        o->err_msg = msg;
+    }
+    o->cv.notify_all();
+}
+
+int worker_hip(zero_offload* o, hipError_t e, const char* what) {
+    if (e == hipSuccess) return ZERO_OK;
+    set_worker_error(o, ZERO_EHIP,
+                     std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")");
+    return ZERO_EHIP;
+}
+
+void worker_main(zero_offload* o) {
+    if (worker_hip(o, hipSetDevice(o->device), "hipSetDevice") != ZERO_OK) return;
+    const zero_plan* p = o->plan;
+    for (int64_t j = 0;; ++j) {
+        const int b = static_cast<int>(j & 1);
+        {
+            std::unique_lock<std::mutex> lk(o->mu);
+            o->cv.wait(lk, [&] { return o->stop || o->submitted > j; });
+            if (o->submitted <= j) return;  // stopped with nothing left
+        }
+        if (worker_hip(o, hipEventSynchronize(o->ev_d2h[b]), "gradient copy") != ZERO_OK) return;
+        const OffloadSlot slot = o->hslot[b];
+        bool applied = false;
+        bool sent = false;
+        if (slot.flag == 0) {
+            // the pinned parameter buffer b was last sent by step j - 2
+            if (o->h2d_recorded[b] &&
+                worker_hip(o, hipEventSynchronize(o->ev_h2d[b]), "parameter copy") != ZERO_OK) {
+                return;
+            }
+            CpuAdamArgs a;
+            a.g = o->hgrad[b];
+            a.p = o->master;
+            a.m = o->m;
+            a.v = o->v;
+            a.param = o->pdt ? o->hparam[b] : nullptr;
+            a.n = p->S;
+            a.real = p->real;
+            a.sc = make_scalars(o->hp.lr, o->hp.beta1, o->hp.beta2, o->hp.eps,
+                                o->hp.weight_decay, o->hp.adamw, static_cast<double>(slot.t),
+                                slot.scale);
+            a.gdt = o->gdt;
+            a.pdt = o->pdt;
+            a.adamw = o->hp.adamw != 0;
+            const auto t0 = std::chrono::steady_clock::now();
+            try {
+                cpu_adam(a, o->n_threads);
+            } catch (const std::exception& ex) {
+                set_worker_error(o, ZERO_ENOMEM, std::string("host update: ") + ex.what());
+                return;
+            }
+            const double ms =
+                std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0)
+                    .count();
+            applied = true;
+            uint16_t* dst = nullptr;
+            {
+                std::unique_lock<std::mutex> lk(o->mu);
+                o->host_ms_last = ms;
+                o->host_ms_total += ms;
+                o->cv.wait(lk, [&] { return o->stop || o->rec[b].free_recorded; });
+                if (!o->rec[b].free_recorded) return;
+                dst = o->rec[b].param_dst;
+            }
+            if (o->pdt != 0 && p->real > 0 && dst != nullptr) {
+                if (worker_hip(o, hipStreamWaitEvent(o->xfer, o->ev_free[b], 0), "wait") !=
+                        ZERO_OK ||
+                    worker_hip(o, hipMemcpyAsync(dst, o->hparam[b], 2 * static_cast<size_t>(p->real),
+                                                 hipMemcpyHostToDevice, o->xfer),
+                               "parameter copy") != ZERO_OK ||
+                    worker_hip(o, hipEventRecord(o->ev_h2d[b], o->xfer), "hipEventRecord") !=
+                        ZERO_OK) {
+                    return;
+                }
+                sent = true;
+            }
+        }
+        std::lock_guard<std::mutex> g(o->mu);
+        if (sent) o->h2d_recorded[b] = true;
+        o->rec[b].processed = true;
+        o->rec[b].applied = applied;
+        o->processed = j + 1;
+        o->last_flag = slot.flag;
+        if (applied) o->applied += 1; else o->skipped += 1;
+        o->cv.notify_all();
+    }
+}
+
+int offload_error(zero_offload* o) {
+    std::lock_guard<std::mutex> g(o->mu);
+    if (o->err != ZERO_OK) return fail(o->err, "offload worker failed: " + o->err_msg);
+    return ZERO_OK;
+}
+
+int check_device(zero_offload* o) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != o->device) return fail(ZERO_ESTATE, "offload object is bound to another device");
+    return ZERO_OK;
+}
+
+// Records the release point of step j's device parameters on `s` unless
+// the next submit already did.  Caller holds no lock.
+int release_params(zero_offload* o, int64_t j, hipStream_t s) {
+    const int b = static_cast<int>(j & 1);
+    std::lock_guard<std::mutex> g(o->mu);
+    if (o->rec[b].idx != j || o->rec[b].free_recorded) return ZERO_OK;
+    hipError_t e = hipEventRecord(o->ev_free[b], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    o->rec[b].free_recorded = true;
+    o->cv.notify_all();
+    return ZERO_OK;
+}
+
+// Host wait until step j's host part is done (or an error / stop).
+int wait_processed(zero_offload* o, int64_t j) {
+    std::unique_lock<std::mutex> lk(o->mu);
+    o->cv.wait(lk, [&] { return o->err != ZERO_OK || o->processed > j; });
+    if (o->err != ZERO_OK) return fail(o->err, "offload worker failed: " + o->err_msg);
+    return ZERO_OK;
+}
+
+void release_all(zero_offload* o) {
+    if (o->worker.joinable()) {
+        {
+            std::lock_guard<std::mutex> g(o->mu);
+            o->stop = true;
+        }
+        o->cv.notify_all();
+        o->worker.join();
+    }
+    if (o->xfer) (void)hipStreamSynchronize(o->xfer);
+    for (int b = 0; b < 2; ++b) {
+        if (o->hgrad[b]) (void)hipHostFree(o->hgrad[b]);
+        if (o->hparam[b]) (void)hipHostFree(o->hparam[b]);
+        if (o->ev_d2h[b]) (void)hipEventDestroy(o->ev_d2h[b]);
+        if (o->ev_free[b]) (void)hipEventDestroy(o->ev_free[b]);
+        if (o->ev_h2d[b]) (void)hipEventDestroy(o->ev_h2d[b]);
+    }
+    if (o->hslot) (void)hipHostFree(o->hslot);
+    if (o->dslot) (void)hipFree(o->dslot);
+    if (o->xfer) (void)hipStreamDestroy(o->xfer);
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero_offload_create(zero_plan_t* p, const zero_adam_hparams_t* hp, int32_t grad_dtype,
+                        int32_t param_dtype, float* master, float* exp_avg, float* exp_avg_sq,
+                        int32_t n_threads, zero_offload_t** out) {
+    if (out == nullptr) return fail(ZERO_ENULL, "out is NULL");
+    *out = nullptr;
+    if (p == nullptr || hp == nullptr) return fail(ZERO_ENULL, "plan or hparams is NULL");
+    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16) {
+        return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16");
+    }
+    if (param_dtype != 0 && param_dtype != ZERO_F16 && param_dtype != ZERO_BF16) {
+        return fail(ZERO_EINVAL, "param_dtype must be 0, ZERO_F16 or ZERO_BF16");
+    }
+    if (n_threads < 1 || n_threads > 1024) return fail(ZERO_EINVAL, "n_threads must be in [1, 1024]");
+    if (!(hp->lr >= 0) || !(hp->beta1 >= 0 && hp->beta1 < 1) || !(hp->beta2 >= 0 && hp->beta2 < 1) ||
+        !(hp->eps > 0) || !(hp->weight_decay >= 0)) {
+        return fail(ZERO_EINVAL, "hyperparameters out of range");
+    }
+    if (p->S > 0 && (master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr)) {
+        return fail(ZERO_ENULL, "master, exp_avg and exp_avg_sq must be non-NULL");
+    }
+    if (!p->dev.ready || !p->dev.state_ready) {
+        return fail(ZERO_ESTATE, "no device state: call zero_state_upload first");
+    }
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != p->dev.device) return fail(ZERO_ESTATE, "plan is bound to another device");
+    zero_offload* o = new (std::nothrow) zero_offload();
+    if (o == nullptr) return fail(ZERO_ENOMEM, "offload allocation failed");
+    o->plan = p;
+    o->hp = *hp;
+    o->gdt = grad_dtype;
+    o->pdt = param_dtype;
+    o->master = master;
+    o->m = exp_avg;
+    o->v = exp_avg_sq;
+    o->n_threads = n_threads;
+    o->device = dev;
+    const size_t gbytes = 2 * static_cast<size_t>(p->S > 0 ? p->S : 1);
+    const size_t pbytes = 2 * static_cast<size_t>(p->real > 0 ? p->real : 1);
+    for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+        e = hipHostMalloc(reinterpret_cast<void**>(&o->hgrad[b]), gbytes, hipHostMallocDefault);
+        if (e == hipSuccess) {
+            e = hipHostMalloc(reinterpret_cast<void**>(&o->hparam[b]), pbytes, hipHostMallocDefault);
+        }
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&o->ev_d2h[b], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&o->ev_free[b], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&o->ev_h2d[b], hipEventDisableTiming);
+    }
+    if (e == hipSuccess) {
+        e = hipHostMalloc(reinterpret_cast<void**>(&o->hslot), 2 * sizeof(OffloadSlot),
+                          hipHostMallocDefault);
+    }
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&o->dslot), 2 * sizeof(OffloadSlot));
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&o->xfer, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+        const int rc = hip_fail(e, "offload buffers");
+        release_all(o);
+        delete o;
+        return rc == ZERO_EHIP && e == hipErrorOutOfMemory ? ZERO_ENOMEM : rc;
+    }
+    try {
+        o->worker = std::thread(worker_main, o);
+    } catch (const std::exception& ex) {
+        release_all(o);
+        delete o;
+        return fail(ZERO_ENOMEM, std::string("worker thread: ") + ex.what());
+    }
+    *out = o;
+    return ZERO_OK;
+}
+
+int zero_offload_submit(zero_offload_t* o, const void* flat_grad, void* param, int64_t param_base,
+                        int64_t param_numel, void* stream) {
+    if (o == nullptr) return fail(ZERO_ENULL, "offload is NULL");
+    zero_plan* p = o->plan;
+    if (p->S > 0 && flat_grad == nullptr) return fail(ZERO_ENULL, "flat_grad is NULL");
+    if (o->pdt != 0 && p->real > 0 && param == nullptr) {
+        return fail(ZERO_ENULL, "param is NULL but the offload writes parameters");
+    }
+    uint16_t* param0 = nullptr;
+    if (o->pdt != 0 && p->real > 0) {
+        if ((reinterpret_cast<uintptr_t>(param) & 1u) != 0) {
+            return fail(ZERO_EALIGN, "param must be 2-byte aligned");
+        }
+        if (param_base < 0 || param_numel < 0 || p->begin < param_base ||
+            p->begin + p->real - param_base > param_numel) {
+            return fail(ZERO_EINVAL, "param window must contain the shard's real range");
+        }
+        param0 = static_cast<uint16_t*>(param) + (p->begin - param_base);
+    }
+    int rc = check_device(o);
+    if (rc != ZERO_OK) return rc;
+    if ((rc = offload_error(o)) != ZERO_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t i = o->submitted;
+    const int b = static_cast<int>(i & 1);
+    // everything enqueued so far on `s` (this step's forward and backward)
+    // was computed with the parameters the previous step's update replaces
+    if (i >= 1 && (rc = release_params(o, i - 1, s)) != ZERO_OK) return rc;
+    // buffers b were last used by step i - 2
+    if (i >= 2 && (rc = wait_processed(o, i - 2)) != ZERO_OK) return rc;
+    DeviceStep* st = reinterpret_cast<DeviceStep*>(reinterpret_cast<char*>(p->dev.d_flag) +
+                                                   kStateOffset);
+    hipError_t e = launch_offload_snapshot(p->dev.d_flag, st, o->dslot + b, s);
+    if (e != hipSuccess) return hip_fail(e, "snapshot launch");
+    if (p->S > 0) {
+        e = hipMemcpyAsync(o->hgrad[b], flat_grad, 2 * static_cast<size_t>(p->S),
+                           hipMemcpyDeviceToHost, s);
+        if (e != hipSuccess) return hip_fail(e, "gradient copy");
+    }
+    e = hipMemcpyAsync(o->hslot + b, o->dslot + b, sizeof(OffloadSlot), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "slot copy");
+    e = hipEventRecord(o->ev_d2h[b], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    {
+        std::lock_guard<std::mutex> g(o->mu);
+        Pending& r = o->rec[b];
+        r = Pending{};
+        r.idx = i;
+        r.param_dst = param0;
+        o->submitted = i + 1;
+    }
+    o->cv.notify_all();
+    // the flatten bookkeeping of this flat buffer is consumed
+    std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
+    p->flatten_all_done = false;
+    p->flattened_into = nullptr;
+    return ZERO_OK;
+}
+
+int zero_offload_wait_params(zero_offload_t* o, int32_t lag, void* stream) {
+    if (o == nullptr) return fail(ZERO_ENULL, "offload is NULL");
+    // with one device parameter buffer, step j's copy may start once the
+    // next step is submitted, so only the parameters of all steps but the
+    // newest one (lag 1) or of all steps (lag 0) can be waited for safely
+    if (lag != 0 && lag != 1) return fail(ZERO_EINVAL, "lag must be 0 or 1");
+    int rc = check_device(o);
+    if (rc != ZERO_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int64_t submitted;
+    {
+        std::lock_guard<std::mutex> g(o->mu);
+        submitted = o->submitted;
+    }
+    const int64_t last = submitted - 1 - lag;  // newest step whose parameters are needed
+    if (last < 0) return offload_error(o);
+    // the older of the (at most two) pending steps first
+    for (int64_t j = last > 0 ? last - 1 : 0; j <= last; ++j) {
+        if ((rc = release_params(o, j, s)) != ZERO_OK) return rc;
+        if ((rc = wait_processed(o, j)) != ZERO_OK) return rc;
+    }
+    // the newest H2D enqueued covers every older one (one transfer stream)
+    for (int b = 0; b < 2; ++b) {
+        bool wait;
+        {
+            std::lock_guard<std::mutex> g(o->mu);
+            wait = o->h2d_recorded[b];
+        }
+        if (wait) {
+            hipError_t e = hipStreamWaitEvent(s, o->ev_h2d[b], 0);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        }
+    }
+    return offload_error(o);
+}
+
+int zero_offload_drain(zero_offload_t* o, void* stream) {
+    if (o == nullptr) return fail(ZERO_ENULL, "offload is NULL");
+    int rc = zero_offload_wait_params(o, 0, stream);
+    if (rc != ZERO_OK) return rc;
+    hipError_t e = hipStreamSynchronize(o->xfer);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    return offload_error(o);
+}
+
+int zero_offload_stats(zero_offload_t* o, zero_offload_stats_t* out) {
+    if (o == nullptr || out == nullptr) return fail(ZERO_ENULL, "offload or out is NULL");
+    {
+        std::lock_guard<std::mutex> g(o->mu);
+        std::memset(out, 0, sizeof(*out));
+        out->submitted = o->submitted;
+        out->processed = o->processed;
+        out->applied = o->applied;
+        out->skipped = o->skipped;
+        out->last_flag = o->last_flag;
+        out->host_ms_last = o->host_ms_last;
+        out->host_ms_total = o->host_ms_total;
+    }
+    return offload_error(o);
+}
+
+void zero_offload_destroy(zero_offload_t* o) {
+    if (o == nullptr) return;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != o->device) (void)hipSetDevice(o->device);
+    // let the worker finish what was submitted, then stop it
+    {
+        std::unique_lock<std::mutex> lk(o->mu);
+        for (int b = 0; b < 2; ++b) {
+            if (o->rec[b].idx >= 0 && !o->rec[b].free_recorded) {
+                if (hipEventRecord(o->ev_free[b], nullptr) == hipSuccess) o->rec[b].free_recorded = true;
+            }
+        }
+        o->cv.notify_all();
+        o->cv.wait(lk, [&] { return o->err != ZERO_OK || o->processed >= o->submitted; });
+    }
+    release_all(o);
+    if (cur != o->device && cur >= 0) (void)hipSetDevice(cur);
+    delete o;
+}
+
+}  // extern "C"
