@@ -149,7 +149,12 @@ def run_graph(bufs, steps, warmup, device):
         z.zero_flatten_grads(plan, -1, grads, flat)
         z.zero_adam_step_async(plan, hp, flat, master, m, v, param, plan.begin)
 
-    step()                              # one eager step before capture
+    # eager asynchronous steps first: their update kernel (scalars read from
+    # device memory) is timed with HIP events like the synchronous one
+    dev_ms = []
+    for _ in range(max(warmup, 2)):
+        step()
+        dev_ms.append(plan.kernel_ms(2))
     torch.cuda.synchronize(device)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -165,9 +170,24 @@ def run_graph(bufs, steps, warmup, device):
     after = z.zero_state_download(plan)
     done = (after.applied_steps + after.skipped_steps) - (before.applied_steps +
                                                           before.skipped_steps)
-    assert done == steps + warmup + 1, (done, steps, warmup)
+    assert done == steps + warmup + max(warmup, 2), (done, steps, warmup)
     log(f"[bench] graph: {steps} replays in {wall:.3f} s; skipped {after.skipped_steps}")
-    return wall
+    return wall, sum(dev_ms[1:]) / len(dev_ms[1:])
+
+
+def time_standalone_kernels(bufs):
+    """One launch each of the kernels the default step does not run: the
+    standalone parameter cast (6 B/element) and the overflow scan of a flat
+    shard that was not flattened this step (2 B/element; it runs inside a
+    zero_adam_step, whose update is timed separately)."""
+    import zero_partitioned_mixed_plan_amd as z
+
+    plan, master, m, v, flat, param, grads, hp, scaler = bufs
+    z.zero_write_param_shard(plan, master, param, plan.begin)
+    write_ms = plan.kernel_ms(3)
+    z.zero_adam_step(plan, hp, 1, scaler.scale, flat, master, m, v, param, plan.begin)
+    scan_ms = plan.kernel_ms(1)
+    return write_ms, scan_ms
 
 
 def run_offload(w, steps, warmup, device, n_threads):
@@ -344,7 +364,9 @@ def main(argv=None):
             "offload": res}), flush=True)
         return 0
     plan, wall, times, state, bufs = run_gpu(w, args.steps, args.warmup, device)
-    graph_wall = None if args.no_graph else run_graph(bufs, args.steps, args.warmup, device)
+    write_ms, scan_ms = time_standalone_kernels(bufs)
+    graph_wall, devsc_ms = (None, None) if args.no_graph else run_graph(bufs, args.steps,
+                                                                        args.warmup, device)
     S, real, begin = plan.S, plan.real, plan.begin
     ms_per_step = wall * 1000.0 / args.steps
     adam_ms = sum(times["adam"]) / len(times["adam"])
@@ -377,11 +399,15 @@ def main(argv=None):
                            "params_per_s": S / (adam_ms * 1e-3)},
             "flatten": {"avg_ms": flat_ms, "min_ms": min(times["flatten"]),
                         "bytes_per_elem": FLATTEN_BYTES_PER_ELEM, "gbps": flat_gbs},
+            "write_param": {"ms": write_ms, "bytes_per_elem": 6,
+                            "gbps": 6 * real / (write_ms * 1e-3) / 1e9},
+            "scan": {"ms": scan_ms, "bytes_per_elem": 2, "gbps": 2 * S / (scan_ms * 1e-3) / 1e9},
         },
         "skipped_steps": state["skipped"],
         "graph_replay": None if graph_wall is None else {
             "ms_per_step": graph_wall * 1000.0 / args.steps,
             "value": real / (graph_wall / args.steps),
+            "adam_device_scalars_ms": devsc_ms,
             "what": "flatten + zero_adam_step_async (device-resident t and loss scale) captured "
                     "once into a HIP graph, replayed per step; no host round trip"},
         "roofline": {"bound": "hbm", "achieved": adam_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -29,6 +29,11 @@
 //     scalar loads); two vectors per thread (4096-element tiles) amortise
 //     that better than one or four (-3% flatten time on a 70B-class shard,
 //     -5% on a shard of 300 mostly misaligned pieces).
+//   * a workgroup must move enough bytes: the dispatcher starts roughly two
+//     billion workgroups a second, so the 6 B/element parameter cast with
+//     one element per thread (256 per workgroup) ran at 3.1 TB/s; eight
+//     strided elements per thread (2048 per workgroup) reach 6.2 TB/s
+//     (4: 5.4, 16: 5.9).
 //   * grids are 2-D (x up to 65536 workgroups) because a 1-D grid is limited
 //     to 2^32 work-items and a 70B-class shard has more elements than that;
 //     workgroup id = blockIdx.y * gridDim.x + blockIdx.x keeps address order.
@@ -55,6 +60,8 @@ constexpr int64_t kGridX = 65536;           // x extent of the 2-D grids
 constexpr int kAdamThreads = 128;           // update: two waves per workgroup,
 constexpr int kAdamPer = 2;                 // two elements per thread,
 constexpr int64_t kAdamSpan = kAdamThreads * kAdamPer;  // 256 elements per workgroup
+constexpr int kWritePer = 8;                // parameter cast: elements per thread,
+constexpr int64_t kWriteSpan = kThreads * kWritePer;  // 2048 per workgroup
 
 __device__ __forceinline__ int64_t block_id() {
     return static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
@@ -314,11 +321,23 @@ adam_kernel(const uint16_t* __restrict__ g, float* __restrict__ master, float* _
 }
 
 // ------------------------------------------------------------ param cast
+// A workgroup casts kWriteSpan consecutive elements; thread t takes t +
+// j * 256 for j < kWritePer, all loads first.
 template <int PDT>
 __global__ void __launch_bounds__(kThreads)
 write_param_kernel(const float* __restrict__ master, uint16_t* __restrict__ param, int64_t real) {
-    const int64_t k = block_id() * kThreads + threadIdx.x;
-    if (k < real) param[k] = f32_to_half<PDT>(__builtin_nontemporal_load(master + k));
+    const int64_t k0 = block_id() * kWriteSpan + threadIdx.x;
+    float p[kWritePer];
+#pragma unroll
+    for (int j = 0; j < kWritePer; ++j) {
+        const int64_t k = k0 + j * kThreads;
+        if (k < real) p[j] = __builtin_nontemporal_load(master + k);
+    }
+#pragma unroll
+    for (int j = 0; j < kWritePer; ++j) {
+        const int64_t k = k0 + j * kThreads;
+        if (k < real) param[k] = f32_to_half<PDT>(p[j]);
+    }
 }
 
 __global__ void flag_clear_kernel(int* flag) { *flag = 0; }
@@ -458,7 +477,7 @@ hipError_t launch_adam(const uint16_t* g, float* master, float* m, float* v, uin
 hipError_t launch_write_param(const float* master, uint16_t* param_at_0, int64_t real,
                               int param_dtype, hipStream_t s) {
     if (real <= 0) return hipSuccess;
-    const dim3 grid = grid_2d((real + kThreads - 1) / kThreads);
+    const dim3 grid = grid_2d((real + kWriteSpan - 1) / kWriteSpan);
     if (param_dtype == ZERO_F16) {
         hipLaunchKernelGGL(write_param_kernel<ZERO_F16>, grid, dim3(kThreads), 0, s, master,
                            param_at_0, real);
