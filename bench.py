@@ -285,21 +285,33 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "adam_fused_llama2_70b_rank7_hbm_
 KERNELS_SRC = os.path.join(ROOT, "zero_partitioned_mixed_plan_amd", "csrc", "kernels.hip")
 
 
+def kernels_digest(path=KERNELS_SRC):
+    """SHA-256 of the kernel source with // comments and blank lines removed,
+    so that a comment edit does not count as a kernel change."""
+    import hashlib
+    import re
+    lines = []
+    for line in open(path).read().splitlines():
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line.strip():
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def counted_traffic(workload_name):
     """HBM bytes per launch of the update kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (copy-calibrated), or None when that
     summary is for another workload or the kernels have changed since."""
-    import hashlib
     import re
     try:
         text = open(COUNTERS_FILE).read()
-        src = open(KERNELS_SRC, "rb").read()
+        digest = kernels_digest()
     except OSError:
         return None
     vals = dict(re.findall(r"^(\w+) = (\S+)$", text, flags=re.M))
     if vals.get("workload") != workload_name:
         return None
-    if vals.get("kernels_sha256") != hashlib.sha256(src).hexdigest():
+    if vals.get("kernels_sha256") != digest:
         return None
     return int(vals["traffic_bytes_per_launch"])
 
@@ -336,7 +348,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("this build measures one GPU only: it runs one rank's real-sized shard on a "
+        print("bench.py measures one GPU only: it runs one rank's real-sized shard on a "
               "single MI355X; --gpus must be 1", file=sys.stderr)
         return 2
     _ensure_built()

@@ -1,9 +1,10 @@
 // HIP kernels for gfx950 (MI355X): flatten + overflow test, overflow scan,
-// fused unscale + Adam/AdamW + half cast, and the standalone parameter cast.
+// fused unscale + Adam/AdamW + half cast, the standalone parameter cast, and
+// the one-thread bookkeeping kernels of the asynchronous and offloaded steps.
 //
-// All four are streaming, memory-bound kernels (no contraction, so no
-// MFMA).  Launch shape and cache policy, chosen by measurement on MI355X
-// (2^31-element buffers, HIP events):
+// The four streaming kernels are memory-bound (no contraction, so no MFMA).
+// Launch shape and cache policy, chosen by measurement on MI355X (2^31- and
+// 8.6e9-element buffers, HIP events):
 //   * exact-cover grids: every workgroup handles one fixed piece of the
 //     shard and exits, so the hardware dispatcher walks memory in address
 //     order.  Grid-stride loops over a CU-sized grid reached ~5.0 TB/s on
@@ -15,8 +16,8 @@
 //     write streams, vector accesses were 5-15% slower.  On a 70B-class
 //     shard (8.6e9 elements) the best shape was 128-thread workgroups with
 //     two elements per thread, t and t + 128, both loaded before the math:
-//     36.9 ms vs 37.5 ms for 256 threads x 1 element and 38.2 ms for
-//     64 x 2 or 256 x 4.
+//     37.1 ms vs 38.2 ms for 256 threads x 1 element, 37.6 ms for 256 x 4
+//     and 38.1 ms for 64 x 2 (same box, same run).
 //   * non-temporal loads and stores (the streaming cache policy) on the
 //     three fp32 state arrays, plain accesses for the half gradient and
 //     parameter: +3-6% on the update.  Every byte of the state is touched
