@@ -5,6 +5,10 @@ and the ``cpu_baseline`` leg of ``bench.py``.  The product package never
 imports it.  The arithmetic lives in ``zero_oracle.c`` (plain scalar C,
 built by ``__graft_entry__.build()`` into ``liboracle.so``); this module only
 marshals numpy arrays.
+
+ZERO_ORACLE_LIB (tests only) names another build of ``zero_oracle.c`` to
+load instead of ``liboracle.so``: the mutation tests use it to show that the
+oracle's pins fail when a plausible mistake is planted in it.
 """
 from __future__ import annotations
 
@@ -16,7 +20,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+LIB_PATH = os.environ.get("ZERO_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 F16 = 1
 BF16 = 2
@@ -110,7 +114,7 @@ def flatten(p: OraclePlan, grads: List[Optional[np.ndarray]]) -> np.ndarray:
         g = keep[int(p.seg_tensor[s])]
         if g is None or g.size < p.seg_tensor_off[s] + p.seg_numel[s]:
             raise ValueError(f"gradient of tensor {int(p.seg_tensor[s])} missing or too small")
-    flat = np.empty(p.S, dtype=np.uint16)
+    flat = np.full(p.S, 0xDEAD, dtype=np.uint16)   # every element must be written
     _load().oracle_flatten(ctypes.addressof(ptrs), _ptr(p.seg_tensor), _ptr(p.seg_tensor_off),
                            _ptr(p.seg_shard_off), _ptr(p.seg_numel), p.n_segments, p.S, p.real,
                            _ptr(flat))

@@ -161,6 +161,25 @@ def test_memory_accounting_matches_pages():
     assert abs(red / g["optimizer_state_reduction_at_8"] - 1) < 1e-6
 
 
+def test_stage_bytes_from_the_pages_components():
+    # per-rank model-state bytes built from the pages' per-parameter bytes
+    # (half parameters, half gradients, fp32 master + momentum + variance)
+    # and from what each stage partitions (stage 1 the optimizer states,
+    # stage 2 also the gradients, stage 3 also the parameters); partitioned
+    # parts are held for the S elements of the shard, replicated ones for P
+    g = _golden()
+    pb, gb, sb = (int(g["param_bytes_fp16"]), int(g["grad_bytes_fp16"]),
+                  int(g["state_bytes_fp32"]))
+    rng = np.random.default_rng(4)
+    for _ in range(20):
+        numels = rng.integers(0, 5000, int(rng.integers(1, 30))).tolist()
+        R = int(rng.integers(1, 9))
+        p = oracle.plan(numels, R, int(rng.integers(0, R)), int(rng.integers(1, 65)))
+        assert p.bytes_stage1 == pb * p.P + gb * p.P + sb * p.S
+        assert p.bytes_stage2 == pb * p.P + gb * p.S + sb * p.S
+        assert p.bytes_stage3 == pb * p.S + gb * p.S + sb * p.S
+
+
 def test_stage_factors_match_pages():
     g = _golden()
     numels = [1 << 30] * 8

@@ -77,6 +77,15 @@ def test_scale_growth_backoff_and_floor():
     for ovf in (1, 0, 0, 1):
         st.update(ovf)
         assert st.value == 1.0
+    # growth restarts the clean-step count: with a window of 2, six clean
+    # steps double the scale after the 2nd, 4th and 6th, not after every step
+    # from the 2nd on
+    s = oracle.Scaler(8.0, dynamic=True, window=2)
+    trail = []
+    for _ in range(6):
+        s.update(0)
+        trail.append((s.value, s.good.value))
+    assert trail == [(8.0, 1), (16.0, 0), (16.0, 1), (32.0, 0), (32.0, 1), (64.0, 0)]
 
 
 def test_dna_scale_trajectory_halves_per_injection():
@@ -126,6 +135,24 @@ def test_partitioned_step_equals_unpartitioned(R):
     assert np.array_equal(part_param, full_param)
     assert np.array_equal(part_master.view(np.uint32), full_master.view(np.uint32))
     assert part_master.size == sum(numels)
+
+
+@pytest.mark.parametrize("pdt", ["f16", "bf16"])
+def test_write_param_casts_like_the_library_conversion(pdt):
+    # the written parameters are the IEEE round-to-nearest-even cast of the
+    # master (numpy float16 / torch bfloat16), in the parameter dtype asked for
+    import torch
+    rng = np.random.default_rng(11)
+    master = np.concatenate([rng.normal(0, 0.02, 3000), rng.normal(0, 300.0, 1000),
+                             rng.normal(0, 1e-6, 1000)]).astype(np.float32)
+    param = np.zeros(master.size, np.uint16)
+    oracle.write_param(master, master.size, 0, 0, param, pdt)
+    if pdt == "f16":
+        want = master.astype(np.float16).view(np.uint16)
+    else:
+        want = torch.from_numpy(master).to(torch.bfloat16).view(torch.int16).numpy().view(
+            np.uint16)
+    assert np.array_equal(param, want)
 
 
 def test_write_param_lands_at_offset_and_skips_padding():
