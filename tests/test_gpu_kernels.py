@@ -272,3 +272,71 @@ def test_wrong_device_and_bad_buffers_raise():
         z.zero_flatten_grads(plan, -1, [master], flat)
     with pytest.raises(z.ZeroError):         # window misses the shard
         z.zero_write_param_shard(plan, master, flat[:10], 0)
+
+
+@pytest.mark.parametrize("pdt", ["f16", "bf16"])
+def test_write_param_ragged_sizes_and_windows(pdt):
+    """The standalone cast on shards whose real length leaves a partial
+    2048-element block (and tiny ones), written through parameter windows
+    at several bases; everything outside the shard's range stays untouched."""
+    import torch
+    rng = np.random.default_rng(23)
+    for numels, R, r, A in [([1], 1, 0, 1), ([5], 1, 0, 1), ([2049], 1, 0, 1),
+                            ([4095, 3], 2, 1, 1), ([2048 * 7 + 1, 2047], 3, 2, 8),
+                            ([100003, 65, 2048], 2, 0, 64), ([100003, 65, 2048], 2, 1, 64)]:
+        plan = z.zero_partition_plan(numels, R, r, A)
+        P, S, real, begin = sum(numels), plan.S, plan.real, plan.begin
+        master = rng.normal(0, 0.5, S).astype(np.float32)
+        for base in (0, begin, max(begin - 3, 0)):
+            numel = P - base
+            buf = torch.full((numel + 5,), 7.0, dtype=torch_dtype(pdt), device=DEV)
+            win = buf[:numel]
+            z.zero_write_param_shard(plan, torch.from_numpy(master).to(DEV), win, base)
+            got = _bits(buf)
+            want = _bits(torch.full((numel + 5,), 7.0, dtype=torch_dtype(pdt)))
+            oracle.write_param(master, real, begin, base, want, pdt)
+            assert np.array_equal(got, want), (numels, R, r, base)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_partial_flatten_makes_the_step_scan(dt):
+    """Only some buckets are flattened; the rest of the flat shard is filled
+    another way (as a reduce-scatter would).  The step must test the whole
+    shard: an inf planted in the unflattened part skips it, a finite one
+    applies it exactly as the oracle does."""
+    import torch
+    numels = [3000, 1, 7, 100003, 65, 2048, 511, 30000, 13, 4099]
+    op = oracle.plan(numels, 2, 0, 8, bucket_elems=20000)
+    plan = z.zero_partition_plan(numels, 2, 0, 8, 20000)
+    assert plan.n_buckets >= 3
+    rng = np.random.default_rng(5)
+    host = [synth.half_bits(rng.normal(0, 1e-2, n).astype(np.float32), dt) for n in numels]
+    expect_flat = oracle.flatten(op, host)
+    tb = plan.tensor_buckets()
+    segs = plan.segments()
+    skip_b = tb[int(op.seg_tensor[0])]            # the bucket holding the first segment
+    lo = min(s.shard_off for s in segs if s.bucket == skip_b)
+    hi = max(s.shard_off + s.numel for s in segs if s.bucket == skip_b)
+    for plant in (False, True):
+        grads = [_to_dev_half(h, dt) for h in host]
+        flat = torch.empty(op.S, dtype=torch_dtype(dt), device=DEV)
+        for b in range(plan.n_buckets):
+            if b != skip_b:
+                z.zero_flatten_grads(plan, b, [g if tb[i] == b else None
+                                               for i, g in enumerate(grads)], flat)
+        part = expect_flat[lo:hi].copy()
+        if plant:
+            part[(hi - lo) // 2] = 0x7C00 if dt == "f16" else 0x7F80
+        flat[lo:hi].copy_(_to_dev_half(part, dt))
+        m0 = rng.normal(0, 0.02, op.S).astype(np.float32)
+        master = torch.from_numpy(m0.copy()).to(DEV)
+        mo = torch.zeros(op.S, device=DEV)
+        va = torch.zeros(op.S, device=DEV)
+        flag = z.zero_adam_step(plan, z.AdamHParams(), 1, 1.0, flat, master, mo, va)
+        om, omo, ov = m0.copy(), np.zeros(op.S, np.float32), np.zeros(op.S, np.float32)
+        oflat = expect_flat.copy()
+        oflat[lo:hi] = part
+        oflag = oracle.adam_step(1, 1.0, oflat, dt, om, omo, ov)
+        assert flag == oflag == (1 if plant else 0)
+        assert np.array_equal(master.cpu().numpy().view(np.uint32), om.view(np.uint32))
+        assert np.array_equal(va.cpu().numpy().view(np.uint32), ov.view(np.uint32))
