@@ -199,6 +199,11 @@ def test_offload_argument_errors_before_device_work():
                   ctypes.byref(out)) == _abi.ZERO_EINVAL
     assert create(plan.handle, ctypes.byref(hp), z.ZERO_BF16, z.ZERO_BF16, None, fake, fake, 4,
                   ctypes.byref(out)) == _abi.ZERO_ENULL
+    for bad in (z.AdamHParams(lr=float("inf")), z.AdamHParams(eps=float("inf")),
+                z.AdamHParams(beta2=1.0), z.AdamHParams(weight_decay=-1.0)):
+        bhp = bad.to_c()
+        assert create(plan.handle, ctypes.byref(bhp), z.ZERO_BF16, z.ZERO_BF16, fake, fake, fake,
+                      4, ctypes.byref(out)) == _abi.ZERO_EINVAL
     # the device state must be uploaded first
     assert create(plan.handle, ctypes.byref(hp), z.ZERO_BF16, z.ZERO_BF16, fake, fake, fake, 4,
                   ctypes.byref(out)) == _abi.ZERO_ESTATE

@@ -26,6 +26,17 @@ int hip_fail(hipError_t e, const char* what) {
     return ZERO_EHIP;
 }
 
+int check_hparams(const zero_adam_hparams_t* hp) {
+    if (!(hp->lr >= 0 && std::isfinite(hp->lr)) || !(hp->beta1 >= 0 && hp->beta1 < 1) ||
+        !(hp->beta2 >= 0 && hp->beta2 < 1) || !(hp->eps > 0 && std::isfinite(hp->eps)) ||
+        !(hp->weight_decay >= 0 && std::isfinite(hp->weight_decay))) {
+        return fail(ZERO_EINVAL, "hyperparameters out of range (lr >= 0, 0 <= betas < 1, eps > 0, "
+                                 "weight_decay >= 0)");
+    }
+    return ZERO_OK;
+}
+
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -116,16 +127,6 @@ DeviceStep* device_step(zero_plan* p) {
 AdamScalars* device_scalars(zero_plan* p) {
     return reinterpret_cast<AdamScalars*>(reinterpret_cast<char*>(p->dev.d_flag) +
                                           kScalarsOffset);
-}
-
-int check_hparams(const zero_adam_hparams_t* hp) {
-    if (!(hp->lr >= 0 && std::isfinite(hp->lr)) || !(hp->beta1 >= 0 && hp->beta1 < 1) ||
-        !(hp->beta2 >= 0 && hp->beta2 < 1) || !(hp->eps > 0 && std::isfinite(hp->eps)) ||
-        !(hp->weight_decay >= 0 && std::isfinite(hp->weight_decay))) {
-        return fail(ZERO_EINVAL, "hyperparameters out of range (lr >= 0, 0 <= betas < 1, eps > 0, "
-                                 "weight_decay >= 0)");
-    }
-    return ZERO_OK;
 }
 
 int check_scaler(const zero_scaler_t* sc) {

@@ -17,6 +17,9 @@ namespace zmi {
 void set_error(const std::string& msg);
 int fail(int code, const std::string& msg);
 int hip_fail(hipError_t e, const char* what);
+// ZERO_OK, or ZERO_EINVAL (with the message set) for hyperparameters out of
+// range: lr >= 0, 0 <= betas < 1, eps > 0, weight_decay >= 0, all finite.
+int check_hparams(const zero_adam_hparams_t* hp);
 
 // ---------------------------------------------------------------- plan
 struct Segment {

@@ -256,10 +256,8 @@ int zero_offload_create(zero_plan_t* p, const zero_adam_hparams_t* hp, int32_t g
         return fail(ZERO_EINVAL, "param_dtype must be 0, ZERO_F16 or ZERO_BF16");
     }
     if (n_threads < 1 || n_threads > 1024) return fail(ZERO_EINVAL, "n_threads must be in [1, 1024]");
-    if (!(hp->lr >= 0) || !(hp->beta1 >= 0 && hp->beta1 < 1) || !(hp->beta2 >= 0 && hp->beta2 < 1) ||
-        !(hp->eps > 0) || !(hp->weight_decay >= 0)) {
-        return fail(ZERO_EINVAL, "hyperparameters out of range");
-    }
+    const int hrc = check_hparams(hp);
+    if (hrc != ZERO_OK) return hrc;
     if (p->S > 0 && (master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr)) {
         return fail(ZERO_ENULL, "master, exp_avg and exp_avg_sq must be non-NULL");
     }
