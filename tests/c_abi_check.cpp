@@ -1,0 +1,223 @@
+// The C ABI on its own: a host program that drives libzero_mi355x through
+// include/zero_mi355x.h with hipMalloc'ed buffers (no Python, no torch) and
+// checks every step against the CPU oracle (oracle/zero_oracle.c, linked
+// as test infrastructure), bit for bit.
+//
+// Case: a ragged 9-tensor model, data-parallel degree 3, rank 1, align 8,
+// fp16 gradients and parameters, dynamic loss scale from 1024 with a window
+// of 2, AdamW, 8 steps, +inf injected into step 3's gradients.  Then the
+// same with Adam-L2 and bf16.  Inputs come from the seeded generator
+// (synth/synth_host.c); the fp32 -> half rounding of the inputs uses the
+// compiler's _Float16 / __bf16 conversions (IEEE round to nearest even).
+//
+// Prints "c-abi ok" and exits 0 on success; prints the first mismatch and
+// exits 1 otherwise.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "zero_mi355x.h"
+
+extern "C" {
+// oracle/zero_oracle.c
+int oracle_plan(const int64_t* numels, int64_t n, int64_t R, int64_t r, int64_t A, int64_t B,
+                int64_t* scal, int64_t* seg_tensor, int64_t* seg_tensor_off, int64_t* seg_shard_off,
+                int64_t* seg_numel, int64_t* tensor_bucket);
+void oracle_flatten(const uint16_t* const* grads, const int64_t* seg_tensor,
+                    const int64_t* seg_tensor_off, const int64_t* seg_shard_off,
+                    const int64_t* seg_numel, int64_t nseg, int64_t S, int64_t real, uint16_t* flat);
+int oracle_adam_step(int64_t n, int64_t t, double scale, const uint16_t* flat, int gdt,
+                     float* master, float* m, float* v, double lr, double b1, double b2,
+                     double eps, double wd, int adamw);
+void oracle_write_param(const float* master, int64_t real, int64_t begin, int64_t base,
+                        uint16_t* param, int pdt);
+void oracle_update_scale(double* scale, int32_t* good, int overflow, int dynamic,
+                         double min_scale, double backoff, double growth, int32_t window);
+// synth/synth_host.c
+uint64_t synth_key(uint64_t seed, uint32_t stream, uint32_t iter);
+void synth_fill_f32(float* out, int64_t n, uint64_t key, int64_t index0, float sigma, float scale,
+                    uint32_t outlier_thresh, float outlier_mult);
+}
+
+namespace {
+
+#define HIP_OK(x)                                                                \
+    do {                                                                         \
+        hipError_t e_ = (x);                                                     \
+        if (e_ != hipSuccess) {                                                  \
+            std::printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+            return 1;                                                            \
+        }                                                                        \
+    } while (0)
+
+#define ZERO_OK_OR_FAIL(x)                                                       \
+    do {                                                                         \
+        int rc_ = (x);                                                           \
+        if (rc_ < 0) {                                                           \
+            std::printf("%s failed: %d (%s)\n", #x, rc_, zero_last_error());      \
+            return 1;                                                            \
+        }                                                                        \
+    } while (0)
+
+uint16_t to_half(float x, int dt) {
+    uint16_t h;
+    if (dt == ZERO_F16) {
+        _Float16 y = static_cast<_Float16>(x);
+        std::memcpy(&h, &y, 2);
+    } else {
+        __bf16 y = static_cast<__bf16>(x);
+        std::memcpy(&h, &y, 2);
+    }
+    return h;
+}
+
+int run_case(int gdt, int adamw) {
+    const std::vector<int64_t> numels = {3000, 1, 7, 100003, 65, 2048, 511, 30000, 13};
+    const int R = 3, r = 1, A = 8, steps = 8, inject_step = 3;
+    const int64_t B = 20000;
+    const int n = static_cast<int>(numels.size());
+    int64_t P = 0;
+    std::vector<int64_t> off(n + 1, 0);
+    for (int i = 0; i < n; ++i) off[i + 1] = off[i] + numels[i];
+    P = off[n];
+
+    // plans: library and oracle
+    zero_plan_t* plan = nullptr;
+    ZERO_OK_OR_FAIL(zero_partition_plan(numels.data(), n, R, r, A, B, &plan));
+    zero_plan_info_t info;
+    ZERO_OK_OR_FAIL(zero_plan_info(plan, &info));
+    int64_t scal[10];
+    std::vector<int64_t> st(n), sto(n), sso(n), sn(n), tb(n);
+    if (oracle_plan(numels.data(), n, R, r, A, B, scal, st.data(), sto.data(), sso.data(),
+                    sn.data(), tb.data()) != 0) {
+        std::printf("oracle_plan failed\n");
+        return 1;
+    }
+    const int64_t S = scal[2], begin = scal[3], real = scal[4], nseg = scal[5];
+    if (info.shard_numel != S || info.shard_begin != begin || info.real_numel != real ||
+        info.n_segments != nseg) {
+        std::printf("plan mismatch\n");
+        return 1;
+    }
+
+    // device buffers
+    std::vector<void*> d_grads(n, nullptr);
+    for (int i = 0; i < n; ++i) HIP_OK(hipMalloc(&d_grads[i], 2 * numels[i]));
+    void *d_flat, *d_param;
+    float *d_master, *d_m, *d_v;
+    HIP_OK(hipMalloc(&d_flat, 2 * S));
+    HIP_OK(hipMalloc(&d_param, 2 * P));
+    HIP_OK(hipMalloc(reinterpret_cast<void**>(&d_master), 4 * S));
+    HIP_OK(hipMalloc(reinterpret_cast<void**>(&d_m), 4 * S));
+    HIP_OK(hipMalloc(reinterpret_cast<void**>(&d_v), 4 * S));
+
+    // initial state: master ~ N(0, 0.02) on the real part, moments zero,
+    // parameters filled with a pattern no finite master casts to
+    std::vector<float> o_master(S, 0.0f), o_m(S, 0.0f), o_v(S, 0.0f);
+    synth_fill_f32(o_master.data(), real, synth_key(0, 2, 0), begin, 0.02f, 1.0f, 0, 1.0f);
+    std::vector<uint16_t> o_param(P, 0xFFFF);
+    HIP_OK(hipMemcpy(d_master, o_master.data(), 4 * S, hipMemcpyHostToDevice));
+    HIP_OK(hipMemset(d_m, 0, 4 * S));
+    HIP_OK(hipMemset(d_v, 0, 4 * S));
+    HIP_OK(hipMemcpy(d_param, o_param.data(), 2 * P, hipMemcpyHostToDevice));
+
+    zero_adam_hparams_t hp = {1e-3, 0.9, 0.999, 1e-8, 0.05, adamw, 0};
+    const int dynamic = gdt == ZERO_F16;
+    zero_scaler_t scaler = {dynamic ? 1024.0 : 1.0, 1.0, 0.5, 2.0, 2, 0, dynamic, 0};
+    double o_scale = scaler.scale;
+    int32_t o_good = 0;
+    int64_t t = 0, o_t = 0;
+    hipStream_t s;
+    HIP_OK(hipStreamCreate(&s));
+
+    std::vector<std::vector<uint16_t>> grads(n);
+    std::vector<const uint16_t*> gptr(n);
+    std::vector<uint16_t> o_flat(S), g_flat(S), g_param(P);
+    std::vector<float> g_master(S), g_m(S), g_v(S), vals;
+    for (int it = 1; it <= steps; ++it) {
+        // this step's gradients, scaled by the current loss scale
+        for (int i = 0; i < n; ++i) {
+            vals.assign(numels[i], 0.0f);
+            synth_fill_f32(vals.data(), numels[i], synth_key(0, 1, it), off[i], 1e-2f,
+                           static_cast<float>(o_scale), 0, 1.0f);
+            grads[i].resize(numels[i]);
+            for (int64_t k = 0; k < numels[i]; ++k) grads[i][k] = to_half(vals[k], gdt);
+            gptr[i] = grads[i].data();
+        }
+        if (it == inject_step) {  // +inf in the middle of the shard's first segment
+            grads[st[0]][sto[0] + sn[0] / 2] = gdt == ZERO_F16 ? 0x7C00 : 0x7F80;
+        }
+        for (int i = 0; i < n; ++i) {
+            HIP_OK(hipMemcpy(d_grads[i], grads[i].data(), 2 * numels[i], hipMemcpyHostToDevice));
+        }
+        // library: flatten all buckets, gated step, scaler
+        std::vector<const void*> dg(d_grads.begin(), d_grads.end());
+        ZERO_OK_OR_FAIL(zero_flatten_grads(plan, -1, dg.data(), gdt, d_flat, s));
+        const double scale_used = scaler.scale;
+        const int flag = zero_adam_step(plan, &hp, t + 1, scale_used, d_flat, gdt, d_master, d_m,
+                                        d_v, d_param, 0, P, gdt, s);
+        ZERO_OK_OR_FAIL(flag);
+        ZERO_OK_OR_FAIL(zero_update_loss_scale(&scaler, flag));
+        if (!flag) ++t;
+        // oracle
+        oracle_flatten(gptr.data(), st.data(), sto.data(), sso.data(), sn.data(), nseg, S, real,
+                       o_flat.data());
+        const int o_flag = oracle_adam_step(S, o_t + 1, o_scale, o_flat.data(), gdt,
+                                            o_master.data(), o_m.data(), o_v.data(), hp.lr,
+                                            hp.beta1, hp.beta2, hp.eps, hp.weight_decay, adamw);
+        if (!o_flag) {
+            ++o_t;
+            oracle_write_param(o_master.data(), real, begin, 0, o_param.data(), gdt);
+        }
+        oracle_update_scale(&o_scale, &o_good, o_flag, dynamic, 1.0, 0.5, 2.0, 2);
+        // compare
+        if (flag != o_flag || t != o_t || scaler.scale != o_scale || scaler.good_steps != o_good) {
+            std::printf("step %d: flag %d/%d t %lld/%lld scale %g/%g\n", it, flag, o_flag,
+                        static_cast<long long>(t), static_cast<long long>(o_t), scaler.scale,
+                        o_scale);
+            return 1;
+        }
+        HIP_OK(hipMemcpy(g_flat.data(), d_flat, 2 * S, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_master.data(), d_master, 4 * S, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_m.data(), d_m, 4 * S, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_v.data(), d_v, 4 * S, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_param.data(), d_param, 2 * P, hipMemcpyDeviceToHost));
+        if (std::memcmp(g_flat.data(), o_flat.data(), 2 * S) != 0 ||
+            std::memcmp(g_master.data(), o_master.data(), 4 * S) != 0 ||
+            std::memcmp(g_m.data(), o_m.data(), 4 * S) != 0 ||
+            std::memcmp(g_v.data(), o_v.data(), 4 * S) != 0 ||
+            std::memcmp(g_param.data(), o_param.data(), 2 * P) != 0) {
+            std::printf("step %d: state differs from the oracle\n", it);
+            return 1;
+        }
+    }
+    // window 2, overflow at step 3: x2 after step 2, /2 at step 3, x2 after
+    // steps 5 and 7 -> 4096
+    if (dynamic && o_scale != 4096.0) {
+        std::printf("unexpected scale trajectory: %g\n", o_scale);
+        return 1;
+    }
+    for (void* p : d_grads) HIP_OK(hipFree(p));
+    HIP_OK(hipFree(d_flat));
+    HIP_OK(hipFree(d_param));
+    HIP_OK(hipFree(d_master));
+    HIP_OK(hipFree(d_m));
+    HIP_OK(hipFree(d_v));
+    HIP_OK(hipStreamDestroy(s));
+    zero_plan_destroy(plan);
+    std::printf("case gdt=%d adamw=%d: %d steps, %lld applied, scale %g\n", gdt, adamw, steps,
+                static_cast<long long>(t), scaler.scale);
+    return 0;
+}
+
+}  // namespace
+
+int main() {
+    if (run_case(ZERO_F16, 1) != 0) return 1;
+    if (run_case(ZERO_BF16, 0) != 0) return 1;
+    std::printf("c-abi ok\n");
+    return 0;
+}
