@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import statistics
 import os
 import sys
 import time
@@ -92,7 +93,8 @@ def setup(w, device):
         synth.dev_fill_half(part, gkey, offs[i] + s.tensor_off, w.grad_sigma, scale,
                             synth.outlier_thresh(w.outlier_p), w.outlier_mult)
     torch.cuda.synchronize(device)
-    return plan, master, m, v, flat, param, grads
+    # bound once, as a training loop that keeps its gradient buffers does
+    return plan, master, m, v, flat, param, z.GradList(plan, grads)
 
 
 def run_gpu(w, steps, warmup, device):
@@ -224,21 +226,116 @@ def run_offload(w, steps, warmup, device, n_threads):
         for _ in range(warmup):
             step()
         off.drain()
-        h0 = off.stats()["host_ms_total"]
+        s0 = off.stats()
         t0 = time.perf_counter()
         for _ in range(steps):
             step()
         off.drain()
         wall = time.perf_counter() - t0
         st = off.stats()
-        host_ms = (st["host_ms_total"] - h0) / steps
+        host_ms = (st["host_ms_total"] - s0["host_ms_total"]) / steps
         off.close()
         out[f"lag{lag}"] = {"ms_per_step": wall * 1000.0 / steps, "host_update_ms": host_ms,
                             "value": real / (wall / steps),
                             "host_update_params_per_s": S / (host_ms * 1e-3),
-                            "host_update_gbps": ADAM_BYTES_PER_ELEM * S / (host_ms * 1e-3) / 1e9}
+                            "host_update_gbps": ADAM_BYTES_PER_ELEM * S / (host_ms * 1e-3) / 1e9,
+                            # per step: where the worker and the caller wait
+                            "waits_ms": {k[:-len("_ms_total")]: (st[k] - s0[k]) / steps
+                                         for k in ("wait_submit_ms_total",
+                                                   "wait_grad_ms_total", "wait_h2d_ms_total",
+                                                   "wait_release_ms_total",
+                                                   "caller_wait_ms_total")}}
         log(f"[bench] offload lag={lag}: {out[f'lag{lag}']}")
     return plan, out
+
+
+def host_info():
+    """CPU model and core counts of the host the bench runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    quota = None
+    try:  # cgroup v2 CPU quota: "max" or "<quota> <period>"
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+        if q != "max":
+            quota = max(1, int(int(q) // int(period)))
+    except (OSError, ValueError):
+        pass
+    usable = affinity
+    for cap in (quota, os.environ.get("OMP_NUM_THREADS")):
+        if cap:
+            usable = min(usable, int(cap))
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": affinity,
+            "cgroup_quota_cpus": quota, "usable_cpus": max(1, usable)}
+
+
+def cpu_baseline_all_cores(w, plan_S, plan_begin, n_threads, target_s=8.0, window=1 << 22):
+    """The same oracle calls on n_threads host threads at once, each on its own
+    window of the shard (the step is elementwise, so the windows are
+    independent; ctypes releases the GIL inside the oracle's C code).  Rate =
+    elements processed by all threads / wall time of the concurrent run."""
+    import threading
+
+    import numpy as np
+
+    import oracle
+    import synth
+
+    n_threads = max(1, min(n_threads, plan_S // window if plan_S >= window else 1))
+    n = min(window, plan_S)
+    op = oracle.plan([n], 1, 0, 1)
+    hp = dict(lr=w.lr, b1=w.beta1, b2=w.beta2, eps=w.eps, wd=w.weight_decay, adamw=w.adamw)
+    gkey = synth.key(w.seed, synth.STREAM_GRAD, 1)
+    mkey = synth.key(w.seed, synth.STREAM_MASTER, 0)
+    bufs = []
+    for t in range(n_threads):
+        i0 = plan_begin + t * n
+        vals = synth.host_values(gkey, i0, n, w.grad_sigma, 1.0,
+                                 synth.outlier_thresh(w.outlier_p), w.outlier_mult)
+        bufs.append((synth.half_bits(vals, w.grad_dtype),
+                     synth.host_values(mkey, i0, n, w.master_sigma),
+                     np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)))
+    start = threading.Barrier(n_threads + 1)
+    counts = [0] * n_threads
+    stop_at = [0.0]
+
+    def work(t):
+        gbits, master, mm, vv, param = bufs[t]
+        start.wait()
+        while True:
+            flat = oracle.flatten(op, [gbits])
+            ovf = oracle.adam_step(counts[t] + 1, 1.0, flat, w.grad_dtype, master, mm, vv, **hp)
+            if not ovf:
+                oracle.write_param(master, n, 0, 0, param, w.param_dtype)
+            counts[t] += 1
+            if time.perf_counter() >= stop_at[0]:
+                break
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(n_threads)]
+    for th in threads:
+        th.start()
+    t0 = time.perf_counter()
+    stop_at[0] = t0 + target_s
+    start.wait()
+    for th in threads:
+        th.join()
+    el = time.perf_counter() - t0
+    rate = n * sum(counts) / el
+    return {"value": rate, "unit": "params/s", "cores": n_threads, "kind": "oracle",
+            "sample": f"{n_threads} host threads at once, each running the oracle (scalar C) "
+                      f"flatten + overflow test + AdamW + {w.param_dtype} cast on its own "
+                      f"{n}-element window of the shard; {sum(counts)} window-steps in {el:.1f} s"}
 
 
 def cpu_baseline(w, plan_S, plan_begin, target_s=12.0, window=1 << 24):
@@ -341,8 +438,10 @@ def main(argv=None):
     ap.add_argument("--mode", choices=["device", "offload"], default="device",
                     help="device: the whole step on the GPU (default); offload: ZeRO-Offload "
                          "(host-resident state, host update, one-step delayed update)")
-    ap.add_argument("--host-threads", type=int,
-                    default=int(os.environ.get("OMP_NUM_THREADS", "16")))
+    ap.add_argument("--host-threads", type=int, default=None,
+                    help="threads of the offload host update (default: the usable CPUs "
+                         "less one, which the caller and the HIP runtime need while the "
+                         "delayed update runs)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run only a plain copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
@@ -364,7 +463,8 @@ def main(argv=None):
     from synth.workloads import get
     w = get(args.workload)
     if args.mode == "offload":
-        plan, res = run_offload(w, args.steps, args.warmup, device, args.host_threads)
+        threads = args.host_threads or max(1, host_info()["usable_cpus"] - 1)
+        plan, res = run_offload(w, args.steps, args.warmup, device, threads)
         print(json.dumps({
             "metric": METRIC, "value": res["lag1"]["value"], "unit": "params/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["lag1"]["ms_per_step"],
@@ -406,10 +506,12 @@ def main(argv=None):
         "hbm_gbps_step": step_gbs,
         "pct_peak_step": 100.0 * step_gbs / HBM_PEAK_GBS,
         "kernels": {
-            "adam_fused": {"avg_ms": adam_ms, "min_ms": min(times["adam"]),
+            "adam_fused": {"avg_ms": adam_ms, "median_ms": statistics.median(times["adam"]),
+                           "min_ms": min(times["adam"]),
                            "bytes_per_elem": ADAM_BYTES_PER_ELEM, "gbps": adam_gbs,
                            "params_per_s": S / (adam_ms * 1e-3)},
-            "flatten": {"avg_ms": flat_ms, "min_ms": min(times["flatten"]),
+            "flatten": {"avg_ms": flat_ms, "median_ms": statistics.median(times["flatten"]),
+                        "min_ms": min(times["flatten"]),
                         "bytes_per_elem": FLATTEN_BYTES_PER_ELEM, "gbps": flat_gbs},
             "write_param": {"ms": write_ms, "bytes_per_elem": 6,
                             "gbps": 6 * real / (write_ms * 1e-3) / 1e9},
@@ -430,6 +532,11 @@ def main(argv=None):
         log("[bench] timing the oracle on the host")
         cb = cpu_baseline(w, S, begin, target_s=args.cpu_seconds)
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        host = host_info()
+        out["cpu_baseline"]["host"] = host
+        log(f"[bench] timing the oracle on {host['usable_cpus']} host threads")
+        out["cpu_baseline"]["all_cores"] = cpu_baseline_all_cores(
+            w, S, begin, host["usable_cpus"], target_s=max(2.0, args.cpu_seconds * 2 / 3))
     print(json.dumps(out), flush=True)
     return 0
 

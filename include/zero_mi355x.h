@@ -339,6 +339,18 @@ typedef struct {
     int32_t _pad;
     double host_ms_last;    /* host update time of the last applied step */
     double host_ms_total;
+    /* where the time outside the host update goes (totals, ms): the worker
+     * idle until the next submit, waiting for a step's gradient copy, for
+     * the previous parameter copy out of the same pinned buffer, and for the
+     * caller's release of the device parameters; the caller's threads
+     * blocked in submit / wait_params until the worker finished a step.  A
+     * pipeline bound by the host update shows caller waits and almost no
+     * worker waits; one bound by the caller shows wait_submit. */
+    double wait_submit_ms_total;
+    double wait_grad_ms_total;
+    double wait_h2d_ms_total;
+    double wait_release_ms_total;
+    double caller_wait_ms_total;
 } zero_offload_stats_t;
 
 /* Creates the pipeline for `plan`, whose device state must already hold t

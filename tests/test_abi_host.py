@@ -12,6 +12,7 @@ import os
 import random
 import re
 
+import numpy as np
 import pytest
 
 import oracle
@@ -180,6 +181,19 @@ def test_async_step_argument_errors_before_device_work():
     sc = _abi.zero_scaler_t(1024.0, 1.0, 0.5, 2.0, 10, 0, 1, 0)
     assert lib.zero_state_upload(plan.handle, -1, ctypes.byref(sc), None) == _abi.ZERO_EINVAL
     assert lib.zero_state_upload(None, 0, ctypes.byref(sc), None) == _abi.ZERO_ENULL
+
+
+def test_grad_list_checks_when_bound():
+    import torch
+    plan = z.zero_partition_plan([1000, 24], 2, 0, 8)
+    with pytest.raises(ValueError, match="need 2 gradient entries"):
+        z.GradList(plan, [None])
+    with pytest.raises(ValueError, match="device tensor"):
+        z.GradList(plan, [torch.zeros(1000, dtype=torch.bfloat16), None])
+    with pytest.raises(TypeError, match="torch tensor"):
+        z.GradList(plan, [np.zeros(1000, np.uint16), None])
+    empty = z.GradList(plan, [None, None])   # nothing bound: no dtype to check
+    assert empty.dtype is None and list(empty.ptrs) == [None, None]
 
 
 def test_offload_argument_errors_before_device_work():

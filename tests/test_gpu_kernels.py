@@ -66,10 +66,16 @@ def test_flatten_every_source_misalignment(dt):
             views.append(v)
             off += n + (8 - (off + n) % 8)
         expect = oracle.flatten(op, host)
-        for mode in ("all", "buckets", "reverse"):
+        bound = z.GradList(plan, views)
+        for mode in ("all", "buckets", "reverse", "bound", "bound buckets"):
             flat = torch.full((max(op.S, 8),), float("nan"), dtype=torch_dtype(dt), device=DEV)
             if mode == "all":
                 z.zero_flatten_grads(plan, -1, views, flat)
+            elif mode == "bound":
+                z.zero_flatten_grads(plan, -1, bound, flat)
+            elif mode == "bound buckets":  # one bound list serves every bucket
+                for b in range(plan.n_buckets):
+                    z.zero_flatten_grads(plan, b, bound, flat)
             else:
                 tb = plan.tensor_buckets()
                 order = range(plan.n_buckets) if mode == "buckets" else \

@@ -70,6 +70,10 @@ def _offload_run(case, lag, label, write_params=True, n_threads=4):
     off.drain()
     stats = off.stats()
     assert stats["applied"] == orc.t and stats["skipped"] == skipped, stats
+    assert stats["submitted"] == stats["processed"] == case.steps, stats
+    for k in ("host_ms_total", "wait_submit_ms_total", "wait_grad_ms_total",
+              "wait_h2d_ms_total", "wait_release_ms_total", "caller_wait_ms_total"):
+        assert np.isfinite(stats[k]) and stats[k] >= 0.0, (k, stats)
     st = z.zero_state_download(plan)
     assert (st.applied_steps, st.skipped_steps, st.scale) == (orc.t, skipped, orc.scaler.value)
     for name, a, b in (("master", master, orc.master), ("m", mom, orc.m), ("v", var, orc.v)):

@@ -8,6 +8,7 @@ and the stream.  The functions keep the names of the C ABI
 
     zero_partition_plan(numels, world_size, rank, align_elems, bucket_elems) -> Plan
     zero_flatten_grads(plan, bucket, grads, flat_grad, stream=None)
+                                (grads: a list of tensors, or a GradList bound once)
     zero_adam_step(plan, hparams, step, loss_scale, flat_grad, master, exp_avg,
                    exp_avg_sq, param=None, param_base=0, stream=None) -> 0 | 1
     zero_update_loss_scale(scaler, overflow)
@@ -42,7 +43,7 @@ from . import _abi
 from ._abi import ZERO_BF16, ZERO_F16, ZeroError, check, lib  # noqa: F401
 
 __all__ = ["Plan", "AdamHParams", "LossScaler", "DeviceStepState", "ZeroError",
-           "zero_partition_plan", "zero_flatten_grads", "zero_adam_step",
+           "zero_partition_plan", "GradList", "zero_flatten_grads", "zero_adam_step",
            "zero_update_loss_scale", "zero_write_param_shard", "zero_state_upload",
            "zero_adam_step_async", "zero_state_download", "zero_state_device_scale",
            "zero_cpu_adam_step", "zero_cpu_isa", "Offload", "zero_last_error", "ZERO_F16",
@@ -124,10 +125,14 @@ class Plan:
         check(lib.zero_plan_info(self._h, ctypes.byref(info)), "zero_plan_info")
         self.info = info
 
+    # bound at class creation: module globals may already be gone when a
+    # plan is collected at interpreter exit
+    _destroy = staticmethod(lib.zero_plan_destroy)
+
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            lib.zero_plan_destroy(h)
+            self._destroy(h)
             self._h = None
 
     @property
@@ -177,23 +182,58 @@ def zero_partition_plan(numels: Sequence[int], world_size: int, rank: int,
     return plan
 
 
-def zero_flatten_grads(plan: Plan, bucket: int, grads: Sequence, flat_grad, stream=None) -> None:
+class GradList:
+    """A plan's gradient tensors, checked once.
+
+    A training loop that keeps its gradient buffers from step to step binds
+    them once; zero_flatten_grads then takes the stored pointer array as is,
+    with no per-tensor checks on the step path (a model with hundreds of
+    tensors otherwise spends about a millisecond per call in them).  The
+    list keeps the tensors alive; rebind after reallocating any of them."""
+
+    def __init__(self, plan: Plan, grads: Sequence):
+        torch = _torch()
+        if len(grads) != plan.n_tensors:
+            raise ValueError(f"need {plan.n_tensors} gradient entries, got {len(grads)}")
+        numels = _plan_numels(plan)
+        self.plan = plan
+        self.dtype = None
+        self.ptrs = (ctypes.c_void_p * max(len(grads), 1))()
+        for i, g in enumerate(grads):
+            if g is None:
+                continue
+            _require(g, f"grads[{i}]", int(numels[i]),
+                     (self.dtype,) if self.dtype is not None else (torch.float16, torch.bfloat16))
+            self.dtype = g.dtype
+            self.ptrs[i] = g.data_ptr()
+        self._tensors = list(grads)
+
+
+def zero_flatten_grads(plan: Plan, bucket: int, grads, flat_grad, stream=None) -> None:
     """grads: one entry per tensor (a contiguous fp16/bf16 device tensor, or None for a
-    tensor without elements in the requested buckets of this shard)."""
+    tensor without elements in the requested buckets of this shard), or a GradList
+    bound to this plan."""
     torch = _torch()
-    if len(grads) != plan.n_tensors:
-        raise ValueError(f"need {plan.n_tensors} gradient entries, got {len(grads)}")
     _require(flat_grad, "flat_grad", plan.S, (torch.float16, torch.bfloat16))
-    numels = None
-    ptrs = (ctypes.c_void_p * max(len(grads), 1))()
-    for i, g in enumerate(grads):
-        if g is None:
-            ptrs[i] = None
-            continue
-        if numels is None:
-            numels = [int(n) for n in _plan_numels(plan)]
-        _require(g, f"grads[{i}]", numels[i], (flat_grad.dtype,))
-        ptrs[i] = g.data_ptr()
+    if isinstance(grads, GradList):
+        if grads.plan is not plan:
+            raise ValueError("the GradList is bound to another plan")
+        if grads.dtype is not None and grads.dtype != flat_grad.dtype:
+            raise TypeError(f"gradients are {grads.dtype}, flat_grad is {flat_grad.dtype}")
+        ptrs = grads.ptrs
+    else:
+        if len(grads) != plan.n_tensors:
+            raise ValueError(f"need {plan.n_tensors} gradient entries, got {len(grads)}")
+        numels = None
+        ptrs = (ctypes.c_void_p * max(len(grads), 1))()
+        for i, g in enumerate(grads):
+            if g is None:
+                ptrs[i] = None
+                continue
+            if numels is None:
+                numels = [int(n) for n in _plan_numels(plan)]
+            _require(g, f"grads[{i}]", numels[i], (flat_grad.dtype,))
+            ptrs[i] = g.data_ptr()
     check(lib.zero_flatten_grads(plan.handle, bucket, ptrs, _dtype_code(flat_grad),
                                  flat_grad.data_ptr(), _stream_handle(stream, flat_grad.device)),
           "zero_flatten_grads")
@@ -415,10 +455,12 @@ class Offload:
         check(lib.zero_offload_stats(self._h, ctypes.byref(st)), "zero_offload_stats")
         return {k: getattr(st, k) for k, _ in st._fields_ if k != "_pad"}
 
+    _destroy = staticmethod(lib.zero_offload_destroy)
+
     def close(self) -> None:
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            lib.zero_offload_destroy(h)
+            self._destroy(h)
             self._h = None
 
     def __del__(self):

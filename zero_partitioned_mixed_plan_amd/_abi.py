@@ -52,7 +52,11 @@ class zero_offload_stats_t(ctypes.Structure):
     _fields_ = [("submitted", ctypes.c_int64), ("processed", ctypes.c_int64),
                 ("applied", ctypes.c_int64), ("skipped", ctypes.c_int64),
                 ("last_flag", ctypes.c_int32), ("_pad", ctypes.c_int32),
-                ("host_ms_last", ctypes.c_double), ("host_ms_total", ctypes.c_double)]
+                ("host_ms_last", ctypes.c_double), ("host_ms_total", ctypes.c_double),
+                ("wait_submit_ms_total", ctypes.c_double),
+                ("wait_grad_ms_total", ctypes.c_double), ("wait_h2d_ms_total", ctypes.c_double),
+                ("wait_release_ms_total", ctypes.c_double),
+                ("caller_wait_ms_total", ctypes.c_double)]
 
 
 class zero_scaler_t(ctypes.Structure):

@@ -82,11 +82,19 @@ struct zero_offload {
     int64_t applied = 0, skipped = 0;
     int32_t last_flag = 0;
     double host_ms_last = 0, host_ms_total = 0;
+    double wait_submit_ms = 0, wait_grad_ms = 0, wait_h2d_ms = 0, wait_release_ms = 0;
+    double caller_wait_ms = 0;
     int err = ZERO_OK;
     std::string err_msg;
 };
 
 namespace {
+
+using Clock = std::chrono::steady_clock;
+
+double ms_since(Clock::time_point t0) {
+    return std::chrono::duration<double, std::milli>(Clock::now() - t0).count();
+}
 
 void set_worker_error(zero_offload* o, int code, const std::string& msg) {
     std::lock_guard<std::mutex> g(o->mu);
@@ -109,21 +117,27 @@ void worker_main(zero_offload* o) {
     const zero_plan* p = o->plan;
     for (int64_t j = 0;; ++j) {
         const int b = static_cast<int>(j & 1);
+        auto tw = Clock::now();
         {
             std::unique_lock<std::mutex> lk(o->mu);
             o->cv.wait(lk, [&] { return o->stop || o->submitted > j; });
             if (o->submitted <= j) return;  // stopped with nothing left
         }
+        const double wait_submit = ms_since(tw);
+        tw = Clock::now();
         if (worker_hip(o, hipEventSynchronize(o->ev_d2h[b]), "gradient copy") != ZERO_OK) return;
+        double wait_grad = ms_since(tw), wait_h2d = 0, wait_release = 0;
         const OffloadSlot slot = o->hslot[b];
         bool applied = false;
         bool sent = false;
         if (slot.flag == 0) {
             // the pinned parameter buffer b was last sent by step j - 2
+            tw = Clock::now();
             if (o->h2d_recorded[b] &&
                 worker_hip(o, hipEventSynchronize(o->ev_h2d[b]), "parameter copy") != ZERO_OK) {
                 return;
             }
+            wait_h2d = ms_since(tw);
             CpuAdamArgs a;
             a.g = o->hgrad[b];
             a.p = o->master;
@@ -138,24 +152,24 @@ void worker_main(zero_offload* o) {
             a.gdt = o->gdt;
             a.pdt = o->pdt;
             a.adamw = o->hp.adamw != 0;
-            const auto t0 = std::chrono::steady_clock::now();
+            const auto t0 = Clock::now();
             try {
                 cpu_adam(a, o->n_threads);
             } catch (const std::exception& ex) {
                 set_worker_error(o, ZERO_ENOMEM, std::string("host update: ") + ex.what());
                 return;
             }
-            const double ms =
-                std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0)
-                    .count();
+            const double ms = ms_since(t0);
             applied = true;
             uint16_t* dst = nullptr;
             {
                 std::unique_lock<std::mutex> lk(o->mu);
                 o->host_ms_last = ms;
                 o->host_ms_total += ms;
+                tw = Clock::now();
                 o->cv.wait(lk, [&] { return o->stop || o->rec[b].free_recorded; });
                 if (!o->rec[b].free_recorded) return;
+                wait_release = ms_since(tw);
                 dst = o->rec[b].param_dst;
             }
             if (o->pdt != 0 && p->real > 0 && dst != nullptr) {
@@ -173,6 +187,10 @@ void worker_main(zero_offload* o) {
         }
         std::lock_guard<std::mutex> g(o->mu);
         if (sent) o->h2d_recorded[b] = true;
+        o->wait_submit_ms += wait_submit;
+        o->wait_grad_ms += wait_grad;
+        o->wait_h2d_ms += wait_h2d;
+        o->wait_release_ms += wait_release;
         o->rec[b].processed = true;
         o->rec[b].applied = applied;
         o->processed = j + 1;
@@ -212,7 +230,11 @@ int release_params(zero_offload* o, int64_t j, hipStream_t s) {
 // Host wait until step j's host part is done (or an error / stop).
 int wait_processed(zero_offload* o, int64_t j) {
     std::unique_lock<std::mutex> lk(o->mu);
-    o->cv.wait(lk, [&] { return o->err != ZERO_OK || o->processed > j; });
+    if (o->err == ZERO_OK && o->processed <= j) {
+        const auto tw = Clock::now();
+        o->cv.wait(lk, [&] { return o->err != ZERO_OK || o->processed > j; });
+        o->caller_wait_ms += ms_since(tw);
+    }
     if (o->err != ZERO_OK) return fail(o->err, "offload worker failed: " + o->err_msg);
     return ZERO_OK;
 }
@@ -431,6 +453,11 @@ int zero_offload_stats(zero_offload_t* o, zero_offload_stats_t* out) {
         out->last_flag = o->last_flag;
         out->host_ms_last = o->host_ms_last;
         out->host_ms_total = o->host_ms_total;
+        out->wait_submit_ms_total = o->wait_submit_ms;
+        out->wait_grad_ms_total = o->wait_grad_ms;
+        out->wait_h2d_ms_total = o->wait_h2d_ms;
+        out->wait_release_ms_total = o->wait_release_ms;
+        out->caller_wait_ms_total = o->caller_wait_ms;
     }
     return offload_error(o);
 }
