@@ -24,7 +24,8 @@ LIB_PATH = os.environ.get("ZERO_ORACLE_LIB") or os.path.join(_HERE, "liboracle.s
 
 F16 = 1
 BF16 = 2
-DTYPES = {"f16": F16, "bf16": BF16}
+F32 = 3
+DTYPES = {"f16": F16, "bf16": BF16, "f32": F32}
 
 _lib = None
 
@@ -40,6 +41,8 @@ def _load():
         lib.oracle_plan.argtypes = [P, i64, i64, i64, i64, i64, P, P, P, P, P, P]
         lib.oracle_flatten.restype = None
         lib.oracle_flatten.argtypes = [P, P, P, P, P, i64, i64, i64, P]
+        lib.oracle_flatten_f32.restype = None
+        lib.oracle_flatten_f32.argtypes = [P, P, P, P, P, i64, i64, i64, P]
         lib.oracle_nonfinite.restype = ctypes.c_int
         lib.oracle_nonfinite.argtypes = [P, i64, ctypes.c_int]
         lib.oracle_half_to_float_n.restype = None
@@ -104,9 +107,24 @@ def plan(numels: Sequence[int], world_size: int, rank: int, align: int = 64,
                       bytes_stage2=int(scal[8]), bytes_stage3=int(scal[9]))
 
 
-def flatten(p: OraclePlan, grads: List[Optional[np.ndarray]]) -> np.ndarray:
-    """grads[i]: uint16 array of tensor i's gradient bits (None when it has no segment)."""
-    keep = [np.ascontiguousarray(g, dtype=np.uint16) if g is not None else None for g in grads]
+def _grad_word(grads) -> type:
+    """uint32 when the gradients are fp32 bits (uint32 or float32 arrays), else uint16."""
+    for g in grads:
+        if g is not None:
+            return np.uint32 if np.asarray(g).dtype in (np.uint32, np.float32) else np.uint16
+    return np.uint16
+
+
+def flatten(p: OraclePlan, grads: List[Optional[np.ndarray]],
+            dtype: Optional[str] = None) -> np.ndarray:
+    """grads[i]: tensor i's gradient bits (None when it has no segment): uint16 arrays of
+    fp16 / bf16 bits, or uint32 / float32 arrays of fp32 gradients (then the flat shard
+    is uint32).  dtype ("f16", "bf16", "f32") fixes the element width when no array
+    gives it."""
+    word = _grad_word(grads) if dtype is None else (np.uint32 if dtype == "f32" else np.uint16)
+    keep = [None if g is None else
+            np.ascontiguousarray(np.asarray(g).view(word) if np.asarray(g).dtype == np.float32
+                                 else g, dtype=word) for g in grads]
     ptrs = (ctypes.c_void_p * max(len(keep), 1))()
     for i, g in enumerate(keep):
         ptrs[i] = g.ctypes.data if g is not None else None
@@ -114,15 +132,17 @@ def flatten(p: OraclePlan, grads: List[Optional[np.ndarray]]) -> np.ndarray:
         g = keep[int(p.seg_tensor[s])]
         if g is None or g.size < p.seg_tensor_off[s] + p.seg_numel[s]:
             raise ValueError(f"gradient of tensor {int(p.seg_tensor[s])} missing or too small")
-    flat = np.full(p.S, 0xDEAD, dtype=np.uint16)   # every element must be written
-    _load().oracle_flatten(ctypes.addressof(ptrs), _ptr(p.seg_tensor), _ptr(p.seg_tensor_off),
+    flat = np.full(p.S, 0xDEAD, dtype=word)   # every element must be written
+    fn = _load().oracle_flatten_f32 if word == np.uint32 else _load().oracle_flatten
+    fn(ctypes.addressof(ptrs), _ptr(p.seg_tensor), _ptr(p.seg_tensor_off),
                            _ptr(p.seg_shard_off), _ptr(p.seg_numel), p.n_segments, p.S, p.real,
                            _ptr(flat))
     return flat
 
 
 def nonfinite(h: np.ndarray, dtype: str) -> bool:
-    h = np.ascontiguousarray(h, dtype=np.uint16)
+    """h: uint16 bits of fp16 / bf16 gradients, or uint32 bits of fp32 ones (dtype "f32")."""
+    h = _grad_bits(h, dtype)
     return bool(_load().oracle_nonfinite(_ptr(h), h.size, DTYPES[dtype]))
 
 
@@ -140,10 +160,18 @@ def float_to_half(x: np.ndarray, dtype: str) -> np.ndarray:
     return out
 
 
+def _grad_bits(g: np.ndarray, dtype: str) -> np.ndarray:
+    g = np.asarray(g)
+    if dtype == "f32":
+        return np.ascontiguousarray(g.view(np.uint32) if g.dtype == np.float32 else g,
+                                    dtype=np.uint32)
+    return np.ascontiguousarray(g, dtype=np.uint16)
+
+
 def _adam(fn, t, scale, flat, gdt, master, m, v, lr, b1, b2, eps, wd, adamw):
     for a in (master, m, v):
         assert a.dtype == np.float32 and a.flags.c_contiguous
-    flat = np.ascontiguousarray(flat, dtype=np.uint16)
+    flat = _grad_bits(flat, gdt)
     n = master.size
     assert flat.size == n and m.size == n and v.size == n
     return fn(n, t, scale, _ptr(flat), DTYPES[gdt], _ptr(master), _ptr(m), _ptr(v), lr, b1, b2,

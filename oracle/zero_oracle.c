@@ -16,7 +16,9 @@
  *
  * Precision: the pages fix fp32 for the master weights, momentum and
  * variance ([genomic] memory breakdown; [legal] mixed-precision paragraph),
- * and fp16/bf16 for parameters and gradients.  The update therefore runs in
+ * and fp16/bf16 for parameters and gradients; gradients kept in fp32 (an
+ * accumulation buffer, which the pages do not describe) are accepted too
+ * and enter the same update without a conversion.  The update runs in
  * fp32, one rounding per operation, no contraction (built with
  * -ffp-contract=off, no fast-math); host scalars are formed in double and
  * rounded once to fp32.  The pages leave the Adam formula, the operation
@@ -31,7 +33,7 @@
 #include <stdint.h>
 #include <string.h>
 
-enum { OR_F16 = 1, OR_BF16 = 2 };
+enum { OR_F16 = 1, OR_BF16 = 2, OR_F32 = 3 };
 
 /* ------------------------------------------------------------------------
  * Partition plan.
@@ -134,18 +136,48 @@ void oracle_flatten(const uint16_t* const* grads, const int64_t* seg_tensor,
     for (int64_t k = real; k < S; ++k) flat[k] = 0;
 }
 
+/* The same for fp32 gradients (kept in fp32, e.g. accumulated over
+ * micro-batches): each element is a 4-byte bit copy. */
+void oracle_flatten_f32(const uint32_t* const* grads, const int64_t* seg_tensor,
+                        const int64_t* seg_tensor_off, const int64_t* seg_shard_off,
+                        const int64_t* seg_numel, int64_t nseg, int64_t S, int64_t real,
+                        uint32_t* flat) {
+    for (int64_t s = 0; s < nseg; ++s) {
+        const uint32_t* src = grads[seg_tensor[s]];
+        for (int64_t k = 0; k < seg_numel[s]; ++k) {
+            flat[seg_shard_off[s] + k] = src[seg_tensor_off[s] + k];
+        }
+    }
+    for (int64_t k = real; k < S; ++k) flat[k] = 0u;
+}
+
 /* ------------------------------------------------------------------------
  * Overflow test ([legal] dynamic loss scaling bullet; [instr] loss-scaling
- * bullet).  Reading: a step overflows when any half-precision gradient of
- * the shard is +-inf or NaN, i.e. its exponent field is all ones (IEEE 754
- * binary16: bits 14..10; bfloat16: bits 14..7).
+ * bullet).  Reading: a step overflows when any gradient of the shard is
+ * +-inf or NaN, i.e. its exponent field is all ones (IEEE 754 binary16:
+ * bits 14..10; bfloat16: bits 14..7; binary32, for gradients kept in fp32:
+ * bits 30..23).
  * ---------------------------------------------------------------------- */
 static int half_is_nonfinite(uint16_t h, int dtype) {
     if (dtype == OR_F16) return ((h >> 10) & 0x1F) == 0x1F;
     return ((h >> 7) & 0xFF) == 0xFF;
 }
 
-int oracle_nonfinite(const uint16_t* h, int64_t n, int dtype) {
+/* IEEE 754 binary32: exponent field bits 30..23. */
+static int single_is_nonfinite(uint32_t u) {
+    return ((u >> 23) & 0xFFu) == 0xFFu;
+}
+
+/* g: n gradients of dtype OR_F16 / OR_BF16 (2 bytes each) or OR_F32 (4). */
+int oracle_nonfinite(const void* g, int64_t n, int dtype) {
+    if (dtype == OR_F32) {
+        const uint32_t* w = (const uint32_t*)g;
+        for (int64_t k = 0; k < n; ++k) {
+            if (single_is_nonfinite(w[k])) return 1;
+        }
+        return 0;
+    }
+    const uint16_t* h = (const uint16_t*)g;
     for (int64_t k = 0; k < n; ++k) {
         if (half_is_nonfinite(h[k], dtype)) return 1;
     }
@@ -268,13 +300,25 @@ void oracle_half_to_float_n(const uint16_t* h, int64_t n, int dtype, float* out)
  *   c_decay = 1 - lr*wd (AdamW) or 1 (Adam-L2), c_wd = wd
  * (b^t from the C library's pow).  Per element, fp32, one rounding each:
  *   g = h2f(h) * c_inv;            [Adam-L2: g = g + c_wd * p]
+ *                                  (fp32 gradients: g = h * c_inv)
  *   m = c_b1 * m + c_omb1 * g
  *   v = c_b2 * v + c_omb2 * (g * g)
  *   d = sqrt(v) * c_rsbc2 + c_eps
  *   u = m / d
  *   p = p * c_decay - c_step * u
  * ---------------------------------------------------------------------- */
-void oracle_adam_update(int64_t n, int64_t t, double scale, const uint16_t* flat, int gdt,
+/* Gradient k of the flat shard as fp32: fp32 gradients are read as they
+ * are, half ones converted exactly. */
+static float grad_as_float(const void* flat, int64_t k, int gdt) {
+    if (gdt == OR_F32) {
+        uint32_t u;
+        memcpy(&u, (const unsigned char*)flat + 4 * k, 4);
+        return f32_from_bits(u);
+    }
+    return oracle_half_to_float(((const uint16_t*)flat)[k], gdt);
+}
+
+void oracle_adam_update(int64_t n, int64_t t, double scale, const void* flat, int gdt,
                         float* master, float* m, float* v, double lr, double b1, double b2,
                         double eps, double wd, int adamw) {
     float c_inv = (float)(1.0 / scale);
@@ -289,7 +333,7 @@ void oracle_adam_update(int64_t n, int64_t t, double scale, const uint16_t* flat
     float c_wd = (float)wd;
     for (int64_t k = 0; k < n; ++k) {
         float p = master[k];
-        float g = oracle_half_to_float(flat[k], gdt) * c_inv;
+        float g = grad_as_float(flat, k, gdt) * c_inv;
         if (!adamw) g = g + c_wd * p;
         float mk = c_b1 * m[k] + c_omb1 * g;
         float vk = c_b2 * v[k] + c_omb2 * (g * g);
@@ -305,7 +349,7 @@ void oracle_adam_update(int64_t n, int64_t t, double scale, const uint16_t* flat
 /* Whole step on the shard: an overflowing step changes nothing and returns
  * 1 (reading: the skipped step leaves master, moments and params bit for
  * bit as they were); otherwise the update is applied and 0 is returned. */
-int oracle_adam_step(int64_t n, int64_t t, double scale, const uint16_t* flat, int gdt,
+int oracle_adam_step(int64_t n, int64_t t, double scale, const void* flat, int gdt,
                      float* master, float* m, float* v, double lr, double b1, double b2,
                      double eps, double wd, int adamw) {
     if (oracle_nonfinite(flat, n, gdt)) return 1;

@@ -29,7 +29,7 @@ int oracle_plan(const int64_t* numels, int64_t n, int64_t R, int64_t r, int64_t 
 void oracle_flatten(const uint16_t* const* grads, const int64_t* seg_tensor,
                     const int64_t* seg_tensor_off, const int64_t* seg_shard_off,
                     const int64_t* seg_numel, int64_t nseg, int64_t S, int64_t real, uint16_t* flat);
-int oracle_adam_step(int64_t n, int64_t t, double scale, const uint16_t* flat, int gdt,
+int oracle_adam_step(int64_t n, int64_t t, double scale, const void* flat, int gdt,
                      float* master, float* m, float* v, double lr, double b1, double b2,
                      double eps, double wd, int adamw);
 void oracle_write_param(const float* master, int64_t real, int64_t begin, int64_t base,

@@ -102,7 +102,7 @@ def _torch_run(cls, p0, grads, scale, wd, steps):
 
 
 @pytest.mark.parametrize("adamw", [True, False])
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 def test_matches_torch_optim_in_float64(adamw, dt):
     rng = np.random.default_rng(7)
     n, steps, scale = 4096, 10, (1024.0 if dt == "f16" else 1.0)
@@ -110,10 +110,13 @@ def test_matches_torch_optim_in_float64(adamw, dt):
     raw = [(rng.normal(0, 1e-3, n) * scale).astype(np.float32) for _ in range(steps)]
     if dt == "f16":
         hs = [r.astype(np.float16).view(np.uint16) for r in raw]
-    else:
+    elif dt == "bf16":
         hs = [torch.from_numpy(r).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
               for r in raw]
-    gvals = [oracle.half_to_float(h, dt).astype(np.float64) for h in hs]
+    else:
+        hs = [r.view(np.uint32) for r in raw]
+    gvals = [(r.astype(np.float64) if dt == "f32" else
+              oracle.half_to_float(h, dt).astype(np.float64)) for r, h in zip(raw, hs)]
     p, m, v = p0.copy(), *_zeros(n)[1:]
     for t in range(1, steps + 1):
         assert oracle.adam_step(t, scale, hs[t - 1], dt, p, m, v, LR, B1, B2, EPS, WD, adamw) == 0
@@ -168,3 +171,38 @@ def test_largest_finite_gradient_does_not_skip():
     hb = np.array([0x7F7F, 0xFF7F], np.uint16)                   # bf16 max finite
     p, m, v = _zeros(2)
     assert oracle.adam_step(1, 1.0, hb, "bf16", p, m, v) == 0
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_f32_gradients_equal_the_half_path_on_values_it_represents(dt):
+    # fp32 gradients that are exactly fp16 / bf16 values give the half path's
+    # state bit for bit: the update reads the value, not the encoding
+    rng = np.random.default_rng(11)
+    n, scale = 2049, (1024.0 if dt == "f16" else 1.0)
+    h = oracle.float_to_half((rng.normal(0, 1e-3, n) * scale).astype(np.float32), dt)
+    f = oracle.half_to_float(h, dt)
+    a = [rng.normal(0, 0.02, n).astype(np.float32), *_zeros(n)[1:]]
+    b = [x.copy() for x in a]
+    for t in range(1, 6):
+        for adamw in (True, False):
+            assert oracle.adam_step(t, scale, h, dt, *a, adamw=adamw) == 0
+            assert oracle.adam_step(t, scale, f, "f32", *b, adamw=adamw) == 0
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("bad", [0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001])
+def test_f32_overflow_step_changes_nothing(bad):
+    rng = np.random.default_rng(2)
+    n = 300
+    g = rng.normal(0, 1e-3, n).astype(np.float32).view(np.uint32).copy()
+    g[rng.integers(0, n)] = bad
+    p = rng.normal(0, 1, n).astype(np.float32)
+    m = rng.normal(0, 1e-3, n).astype(np.float32)
+    v = np.abs(rng.normal(0, 1e-6, n)).astype(np.float32)
+    keep = [x.copy() for x in (p, m, v)]
+    assert oracle.adam_step(5, 1.0, g, "f32", p, m, v) == 1
+    for x, y in zip((p, m, v), keep):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    g[g == bad] = 0x7F7FFFFF                       # the largest finite value does not skip
+    assert oracle.adam_step(5, 1.0, g, "f32", p, m, v) == 0

@@ -100,3 +100,20 @@ def test_nonfinite_exhaustive(dt):
         arr = np.zeros(1000, dtype=np.uint16)
         arr[999] = h
         assert oracle.nonfinite(arr, dt)
+
+
+def test_nonfinite_f32_sweep():
+    # every sign / exponent / top-7-fraction-bit pattern (the high half-word),
+    # each with low half-words 0, 1, 0x8000 and 0xFFFF, against numpy's isfinite
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    words = (hi[:, None] | np.array([0x0000, 0x0001, 0x8000, 0xFFFF], np.uint32)[None, :]).ravel()
+    bad = ~np.isfinite(words.view(np.float32))
+    got = np.array([oracle.nonfinite(words[i:i + 1], "f32") for i in range(words.size)])
+    assert np.array_equal(got, bad)
+    # largest finite values, the smallest subnormal and -0 do not trip; inf and NaN do
+    fin = np.array([0x7F7FFFFF, 0xFF7FFFFF, 0x00000001, 0x80000000], np.uint32)
+    assert not oracle.nonfinite(fin, "f32")
+    for w in (0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001):
+        arr = np.zeros(1000, dtype=np.uint32)
+        arr[999] = w
+        assert oracle.nonfinite(arr, "f32")

@@ -75,6 +75,15 @@ MUTATIONS = [
     ("parameters always cast to bf16",
      "param[begin + k - base] = oracle_float_to_half(master[k], pdt);",
      "param[begin + k - base] = oracle_float_to_half(master[k], OR_BF16);"),
+    ("fp32 exponent mask one bit short",
+     "return ((u >> 23) & 0xFFu) == 0xFFu;", "return ((u >> 23) & 0x7Fu) == 0x7Fu;"),
+    ("fp32 gradients read as halves",
+     "    if (gdt == OR_F32) {\n        uint32_t u;", "    if (0) {\n        uint32_t u;"),
+    ("fp32 gradient read at the wrong offset",
+     "memcpy(&u, (const unsigned char*)flat + 4 * k, 4);",
+     "memcpy(&u, (const unsigned char*)flat + 2 * k, 4);"),
+    ("fp32 flat padding not zeroed",
+     "for (int64_t k = real; k < S; ++k) flat[k] = 0u;", ""),
     ("parameter cast of the wrong master element",
      "param[begin + k - base] = oracle_float_to_half(master[k], pdt);",
      "param[begin + k - base] = oracle_float_to_half(master[real - 1 - k], pdt);"),

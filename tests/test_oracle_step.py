@@ -45,6 +45,34 @@ def test_flatten_brute_force(seed):
         assert np.array_equal(flat, exp)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_flatten_brute_force_f32(seed):
+    rng = np.random.default_rng(100 + seed)
+    pr = random.Random(seed)
+    numels = [pr.choice([0, 1, 5, 16, 33, 100]) for _ in range(pr.randint(1, 8))]
+    grads = [rng.normal(0, 1e-2, n).astype(np.float32).view(np.uint32) for n in numels]
+    R = pr.randint(1, 4)
+    A = pr.choice([1, 8])
+    for r in range(R):
+        p = oracle.plan(numels, R, r, A)
+        flat = oracle.flatten(p, grads)
+        assert flat.dtype == np.uint32
+        exp = np.full(p.S, 0xAAAAAAAA, np.uint32)
+        x = 0
+        for g in grads:
+            for j in range(g.size):
+                if p.begin <= x < p.begin + p.S:
+                    exp[x - p.begin] = g[j]
+                x += 1
+        exp[p.real:] = 0
+        assert np.array_equal(flat, exp)
+        # a rank of padding only: zeros of the right width with no arrays to tell it
+        pad = oracle.plan(numels, R, r, A)
+        if pad.real == 0:
+            assert np.array_equal(oracle.flatten(pad, [None] * len(numels), "f32"),
+                                  np.zeros(pad.S, np.uint32))
+
+
 def test_scale_trajectory_of_the_tiny_workload():
     # iterations 1..10, an overflow at iteration 4: the scale halves once and
     # the step counter skips it
