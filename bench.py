@@ -33,6 +33,17 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 ADAM_BYTES_PER_ELEM = 28      # read grad 2 + master/m/v 12; write master/m/v 12 + param 2
 FLATTEN_BYTES_PER_ELEM = 4    # read 2 + write 2
+GRAD_BYTES = {"f16": 2, "bf16": 2, "f32": 4}
+
+
+def adam_bytes(gdt: str) -> int:
+    """Algorithmic bytes per element of the fused update: the gradient, 12 B of
+    fp32 state read and written, the half parameter written."""
+    return ADAM_BYTES_PER_ELEM - 2 + GRAD_BYTES[gdt]
+
+
+def flatten_bytes(gdt: str) -> int:
+    return 2 * GRAD_BYTES[gdt]
 METRIC = "shard params/sec per Adam step + achieved HBM GB/s (% of peak), 1 GPU"
 
 
@@ -59,12 +70,13 @@ def setup(w, device):
 
     plan = z.zero_partition_plan(w.numels, w.world_size, w.rank, w.align, w.bucket_elems)
     S, real, begin = plan.S, plan.real, plan.begin
-    gdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.grad_dtype]
+    gdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[w.grad_dtype]
     pdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.param_dtype]
     segs = plan.segments()
     touched = sorted({s.tensor for s in segs})
     grad_elems = sum(w.numels[i] for i in touched)
-    need = S * (12 + 2) + real * 2 + grad_elems * 2 + (1 << 29)
+    gb = GRAD_BYTES[w.grad_dtype]
+    need = S * (12 + gb) + real * 2 + grad_elems * gb + (1 << 29)
     free, total = torch.cuda.mem_get_info(device)
     log(f"[bench] {w.name}: S={S} real={real} segments={len(segs)} buckets={plan.n_buckets} "
         f"device bytes needed ~{need / 1e9:.1f} GB, free {free / 1e9:.1f} GB")
@@ -238,7 +250,7 @@ def run_offload(w, steps, warmup, device, n_threads):
         out[f"lag{lag}"] = {"ms_per_step": wall * 1000.0 / steps, "host_update_ms": host_ms,
                             "value": real / (wall / steps),
                             "host_update_params_per_s": S / (host_ms * 1e-3),
-                            "host_update_gbps": ADAM_BYTES_PER_ELEM * S / (host_ms * 1e-3) / 1e9,
+                            "host_update_gbps": adam_bytes(w.grad_dtype) * S / (host_ms * 1e-3) / 1e9,
                             # per step: where the worker and the caller wait
                             "waits_ms": {k[:-len("_ms_total")]: (st[k] - s0[k]) / steps
                                          for k in ("wait_submit_ms_total",
@@ -303,7 +315,7 @@ def cpu_baseline_all_cores(w, plan_S, plan_begin, n_threads, target_s=8.0, windo
         i0 = plan_begin + t * n
         vals = synth.host_values(gkey, i0, n, w.grad_sigma, 1.0,
                                  synth.outlier_thresh(w.outlier_p), w.outlier_mult)
-        bufs.append((synth.half_bits(vals, w.grad_dtype),
+        bufs.append((synth.grad_bits(vals, w.grad_dtype),
                      synth.host_values(mkey, i0, n, w.master_sigma),
                      np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)))
     start = threading.Barrier(n_threads + 1)
@@ -352,7 +364,7 @@ def cpu_baseline(w, plan_S, plan_begin, target_s=12.0, window=1 << 24):
     gkey = synth.key(w.seed, synth.STREAM_GRAD, 1)
     vals = synth.host_values(gkey, plan_begin, n, w.grad_sigma, 1.0,
                              synth.outlier_thresh(w.outlier_p), w.outlier_mult)
-    gbits = synth.half_bits(vals, w.grad_dtype)
+    gbits = synth.grad_bits(vals, w.grad_dtype)
     master = synth.host_values(synth.key(w.seed, synth.STREAM_MASTER, 0), plan_begin, n,
                                w.master_sigma)
     mm = np.zeros(n, np.float32)
@@ -375,7 +387,7 @@ def cpu_baseline(w, plan_S, plan_begin, target_s=12.0, window=1 << 24):
             "sample": f"oracle (scalar C, 1 thread) flatten + overflow test + AdamW + "
                       f"{w.param_dtype} cast over the shard's first {n} elements "
                       f"(flat [{plan_begin}, {plan_begin + n})), {steps} steps, {el:.1f} s",
-            "gbps_equiv": rate * (ADAM_BYTES_PER_ELEM + FLATTEN_BYTES_PER_ELEM) / 1e9}
+            "gbps_equiv": rate * (adam_bytes(w.grad_dtype) + flatten_bytes(w.grad_dtype)) / 1e9}
 
 
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "adam_fused_llama2_70b_rank7_hbm_counters.md")
@@ -395,10 +407,11 @@ def kernels_digest(path=KERNELS_SRC):
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
-def counted_traffic(workload_name):
+def counted_traffic(workload_name, grad_dtype="bf16"):
     """HBM bytes per launch of the update kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (copy-calibrated), or None when that
-    summary is for another workload or the kernels have changed since."""
+    summary is for another workload or gradient dtype, or the kernels have
+    changed since."""
     import re
     try:
         text = open(COUNTERS_FILE).read()
@@ -406,7 +419,7 @@ def counted_traffic(workload_name):
     except OSError:
         return None
     vals = dict(re.findall(r"^(\w+) = (\S+)$", text, flags=re.M))
-    if vals.get("workload") != workload_name:
+    if vals.get("workload") != workload_name or vals.get("grad_dtype", "bf16") != grad_dtype:
         return None
     if vals.get("kernels_sha256") != digest:
         return None
@@ -431,6 +444,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama2_70b")
+    ap.add_argument("--grad-dtype", choices=["f16", "bf16", "f32"], default=None,
+                    help="override the workload's gradient dtype (f32: gradients kept in fp32, "
+                         "30 B/element in the update)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true",
@@ -460,8 +476,12 @@ def main(argv=None):
         copy_probe(args.copy_probe, 5, device)
         return 0
 
+    import dataclasses
+
     from synth.workloads import get
     w = get(args.workload)
+    if args.grad_dtype:
+        w = dataclasses.replace(w, grad_dtype=args.grad_dtype)
     if args.mode == "offload":
         threads = args.host_threads or max(1, host_info()["usable_cpus"] - 1)
         plan, res = run_offload(w, args.steps, args.warmup, device, threads)
@@ -483,9 +503,10 @@ def main(argv=None):
     ms_per_step = wall * 1000.0 / args.steps
     adam_ms = sum(times["adam"]) / len(times["adam"])
     flat_ms = sum(times["flatten"]) / len(times["flatten"])
-    adam_gbs = ADAM_BYTES_PER_ELEM * S / (adam_ms * 1e-3) / 1e9
-    flat_gbs = FLATTEN_BYTES_PER_ELEM * S / (flat_ms * 1e-3) / 1e9
-    step_gbs = (ADAM_BYTES_PER_ELEM + FLATTEN_BYTES_PER_ELEM) * S / (ms_per_step * 1e-3) / 1e9
+    ab, fb = adam_bytes(w.grad_dtype), flatten_bytes(w.grad_dtype)
+    adam_gbs = ab * S / (adam_ms * 1e-3) / 1e9
+    flat_gbs = fb * S / (flat_ms * 1e-3) / 1e9
+    step_gbs = (ab + fb) * S / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": real / (ms_per_step * 1e-3),
@@ -508,14 +529,15 @@ def main(argv=None):
         "kernels": {
             "adam_fused": {"avg_ms": adam_ms, "median_ms": statistics.median(times["adam"]),
                            "min_ms": min(times["adam"]),
-                           "bytes_per_elem": ADAM_BYTES_PER_ELEM, "gbps": adam_gbs,
+                           "bytes_per_elem": ab, "gbps": adam_gbs,
                            "params_per_s": S / (adam_ms * 1e-3)},
             "flatten": {"avg_ms": flat_ms, "median_ms": statistics.median(times["flatten"]),
                         "min_ms": min(times["flatten"]),
-                        "bytes_per_elem": FLATTEN_BYTES_PER_ELEM, "gbps": flat_gbs},
+                        "bytes_per_elem": fb, "gbps": flat_gbs},
             "write_param": {"ms": write_ms, "bytes_per_elem": 6,
                             "gbps": 6 * real / (write_ms * 1e-3) / 1e9},
-            "scan": {"ms": scan_ms, "bytes_per_elem": 2, "gbps": 2 * S / (scan_ms * 1e-3) / 1e9},
+            "scan": {"ms": scan_ms, "bytes_per_elem": GRAD_BYTES[w.grad_dtype],
+                     "gbps": GRAD_BYTES[w.grad_dtype] * S / (scan_ms * 1e-3) / 1e9},
         },
         "skipped_steps": state["skipped"],
         "graph_replay": None if graph_wall is None else {
@@ -525,7 +547,8 @@ def main(argv=None):
             "what": "flatten + zero_adam_step_async (device-resident t and loss scale) captured "
                     "once into a HIP graph, replayed per step; no host round trip"},
         "roofline": {"bound": "hbm", "achieved": adam_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": adam_gbs / HBM_PEAK_GBS, "traffic": counted_traffic(w.name)},
+                     "frac": adam_gbs / HBM_PEAK_GBS,
+                     "traffic": counted_traffic(w.name, w.grad_dtype)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

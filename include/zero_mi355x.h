@@ -11,7 +11,7 @@
  *
  * The step of rank r of R, per call:
  *   zero_partition_plan     flat partition + bucket plan (host only)
- *   zero_flatten_grads      half gradients -> the rank's flat gradient shard,
+ *   zero_flatten_grads      gradients -> the rank's flat gradient shard,
  *                           with the inf/NaN test fused into the copy
  *   zero_adam_step          unscale + Adam/AdamW + cast back to half, gated
  *                           on the overflow flag; returns the flag
@@ -49,6 +49,10 @@
  *            one flat index space [0, P).
  *   Dtypes   gradients and parameters are fp16 (ZERO_F16) or bf16
  *            (ZERO_BF16); master weights and both moments are fp32.
+ *            Gradients may also be kept in fp32 (ZERO_F32, e.g. an
+ *            accumulation buffer; the pages describe half gradients only):
+ *            they are flattened, tested and read as they are, 4 bytes per
+ *            element.  Parameters are always fp16 or bf16.
  */
 #ifndef ZERO_MI355X_H
 #define ZERO_MI355X_H
@@ -61,7 +65,7 @@ extern "C" {
 
 typedef struct zero_plan zero_plan_t; /* opaque, library owned */
 
-enum zero_dtype { ZERO_F16 = 1, ZERO_BF16 = 2 };
+enum zero_dtype { ZERO_F16 = 1, ZERO_BF16 = 2, ZERO_F32 = 3 /* gradients only */ };
 
 enum zero_status {
     ZERO_OK = 0,
@@ -157,7 +161,7 @@ int zero_plan_tensor_buckets(const zero_plan_t* plan, int32_t* out, int64_t cap)
 /* Releases the plan, its device block and pinned mirror (NULL is a no-op). */
 void zero_plan_destroy(zero_plan_t* plan);
 
-/* Bucketed flatten of half gradients into the rank's flat shard.
+/* Bucketed flatten of the gradients into the rank's flat shard.
  * [legal] ZeRO-2 bullet / [instr] ZeRO-2 mechanism: a rank keeps only the
  * gradients of its partition.  For every segment of `bucket` (0 <= bucket
  * < n_buckets) or of all buckets (bucket = -1):
@@ -167,9 +171,10 @@ void zero_plan_destroy(zero_plan_t* plan);
  * overflow flag ([legal] dynamic loss scaling bullet); the flag stays
  * raised until the next zero_adam_step consumes it.
  * grads: HOST array of n_tensors DEVICE pointers, each to tensor i's first
- * element, 2-byte aligned; entries of tensors without a segment in the
- * requested bucket(s) may be NULL.  flat_grad: device, >= S elements,
- * 16-byte aligned.  Async on `stream`.
+ * element, aligned to the element size (2 bytes; 4 for ZERO_F32); entries
+ * of tensors without a segment in the requested bucket(s) may be NULL.
+ * grad_dtype: ZERO_F16, ZERO_BF16 or ZERO_F32.  flat_grad: device, >= S
+ * elements of grad_dtype, 16-byte aligned.  Async on `stream`.
  * Errors: ZERO_ENULL, ZERO_EINVAL (bucket, dtype), ZERO_EALIGN, ZERO_EHIP,
  * ZERO_ESTATE (wrong device). */
 int zero_flatten_grads(zero_plan_t* plan, int32_t bucket, const void* const* grads,
@@ -186,15 +191,15 @@ int zero_flatten_grads(zero_plan_t* plan, int32_t bucket, const void* const* gra
  * is written and 1 is returned.  Otherwise, per shard element k < S, in
  * fp32 with one rounding per operation (scalars formed on the host in
  * double and rounded once):
- *   g = half(flat_grad[k]) * fp32(1/loss_scale)  [adamw=0: g += wd * p]
+ *   g = fp32(flat_grad[k]) * fp32(1/loss_scale)  [adamw=0: g += wd * p]
  *   m = b1*m + (1-b1)*g ;  v = b2*v + (1-b2)*(g*g)
  *   d = sqrt(v) * fp32(1/sqrt(1-b2^t)) + eps ;  u = m / d
  *   p = p * fp32(1 - lr*wd [adamw] or 1) - fp32(lr/(1-b1^t)) * u
  * and, if param != NULL, for k < real:
  *   param[shard_begin + k - param_base] = round_to_nearest_even_half(p)
  * step: the bias-correction step t >= 1 (count applied steps only).
- * loss_scale: finite, > 0.  flat_grad: device, >= S elements, 16-byte
- * aligned.  master/exp_avg/exp_avg_sq: device fp32 arrays of >= S
+ * loss_scale: finite, > 0.  flat_grad: device, >= S elements of grad_dtype
+ * (ZERO_F16, ZERO_BF16 or ZERO_F32), 16-byte aligned.  master/exp_avg/exp_avg_sq: device fp32 arrays of >= S
  * elements, 4-byte aligned (for full bandwidth: 256-byte aligned and in
  * separate allocations, as hipMalloc / torch give them -- on MI355X an array
  * starting 12 bytes past a 128-byte line ran the update at 57% of peak
@@ -291,8 +296,8 @@ int zero_adam_step_async(zero_plan_t* plan, const zero_adam_hparams_t* hp, const
 
 /* The update of zero_adam_step, run on the host over HOST buffers: same
  * scalars, same operation order, same rounding, so the result is bit for
- * bit that of the device update.  flat_grad: S half gradients (2-byte
- * aligned); master / exp_avg / exp_avg_sq: S floats each (4-byte aligned);
+ * bit that of the device update.  flat_grad: S gradients of grad_dtype
+ * (ZERO_F16 / ZERO_BF16 2-byte, ZERO_F32 4-byte aligned); master / exp_avg / exp_avg_sq: S floats each (4-byte aligned);
  * param (may be NULL): host buffer holding flat indices [param_base,
  * param_base + param_numel), which must contain the shard's real range.
  * overflow: 1 = skip (nothing written), 0 = apply, -1 = test flat_grad for
@@ -357,8 +362,9 @@ typedef struct {
  * and the scaler (zero_state_upload).  master / exp_avg / exp_avg_sq: HOST
  * fp32 arrays of S elements, owned by the caller and touched only by the
  * library's thread until zero_offload_drain returns.  param_dtype: 0 for no
- * parameter write-back.  Allocates two pinned gradient buffers (2 S bytes
- * each), two pinned parameter buffers (2 real bytes each), a transfer
+ * parameter write-back.  grad_dtype: ZERO_F16, ZERO_BF16 or ZERO_F32.
+ * Allocates two pinned gradient buffers (S elements of grad_dtype each),
+ * two pinned parameter buffers (2 real bytes each), a transfer
  * stream and a worker thread.  Errors: ZERO_ENULL, ZERO_EINVAL, ZERO_ESTATE,
  * ZERO_EHIP, ZERO_ENOMEM. */
 int zero_offload_create(zero_plan_t* plan, const zero_adam_hparams_t* hp, int32_t grad_dtype,

@@ -118,6 +118,14 @@ def half_bits(values: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def grad_bits(values: np.ndarray, dtype: str) -> np.ndarray:
+    """Gradient bits of fp32 values: fp16 / bf16 as half_bits, fp32 ("f32") as they are
+    (uint32)."""
+    if dtype == "f32":
+        return np.ascontiguousarray(values, dtype=np.float32).view(np.uint32).copy()
+    return half_bits(values, dtype)
+
+
 def dev_fill_f32(out, k: int, index0: int, sigma: float, scale: float = 1.0,
                  othresh: int = 0, omult: float = 1.0, stream=None) -> None:
     """Fill a contiguous float32 CUDA tensor with the values of flat indices index0 + j."""
@@ -134,8 +142,12 @@ def dev_fill_f32(out, k: int, index0: int, sigma: float, scale: float = 1.0,
 def dev_fill_half(out, k: int, index0: int, sigma: float, scale: float = 1.0,
                   othresh: int = 0, omult: float = 1.0, chunk: int = 1 << 27) -> None:
     """Fill a contiguous fp16/bf16 CUDA tensor: fp32 values from the device generator,
-    rounded by torch's conversion (RNE), in chunks to bound the fp32 scratch."""
+    rounded by torch's conversion (RNE), in chunks to bound the fp32 scratch.  A float32
+    tensor (fp32 gradients) takes the values as they are."""
     import torch
+    if out.dtype == torch.float32:           # fp32 gradients: no rounding step
+        dev_fill_f32(out.view(-1), k, index0, sigma, scale, othresh, omult)
+        return
     flat = out.view(-1)
     n = flat.numel()
     tmp = torch.empty(min(n, chunk), dtype=torch.float32, device=out.device)

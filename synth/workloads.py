@@ -33,7 +33,7 @@ class Workload:
     shapes: List[Tuple[int, ...]]
     world_size: int
     rank: int
-    grad_dtype: str            # "f16" | "bf16"
+    grad_dtype: str            # "f16" | "bf16" ("f32": gradients kept in fp32)
     param_dtype: str           # "f16" | "bf16"
     grad_sigma: float
     steps: int

@@ -21,7 +21,8 @@ import oracle
 import synth
 import zero_partitioned_mixed_plan_amd as z
 
-INF_BITS = {"f16": 0x7C00, "bf16": 0x7F80}
+INF_BITS = {"f16": 0x7C00, "bf16": 0x7F80, "f32": 0x7F800000}
+GRAD_WORD = {"f16": np.uint16, "bf16": np.uint16, "f32": np.uint32}
 
 
 def log(msg: str) -> None:
@@ -31,7 +32,22 @@ def log(msg: str) -> None:
 
 def torch_dtype(dt: str):
     import torch
-    return {"f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
+
+
+def to_device_grad(bits: np.ndarray, dt: str, dev):
+    """Gradient bits (uint16 for fp16 / bf16, uint32 for fp32) as a device tensor."""
+    import torch
+    signed = np.int32 if dt == "f32" else np.int16
+    return torch.from_numpy(bits.view(signed)).to(dev).view(torch_dtype(dt))
+
+
+def grad_bits_host(t, dt: str) -> np.ndarray:
+    """A device gradient tensor's bits on the host (uint16, or uint32 for fp32)."""
+    import torch
+    if dt == "f32":
+        return t.view(torch.int32).cpu().numpy().view(np.uint32)
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 def flat_offsets(numels: Sequence[int]) -> np.ndarray:
@@ -107,17 +123,17 @@ def host_grad_values(case: Case, it: int, flat0: int, n: int, scale: float) -> n
 
 
 def host_model_grads(case: Case, op, it: int, scale: float) -> List[Optional[np.ndarray]]:
-    """Per-tensor half gradient bits on the host for the tensors that touch the
+    """Per-tensor gradient bits on the host for the tensors that touch the
     shard (full-size tensors whose part outside the shard is zero; the others
     are None), with this iteration's +inf."""
     offs = flat_offsets(case.numels)
     out: List[Optional[np.ndarray]] = [None] * len(case.numels)
     for s in range(op.n_segments):
         i = int(op.seg_tensor[s])
-        g = np.zeros(case.numels[i], np.uint16)
+        g = np.zeros(case.numels[i], GRAD_WORD[case.grad_dtype])
         a, n = int(op.seg_tensor_off[s]), int(op.seg_numel[s])
         vals = host_grad_values(case, it, int(offs[i]) + a, n, scale)
-        g[a:a + n] = synth.half_bits(vals, case.grad_dtype)
+        g[a:a + n] = synth.grad_bits(vals, case.grad_dtype)
         out[i] = g
     pos = case.injection(it, op.real)
     if pos is not None:
@@ -246,9 +262,8 @@ class GpuRun:
     def step(self, it: int, grads_host: List[Optional[np.ndarray]]):
         import torch
         p, c = self.plan, self.case
-        gdt = torch_dtype(c.grad_dtype)
-        grads = [None if g is None else
-                 torch.from_numpy(g.view(np.int16)).to(self.dev).view(gdt) for g in grads_host]
+        grads = [None if g is None else to_device_grad(g, c.grad_dtype, self.dev)
+                 for g in grads_host]
         if c.flatten_mode == "all":
             z.zero_flatten_grads(p, -1, grads, self.flat)
         elif c.flatten_mode in ("buckets", "buckets_shuffled"):
@@ -291,7 +306,7 @@ class GpuRun:
         p = self.plan
         return (self.master.cpu().numpy(), self.m.cpu().numpy(), self.v.cpu().numpy(),
                 self.param_full.view(torch.int16).cpu().numpy().view(np.uint16),
-                self.flat[:p.S].view(torch.int16).cpu().numpy().view(np.uint16))
+                grad_bits_host(self.flat[:p.S], self.case.grad_dtype))
 
 
 def compare_full(case: Case, steps: Optional[int] = None, check_every: int = 1,

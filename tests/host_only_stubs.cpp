@@ -6,11 +6,11 @@
 
 namespace zmi {
 
-hipError_t launch_flatten(const FlatPiece*, int, uint16_t*, int*, int, hipStream_t) {
+hipError_t launch_flatten(const FlatPiece*, int, void*, int*, int, hipStream_t) {
     return hipErrorNoDevice;
 }
-hipError_t launch_scan(const uint16_t*, int64_t, int*, int, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_adam(const uint16_t*, float*, float*, float*, uint16_t*, int64_t, int64_t,
+hipError_t launch_scan(const void*, int64_t, int*, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_adam(const void*, float*, float*, float*, uint16_t*, int64_t, int64_t,
                        const int*, const AdamScalars&, const AdamScalars*, int, int, bool,
                        hipStream_t) {
     return hipErrorNoDevice;

@@ -147,6 +147,12 @@ def test_argument_errors_before_device_work():
                                   None) == _abi.ZERO_EALIGN
     assert lib.zero_flatten_grads(plan.handle, -1, ptrs, z.ZERO_BF16, fake + 2,
                                   None) == _abi.ZERO_EALIGN
+    # fp32 gradients: 4-byte sources
+    ptrs = (ctypes.c_void_p * 1)(fake + 2)
+    assert lib.zero_flatten_grads(plan.handle, -1, ptrs, z.ZERO_F32, fake,
+                                  None) == _abi.ZERO_EALIGN
+    assert lib.zero_flatten_grads(plan.handle, -1, ptrs, 4, fake, None) == _abi.ZERO_EINVAL
+    assert step(gdt=z.ZERO_F32, g=fake + 4) == _abi.ZERO_EALIGN
     bad = _abi.zero_scaler_t(0.0, 1.0, 0.5, 2.0, 10, 0, 1, 0)
     assert lib.zero_update_loss_scale(ctypes.byref(bad), 0) == _abi.ZERO_EINVAL
     assert lib.zero_update_loss_scale(None, 0) == _abi.ZERO_ENULL
@@ -163,7 +169,7 @@ def test_async_step_argument_errors_before_device_work():
     def step(g=fake, gdt=z.ZERO_BF16, m=fake, hpp=hp, param=None, base=0, numel=0, pdt=0):
         return lib.zero_adam_step_async(plan.handle, ctypes.byref(hpp), g, gdt, fake, m, fake,
                                         param, base, numel, pdt, None)
-    assert step(gdt=3) == _abi.ZERO_EINVAL
+    assert step(gdt=4) == _abi.ZERO_EINVAL
     assert step(g=None) == _abi.ZERO_ENULL
     assert step(g=fake + 4) == _abi.ZERO_EALIGN
     assert step(m=fake + 1) == _abi.ZERO_EALIGN

@@ -1,6 +1,6 @@
 """ZeRO-Offload's host-side update (zero_cpu_adam_step) against the oracle,
 on the CPU: every instruction-set path (forced with ZERO_CPU_ISA), several
-thread counts, fp16 and bf16, Adam-L2 and AdamW, padding, skipped steps and
+thread counts, fp16, bf16 and fp32 gradients, Adam-L2 and AdamW, padding, skipped steps and
 a sweep of fp32 patterns through the parameter cast.  Bar: bit-identical
 master / moments / parameters (the same arithmetic as the device update)."""
 import os
@@ -25,6 +25,8 @@ def isa(request, monkeypatch):
 
 def _grads(rng, n, dt, scale, sigma=1e-2):
     vals = (rng.normal(0, sigma, n) * scale).astype(np.float32)
+    if dt == "f32":
+        return vals
     if dt == "f16":
         return vals.astype(np.float16).view(np.uint16)
     import torch
@@ -32,7 +34,8 @@ def _grads(rng, n, dt, scale, sigma=1e-2):
 
 
 @pytest.mark.parametrize("gdt,pdt,adamw", [("f16", "f16", True), ("bf16", "bf16", True),
-                                           ("bf16", "f16", False), ("f16", "bf16", False)])
+                                           ("bf16", "f16", False), ("f16", "bf16", False),
+                                           ("f32", "bf16", True), ("f32", "f16", False)])
 @pytest.mark.parametrize("threads", [1, 3, 8])
 def test_host_update_equals_oracle(isa, gdt, pdt, adamw, threads):
     numels = [1000, 37, 5, 2049, 1]          # P = 3092; R = 3, A = 8 -> S = 1032, padding on rank 2
@@ -50,7 +53,7 @@ def test_host_update_equals_oracle(isa, gdt, pdt, adamw, threads):
         hp = z.AdamHParams(weight_decay=0.05, adamw=adamw)
         scale = 1024.0 if gdt == "f16" else 1.0
         for t in range(1, 5):
-            flat = np.zeros(S, np.uint16)
+            flat = np.zeros(S, np.float32 if gdt == "f32" else np.uint16)
             flat[:real] = _grads(rng, real, gdt, scale)
             o = oracle.adam_step(t, scale, flat, gdt, om, omo, ov, lr=hp.lr, b1=hp.beta1,
                                  b2=hp.beta2, eps=hp.eps, wd=hp.weight_decay, adamw=adamw)
@@ -85,6 +88,27 @@ def test_overflow_skips_and_leaves_state_untouched(isa):
                                 grad_dtype="f16", overflow=1) == 1
     assert z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, flat, master, z1, z2,
                                 grad_dtype="f16") == 0
+
+
+def test_f32_overflow_skips_and_leaves_state_untouched(isa):
+    n = 5001                                  # a masked / scalar tail on every path
+    plan = z.zero_partition_plan([n], 1, 0, 1)
+    rng = np.random.default_rng(2)
+    for bad in (0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001):
+        for pos in (0, 17, 4095, 4999, 5000):
+            flat = _grads(rng, n, "f32", 1.0).view(np.uint32).copy()
+            flat[pos] = bad
+            m0 = rng.normal(0, 0.02, n).astype(np.float32)
+            master, mo, v = m0.copy(), np.ones(n, np.float32), np.ones(n, np.float32)
+            param = np.zeros(n, np.uint16)
+            assert z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, flat.view(np.float32),
+                                        master, mo, v, param, grad_dtype="f32",
+                                        param_dtype="bf16", n_threads=3) == 1, (bad, pos)
+            assert np.array_equal(master, m0) and np.all(mo == 1) and np.all(v == 1)
+            assert not param.any()
+    flat = np.full(n, 0x7F7FFFFF, np.uint32).view(np.float32)   # largest finite: no skip
+    z0 = [np.zeros(n, np.float32) for _ in range(3)]
+    assert z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, flat, *z0) == 0
 
 
 @pytest.mark.parametrize("pdt", ["f16", "bf16"])

@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 
 import zero_partitioned_mixed_plan_amd as z
-from harness import Case, GpuRun, OracleRun, compare_full, compare_state, log, torch_dtype
+from harness import (Case, GpuRun, OracleRun, compare_full, compare_state, log, to_device_grad,
+                     torch_dtype)
 from synth.workloads import get
 
 pytestmark = pytest.mark.gpu
@@ -102,7 +103,7 @@ def _graph_run(case, label, check_every=1):
         assert before.scale == o_scale, f"{label} it={it}: scale {before.scale} vs {o_scale}"
         assert _device_double(scale_addr) == o_scale
         for i in touched:
-            grads_dev[i].copy_(torch.from_numpy(grads_host[i].view(np.int16)).view(gdt))
+            grads_dev[i].copy_(to_device_grad(grads_host[i], case.grad_dtype, gpu.dev))
         graph.replay()
         st = z.zero_state_download(p)
         assert st.last_flag == o_ovf, f"{label} it={it}: flag {st.last_flag} vs {o_ovf}"
@@ -126,6 +127,22 @@ def test_graph_replay_ragged_scaler_growth_and_backoff():
                 inject={2: 5, 3: 100000, 7: 1})
     worst = _graph_run(case, "ragged")
     assert worst["skipped"] == 3 and worst["bit_exact"]
+
+
+def test_graph_replay_fp32_gradients_dynamic_scale():
+    case = Case(numels=RAGGED, world_size=2, rank=1, grad_dtype="f32", param_dtype="bf16",
+                steps=8, dynamic=True, init_scale=512.0, window=2, grad_sigma=1e-2,
+                inject={2: 5, 5: 100000})
+    worst = _graph_run(case, "fp32 grads")
+    assert worst["skipped"] == 2 and worst["bit_exact"]
+
+
+def test_async_fp32_gradients():
+    case = Case(numels=RAGGED, world_size=3, rank=0, grad_dtype="f32", param_dtype="f16",
+                steps=5, dynamic=True, init_scale=1024.0, window=2, bucket_elems=50000,
+                inject={3: 77}, flatten_mode="buckets_shuffled")
+    worst = _run(case, "fp32 grads")
+    assert worst["skipped"] == 1 and worst["bit_exact"]
 
 
 def test_graph_replay_gpt2_small():

@@ -9,7 +9,7 @@ import pytest
 import oracle
 import synth
 import zero_partitioned_mixed_plan_amd as z
-from harness import Case, GpuRun, OracleRun, compare_full, log, torch_dtype
+from harness import Case, GpuRun, OracleRun, compare_full, log, to_device_grad, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -18,12 +18,14 @@ DEV = "cuda:0"
 
 def _bits(t):
     import torch
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).cpu().numpy().view(np.uint32)
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 def _to_dev_half(bits, dt):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch_dtype(dt))
+    """Gradient bits (uint16, or uint32 for "f32") as a device tensor."""
+    return to_device_grad(np.ascontiguousarray(bits), dt, DEV)
 
 
 def test_device_generator_matches_host_bit_for_bit():
@@ -43,10 +45,11 @@ def test_device_generator_matches_host_bit_for_bit():
             assert np.array_equal(_bits(dh), synth.half_bits(h, dt))
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_flatten_every_source_misalignment(dt):
     """Tensors are views at element offsets 0..7 of one buffer, so their
-    sources sit at every 2-byte misalignment of a 16-byte block."""
+    sources sit at every 2-byte misalignment of a 16-byte block (every
+    4-byte one for fp32 gradients)."""
     import torch
     rng = np.random.default_rng(3)
     numels = [5000, 4099, 2048, 3, 70000, 1, 2047, 9000, 4097, 12345, 600, 8191]
@@ -59,7 +62,7 @@ def test_flatten_every_source_misalignment(dt):
         for i, n in enumerate(numels):
             mis = i % 8
             off += mis
-            bits = synth.half_bits(rng.normal(0, 1e-2, n).astype(np.float32), dt)
+            bits = synth.grad_bits(rng.normal(0, 1e-2, n).astype(np.float32), dt)
             v = big[off:off + n]
             v.copy_(_to_dev_half(bits, dt))
             host.append(bits)
@@ -95,7 +98,7 @@ def _gate_case(dt, bad_pos, bad_bits, numels=(3000, 4099, 65, 70001, 2048), R=2,
     op = oracle.plan(numels, R, r, 8)
     plan = z.zero_partition_plan(numels, R, r, 8)
     rng = np.random.default_rng(11)
-    host = [synth.half_bits(rng.normal(0, 1e-2, n).astype(np.float32), dt) for n in numels]
+    host = [synth.grad_bits(rng.normal(0, 1e-2, n).astype(np.float32), dt) for n in numels]
     for pos in bad_pos:
         s = int(np.searchsorted(op.seg_shard_off, pos, side="right") - 1)
         host[int(op.seg_tensor[s])][int(op.seg_tensor_off[s] + pos - op.seg_shard_off[s])] = \
@@ -105,7 +108,7 @@ def _gate_case(dt, bad_pos, bad_bits, numels=(3000, 4099, 65, 70001, 2048), R=2,
     master = torch.randn(op.S, device=DEV) * 0.02
     m = torch.randn(op.S, device=DEV) * 1e-4
     v = torch.rand(op.S, device=DEV) * 1e-6
-    param = torch.zeros(op.P, dtype=torch_dtype(dt), device=DEV)
+    param = torch.zeros(op.P, dtype=torch_dtype("bf16" if dt == "f32" else dt), device=DEV)
     keep = [x.clone() for x in (master, m, v, param)]
     z.zero_flatten_grads(plan, -1, grads, flat)
     flag = z.zero_adam_step(plan, z.AdamHParams(), 3, 1024.0, flat, master, m, v, param, 0)
@@ -116,9 +119,10 @@ def _gate_case(dt, bad_pos, bad_bits, numels=(3000, 4099, 65, 70001, 2048), R=2,
     return flag, same, expect, op
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 def test_overflow_positions_and_skip_leaves_state_bit_identical(dt):
-    inf = {"f16": [0x7C00, 0xFC00, 0x7E00, 0x7C01], "bf16": [0x7F80, 0xFF80, 0x7FC0, 0x7F81]}[dt]
+    inf = {"f16": [0x7C00, 0xFC00, 0x7E00, 0x7C01], "bf16": [0x7F80, 0xFF80, 0x7FC0, 0x7F81],
+           "f32": [0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001]}[dt]
     op = oracle.plan([3000, 4099, 65, 70001, 2048], 2, 1, 8)
     edges = [0, op.real - 1] + op.seg_shard_off.tolist()[1:] + \
         [s - 1 for s in op.seg_shard_off.tolist()[1:]] + [2047, 2048, 4095, 12345]
@@ -128,7 +132,8 @@ def test_overflow_positions_and_skip_leaves_state_bit_identical(dt):
             assert expect == 1
             assert flag == 1 and same, (hex(bits), pos)
     # largest finite values, subnormals and -0 never trip
-    fin = {"f16": [0x7BFF, 0xFBFF, 0x0001, 0x8000], "bf16": [0x7F7F, 0xFF7F, 0x0001, 0x8000]}[dt]
+    fin = {"f16": [0x7BFF, 0xFBFF, 0x0001, 0x8000], "bf16": [0x7F7F, 0xFF7F, 0x0001, 0x8000],
+           "f32": [0x7F7FFFFF, 0xFF7FFFFF, 0x00000001, 0x80000000]}[dt]
     for bits in fin:
         flag, same, expect, _ = _gate_case(dt, [0, 17, op.real - 1], bits)
         assert expect == 0 and flag == 0 and not same
@@ -304,7 +309,7 @@ def test_write_param_ragged_sizes_and_windows(pdt):
             assert np.array_equal(got, want), (numels, R, r, base)
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 def test_partial_flatten_makes_the_step_scan(dt):
     """Only some buckets are flattened; the rest of the flat shard is filled
     another way (as a reduce-scatter would).  The step must test the whole
@@ -316,7 +321,7 @@ def test_partial_flatten_makes_the_step_scan(dt):
     plan = z.zero_partition_plan(numels, 2, 0, 8, 20000)
     assert plan.n_buckets >= 3
     rng = np.random.default_rng(5)
-    host = [synth.half_bits(rng.normal(0, 1e-2, n).astype(np.float32), dt) for n in numels]
+    host = [synth.grad_bits(rng.normal(0, 1e-2, n).astype(np.float32), dt) for n in numels]
     expect_flat = oracle.flatten(op, host)
     tb = plan.tensor_buckets()
     segs = plan.segments()
@@ -332,7 +337,7 @@ def test_partial_flatten_makes_the_step_scan(dt):
                                                for i, g in enumerate(grads)], flat)
         part = expect_flat[lo:hi].copy()
         if plant:
-            part[(hi - lo) // 2] = 0x7C00 if dt == "f16" else 0x7F80
+            part[(hi - lo) // 2] = {"f16": 0x7C00, "bf16": 0x7F80, "f32": 0x7F800000}[dt]
         flat[lo:hi].copy_(_to_dev_half(part, dt))
         m0 = rng.normal(0, 0.02, op.S).astype(np.float32)
         master = torch.from_numpy(m0.copy()).to(DEV)

@@ -15,7 +15,7 @@ import pytest
 
 import zero_partitioned_mixed_plan_amd as z
 from harness import Case, OracleRun, host_model_grads, init_master_host, init_param_host, log, \
-    torch_dtype
+    to_device_grad, torch_dtype
 from synth.workloads import get
 
 pytestmark = pytest.mark.gpu
@@ -57,7 +57,7 @@ def _offload_run(case, lag, label, write_params=True, n_threads=4):
         st = z.zero_state_download(plan)
         o_ovf, grads, o_scale = orc.step(it)
         assert st.scale == o_scale, f"{label} it={it}: device scale {st.scale} vs {o_scale}"
-        grads_dev = [None if g is None else torch.from_numpy(g.view(np.int16)).to(dev).view(gdt)
+        grads_dev = [None if g is None else to_device_grad(g, case.grad_dtype, dev)
                      for g in grads]
         z.zero_flatten_grads(plan, -1, grads_dev, flat)
         off.submit(flat, param if write_params else None, 0)
@@ -108,6 +108,14 @@ def test_offload_bf16_padding_rank_and_no_param_write():
                 steps=4, grad_sigma=1e-2, adamw=False, weight_decay=0.1)
     _offload_run(case, 1, "bf16 adam-l2")
     _offload_run(case, 1, "bf16 no param write", write_params=False)
+
+
+@pytest.mark.parametrize("lag", [1, 0])
+def test_offload_fp32_gradients(lag):
+    case = Case(numels=RAGGED, world_size=2, rank=0, grad_dtype="f32", param_dtype="bf16",
+                steps=6, dynamic=True, init_scale=512.0, window=2, grad_sigma=1e-2,
+                inject={3: 4097})
+    assert _offload_run(case, lag, f"fp32 grads lag={lag}") == 1
 
 
 def test_offload_gpt2_small():

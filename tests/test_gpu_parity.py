@@ -88,6 +88,26 @@ def test_dynamic_scale_growth_and_backoff():
     assert worst["skipped"] == 3 and worst["bit_exact"]
 
 
+@pytest.mark.parametrize("align", [1, 64])
+@pytest.mark.parametrize("pdt", ["bf16", "f16"])
+def test_fp32_gradients_every_rank(align, pdt):
+    """Gradients kept in fp32 (4-byte flatten, binary32 overflow test, no
+    conversion in the update), with a dynamic scale: every flatten mode."""
+    for r, mode in enumerate(["all", "buckets_shuffled", "scan"]):
+        case = Case(numels=RAGGED, world_size=3, rank=r, grad_dtype="f32", param_dtype=pdt,
+                    steps=5, align=align, bucket_elems=50000, grad_sigma=1e-2, dynamic=True,
+                    init_scale=1024.0, window=2, inject={2: 1234, 4: 50001},
+                    flatten_mode=mode, param_mode="window" if r == 2 else "full")
+        worst = _run(case, f"fp32 grads A={align} {pdt} r={r} {mode}")
+        assert worst["skipped"] == 2 and worst["bit_exact"]
+
+
+def test_fp32_gradients_gpt2_small():
+    case = Case.from_workload(get("gpt2_small"), grad_dtype="f32", steps=6)
+    worst = _run(case, "gpt2_small fp32 grads", check_every=3)
+    assert worst["bit_exact"]
+
+
 def test_gpt2_small_full_shard_all_steps():
     w = get("gpt2_small")
     case = Case.from_workload(w)

@@ -40,14 +40,14 @@ from dataclasses import dataclass
 from typing import List, Optional, Sequence
 
 from . import _abi
-from ._abi import ZERO_BF16, ZERO_F16, ZeroError, check, lib  # noqa: F401
+from ._abi import ZERO_BF16, ZERO_F16, ZERO_F32, ZeroError, check, lib  # noqa: F401
 
 __all__ = ["Plan", "AdamHParams", "LossScaler", "DeviceStepState", "ZeroError",
            "zero_partition_plan", "GradList", "zero_flatten_grads", "zero_adam_step",
            "zero_update_loss_scale", "zero_write_param_shard", "zero_state_upload",
            "zero_adam_step_async", "zero_state_download", "zero_state_device_scale",
            "zero_cpu_adam_step", "zero_cpu_isa", "Offload", "zero_last_error", "ZERO_F16",
-           "ZERO_BF16"]
+           "ZERO_BF16", "ZERO_F32"]
 
 
 def _torch():
@@ -61,7 +61,14 @@ def _dtype_code(t) -> int:
         return ZERO_F16
     if t.dtype == torch.bfloat16:
         return ZERO_BF16
-    raise TypeError(f"expected a float16 or bfloat16 tensor, got {t.dtype}")
+    if t.dtype == torch.float32:
+        return ZERO_F32
+    raise TypeError(f"expected a float16, bfloat16 or float32 tensor, got {t.dtype}")
+
+
+def _grad_dtypes():
+    torch = _torch()
+    return (torch.float16, torch.bfloat16, torch.float32)
 
 
 def _stream_handle(stream, device) -> Optional[int]:
@@ -203,7 +210,7 @@ class GradList:
             if g is None:
                 continue
             _require(g, f"grads[{i}]", int(numels[i]),
-                     (self.dtype,) if self.dtype is not None else (torch.float16, torch.bfloat16))
+                     (self.dtype,) if self.dtype is not None else _grad_dtypes())
             self.dtype = g.dtype
             self.ptrs[i] = g.data_ptr()
         self._tensors = list(grads)
@@ -214,7 +221,7 @@ def zero_flatten_grads(plan: Plan, bucket: int, grads, flat_grad, stream=None) -
     tensor without elements in the requested buckets of this shard), or a GradList
     bound to this plan."""
     torch = _torch()
-    _require(flat_grad, "flat_grad", plan.S, (torch.float16, torch.bfloat16))
+    _require(flat_grad, "flat_grad", plan.S, _grad_dtypes())
     if isinstance(grads, GradList):
         if grads.plan is not plan:
             raise ValueError("the GradList is bound to another plan")
@@ -251,7 +258,7 @@ def zero_adam_step(plan: Plan, hparams: AdamHParams, step: int, loss_scale: floa
                    stream=None) -> int:
     """Returns 0 when the update was applied, 1 when an overflow skipped it."""
     torch = _torch()
-    _require(flat_grad, "flat_grad", plan.S, (torch.float16, torch.bfloat16))
+    _require(flat_grad, "flat_grad", plan.S, _grad_dtypes())
     for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
         _require(t, name, plan.S, (torch.float32,))
     pptr, pnum, pdt = None, 0, 0
@@ -329,7 +336,7 @@ def zero_adam_step_async(plan: Plan, hparams: AdamHParams, flat_grad, master, ex
     """Enqueue the gated update and the loss-scale policy on the device state;
     returns at once (nothing waits, nothing is allocated)."""
     torch = _torch()
-    _require(flat_grad, "flat_grad", plan.S, (torch.float16, torch.bfloat16))
+    _require(flat_grad, "flat_grad", plan.S, _grad_dtypes())
     for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
         _require(t, name, plan.S, (torch.float32,))
     pptr, pnum, pdt = None, 0, 0
@@ -346,6 +353,7 @@ def zero_adam_step_async(plan: Plan, hparams: AdamHParams, flat_grad, master, ex
 
 
 _HALF_CODES = {"f16": ZERO_F16, "bf16": ZERO_BF16, ZERO_F16: ZERO_F16, ZERO_BF16: ZERO_BF16}
+_GRAD_CODES = {**_HALF_CODES, "f32": ZERO_F32, ZERO_F32: ZERO_F32}
 
 
 def _host_buffer(x, name: str, min_numel: int, itemsize: int):
@@ -375,7 +383,19 @@ def _half_code(x, given):
     torch = _torch()
     if isinstance(x, torch.Tensor) and x.dtype in (torch.float16, torch.bfloat16):
         return _dtype_code(x)
-    raise TypeError("pass grad_dtype / param_dtype ('f16' or 'bf16') for raw 16-bit buffers")
+    raise TypeError("pass param_dtype ('f16' or 'bf16') for raw 16-bit buffers")
+
+
+def _grad_code(x, given):
+    if given is not None:
+        return _GRAD_CODES[given]
+    torch = _torch()
+    if isinstance(x, torch.Tensor) and x.dtype in _grad_dtypes():
+        return _dtype_code(x)
+    import numpy as np
+    if isinstance(x, np.ndarray) and x.dtype == np.float32:
+        return ZERO_F32
+    raise TypeError("pass grad_dtype ('f16', 'bf16' or 'f32') for raw gradient buffers")
 
 
 def zero_cpu_adam_step(plan: Plan, hparams: AdamHParams, step: int, loss_scale: float, flat_grad,
@@ -385,7 +405,8 @@ def zero_cpu_adam_step(plan: Plan, hparams: AdamHParams, step: int, loss_scale: 
     """ZeRO-Offload's update on host buffers; returns 0 applied, 1 skipped.
     overflow: -1 tests flat_grad here, 0 / 1 pass a known flag."""
     import os
-    g, _ = _host_buffer(flat_grad, "flat_grad", plan.S, 2)
+    gcode = _grad_code(flat_grad, grad_dtype)
+    g, _ = _host_buffer(flat_grad, "flat_grad", plan.S, 4 if gcode == ZERO_F32 else 2)
     ptrs = [_host_buffer(t, name, plan.S, 4)[0] for name, t in
             (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq))]
     pptr, pnum, pdt = None, 0, 0
@@ -396,7 +417,7 @@ def zero_cpu_adam_step(plan: Plan, hparams: AdamHParams, step: int, loss_scale: 
         n_threads = max(1, min(16, os.cpu_count() or 1))
     hp = hparams.to_c()
     return check(lib.zero_cpu_adam_step(plan.handle, ctypes.byref(hp), int(step),
-                                        float(loss_scale), g, _half_code(flat_grad, grad_dtype),
+                                        float(loss_scale), g, gcode,
                                         *ptrs, pptr, int(param_base), pnum, pdt, int(overflow),
                                         int(n_threads)), "zero_cpu_adam_step")
 
@@ -424,7 +445,7 @@ class Offload:
         pdt = 0 if param_dtype is None else _HALF_CODES[param_dtype]
         hp = hparams.to_c()
         h = ctypes.c_void_p()
-        check(lib.zero_offload_create(plan.handle, ctypes.byref(hp), _HALF_CODES[grad_dtype], pdt,
+        check(lib.zero_offload_create(plan.handle, ctypes.byref(hp), _GRAD_CODES[grad_dtype], pdt,
                                       *ptrs, int(n_threads), ctypes.byref(h)),
               "zero_offload_create")
         self._h = h
@@ -435,7 +456,7 @@ class Offload:
 
     def submit(self, flat_grad, param=None, param_base: int = 0, stream=None) -> None:
         torch = _torch()
-        _require(flat_grad, "flat_grad", self.plan.S, (torch.float16, torch.bfloat16))
+        _require(flat_grad, "flat_grad", self.plan.S, _grad_dtypes())
         pptr, pnum = None, 0
         if param is not None:
             _require(param, "param", 0, (torch.float16, torch.bfloat16))

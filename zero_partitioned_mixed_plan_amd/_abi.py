@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzero_mi3
 
 ZERO_F16 = 1
 ZERO_BF16 = 2
+ZERO_F32 = 3   # gradients only
 
 ZERO_OK = 0
 ZERO_EINVAL = -1

@@ -45,6 +45,12 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 bool valid_dtype(int32_t d) { return d == ZERO_F16 || d == ZERO_BF16; }
 
+bool valid_grad_dtype(int32_t d) { return valid_dtype(d) || d == ZERO_F32; }
+
+int bad_grad_dtype() {
+    return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16, ZERO_BF16 or ZERO_F32");
+}
+
 // Binds the plan to the current device on first use and creates its flag.
 int ensure_device(zero_plan* p) {
     int dev = -1;
@@ -142,7 +148,7 @@ int check_scaler(const zero_scaler_t* sc) {
 // Checks shared by the synchronous and asynchronous steps.
 int check_step_buffers(const zero_plan* p, const void* flat_grad, int32_t grad_dtype,
                        const float* master, const float* exp_avg, const float* exp_avg_sq) {
-    if (!valid_dtype(grad_dtype)) return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16");
+    if (!valid_grad_dtype(grad_dtype)) return bad_grad_dtype();
     if (p->S > 0 && (flat_grad == nullptr || master == nullptr || exp_avg == nullptr ||
                      exp_avg_sq == nullptr)) {
         return fail(ZERO_ENULL, "flat_grad, master, exp_avg and exp_avg_sq must be non-NULL");
@@ -267,7 +273,7 @@ void zero_plan_destroy(zero_plan_t* p) {
 int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
                        int32_t grad_dtype, void* flat_grad, void* stream) {
     if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");
-    if (!valid_dtype(grad_dtype)) return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16");
+    if (!valid_grad_dtype(grad_dtype)) return bad_grad_dtype();
     if (bucket < -1 || bucket >= p->n_buckets) {
         return fail(ZERO_EINVAL, "bucket must be -1 or in [0, n_buckets)");
     }
@@ -280,6 +286,7 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
     }
     if (s_last > s_first && grads == nullptr) return fail(ZERO_ENULL, "grads is NULL");
     // pieces of this call: the bucket's segments, then the padding tail
+    const uintptr_t esize = static_cast<uintptr_t>(grad_bytes(grad_dtype));
     std::vector<FlatPiece> pieces;
     pieces.reserve(static_cast<size_t>(s_last - s_first) + 1);
     for (int64_t s = s_first; s < s_last; ++s) {
@@ -289,13 +296,14 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
             return fail(ZERO_ENULL, "grads[" + std::to_string(g.tensor) +
                                         "] is NULL but the tensor has elements in this shard");
         }
-        if ((reinterpret_cast<uintptr_t>(src) & 1u) != 0) {
-            return fail(ZERO_EALIGN, "grads[" + std::to_string(g.tensor) + "] is not 2-byte aligned");
+        if ((reinterpret_cast<uintptr_t>(src) & (esize - 1u)) != 0) {
+            return fail(ZERO_EALIGN, "grads[" + std::to_string(g.tensor) + "] is not " +
+                                         std::to_string(esize) + "-byte aligned");
         }
         // byte address of the source of flat element 0 (mod 2^64)
         const uintptr_t base = reinterpret_cast<uintptr_t>(src) +
-                               2u * static_cast<uintptr_t>(g.tensor_off) -
-                               2u * static_cast<uintptr_t>(g.shard_off);
+                               esize * static_cast<uintptr_t>(g.tensor_off) -
+                               esize * static_cast<uintptr_t>(g.shard_off);
         pieces.push_back(FlatPiece{g.shard_off, g.shard_off + g.numel, base});
     }
     if (p->S > p->real) pieces.push_back(FlatPiece{p->real, p->S, 0});
@@ -311,9 +319,8 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
                pieces[j].begin == pieces[j - 1].end) {
             ++j;
         }
-        hipError_t e = launch_flatten(pieces.data() + i, static_cast<int>(j - i),
-                                      static_cast<uint16_t*>(flat_grad), p->dev.d_flag,
-                                      grad_dtype, s);
+        hipError_t e = launch_flatten(pieces.data() + i, static_cast<int>(j - i), flat_grad,
+                                      p->dev.d_flag, grad_dtype, s);
         if (e != hipSuccess) return hip_fail(e, "flatten launch");
         i = j;
     }
@@ -338,7 +345,7 @@ int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, 
                    float* exp_avg_sq, void* param, int64_t param_base, int64_t param_numel,
                    int32_t param_dtype, void* stream) {
     if (p == nullptr || hp == nullptr) return fail(ZERO_ENULL, "plan or hparams is NULL");
-    if (!valid_dtype(grad_dtype)) return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16");
+    if (!valid_grad_dtype(grad_dtype)) return bad_grad_dtype();
     if (step < 1) return fail(ZERO_EINVAL, "step must be >= 1");
     if (!(std::isfinite(loss_scale) && loss_scale > 0)) {
         return fail(ZERO_EINVAL, "loss_scale must be finite and > 0");
@@ -361,13 +368,13 @@ int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, 
     // the gate needs every real gradient of this flat buffer tested
     if (!flatten_covered(p, flat_grad, grad_dtype)) {
         if ((rc = timer_start(p, kTimerScan, s)) != ZERO_OK) return rc;
-        hipError_t e = launch_scan(static_cast<const uint16_t*>(flat_grad), p->S, p->dev.d_flag,
+        hipError_t e = launch_scan(flat_grad, p->S, p->dev.d_flag,
                                    grad_dtype, s);
         if (e != hipSuccess) return hip_fail(e, "scan launch");
         if ((rc = timer_stop(p, kTimerScan, s)) != ZERO_OK) return rc;
     }
     if ((rc = timer_start(p, kTimerAdam, s)) != ZERO_OK) return rc;
-    hipError_t e = launch_adam(static_cast<const uint16_t*>(flat_grad), master, exp_avg,
+    hipError_t e = launch_adam(flat_grad, master, exp_avg,
                                exp_avg_sq, param0, p->S, p->real, p->dev.d_flag, sc, nullptr,
                                grad_dtype, param_dtype, hp->adamw != 0, s);
     if (e != hipSuccess) return hip_fail(e, "adam launch");
@@ -479,7 +486,7 @@ int zero_adam_step_async(zero_plan_t* p, const zero_adam_hparams_t* hp, const vo
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!flatten_covered(p, flat_grad, grad_dtype)) {
         if ((rc = timer_start(p, kTimerScan, s)) != ZERO_OK) return rc;
-        hipError_t e = launch_scan(static_cast<const uint16_t*>(flat_grad), p->S, p->dev.d_flag,
+        hipError_t e = launch_scan(flat_grad, p->S, p->dev.d_flag,
                                    grad_dtype, s);
         if (e != hipSuccess) return hip_fail(e, "scan launch");
         if ((rc = timer_stop(p, kTimerScan, s)) != ZERO_OK) return rc;
@@ -488,7 +495,7 @@ int zero_adam_step_async(zero_plan_t* p, const zero_adam_hparams_t* hp, const vo
     if (e != hipSuccess) return hip_fail(e, "step prologue launch");
     if ((rc = timer_start(p, kTimerAdam, s)) != ZERO_OK) return rc;
     const AdamScalars unused{};
-    e = launch_adam(static_cast<const uint16_t*>(flat_grad), master, exp_avg, exp_avg_sq, param0,
+    e = launch_adam(flat_grad, master, exp_avg, exp_avg_sq, param0,
                     p->S, p->real, p->dev.d_flag, unused, device_scalars(p), grad_dtype,
                     param_dtype, hp->adamw != 0, s);
     if (e != hipSuccess) return hip_fail(e, "adam launch");
@@ -540,7 +547,7 @@ int zero_cpu_adam_step(const zero_plan_t* p, const zero_adam_hparams_t* hp, int6
                        int64_t param_base, int64_t param_numel, int32_t param_dtype,
                        int32_t overflow, int32_t n_threads) {
     if (p == nullptr || hp == nullptr) return fail(ZERO_ENULL, "plan or hparams is NULL");
-    if (!valid_dtype(grad_dtype)) return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16");
+    if (!valid_grad_dtype(grad_dtype)) return bad_grad_dtype();
     if (step < 1) return fail(ZERO_EINVAL, "step must be >= 1");
     if (!(std::isfinite(loss_scale) && loss_scale > 0)) {
         return fail(ZERO_EINVAL, "loss_scale must be finite and > 0");
@@ -553,14 +560,15 @@ int zero_cpu_adam_step(const zero_plan_t* p, const zero_adam_hparams_t* hp, int6
                      exp_avg_sq == nullptr)) {
         return fail(ZERO_ENULL, "flat_grad, master, exp_avg and exp_avg_sq must be non-NULL");
     }
-    if ((reinterpret_cast<uintptr_t>(flat_grad) & 1u) != 0 || !aligned4(master) ||
-        !aligned4(exp_avg) || !aligned4(exp_avg_sq)) {
-        return fail(ZERO_EALIGN, "flat_grad must be 2-byte and the fp32 arrays 4-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(flat_grad) & (grad_bytes(grad_dtype) - 1u)) != 0 ||
+        !aligned4(master) || !aligned4(exp_avg) || !aligned4(exp_avg_sq)) {
+        return fail(ZERO_EALIGN,
+                    "flat_grad must be aligned to its element size and the fp32 arrays to 4 bytes");
     }
     uint16_t* param0 = nullptr;
     rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
     if (rc != ZERO_OK) return rc;
-    const uint16_t* g = static_cast<const uint16_t*>(flat_grad);
+    const void* g = flat_grad;
     const bool skip = overflow < 0 ? cpu_nonfinite(g, p->S, grad_dtype, n_threads) : overflow != 0;
     if (skip) return 1;
     CpuAdamArgs a;

@@ -38,6 +38,7 @@ namespace {
 
 constexpr uint32_t kF16ExpMask = 0x7C00u;
 constexpr uint32_t kBf16ExpMask = 0x7F80u;
+constexpr uint32_t kF32ExpMask = 0x7F800000u;
 
 // ------------------------------------------------------------ scalar path
 // binary16 -> binary32, exact (integer decode).
@@ -106,11 +107,23 @@ float bf16_bits_to_f32(uint32_t h) {
     return x;
 }
 
+// Gradient k as fp32: fp32 gradients as they are, half ones converted.
+template <int GDT>
+float grad_at(const void* g, int64_t k) {
+    if (GDT == ZERO_F32) {
+        float x;
+        std::memcpy(&x, static_cast<const char*>(g) + 4 * k, 4);
+        return x;
+    }
+    const uint16_t h = static_cast<const uint16_t*>(g)[k];
+    return GDT == ZERO_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+}
+
 template <int GDT, int PDT, bool ADAMW>
 void adam_scalar(const CpuAdamArgs& a, int64_t lo, int64_t hi) {
     const AdamScalars& c = a.sc;
     for (int64_t k = lo; k < hi; ++k) {
-        const float g = GDT == ZERO_F16 ? f16_bits_to_f32(a.g[k]) : bf16_bits_to_f32(a.g[k]);
+        const float g = grad_at<GDT>(a.g, k);
         float p = a.p[k];
         float gu = g * c.inv_scale;
         if (!ADAMW) gu = gu + c.wd * p;
@@ -128,9 +141,17 @@ void adam_scalar(const CpuAdamArgs& a, int64_t lo, int64_t hi) {
     }
 }
 
-bool nonfinite_scalar(const uint16_t* g, int64_t lo, int64_t hi, uint32_t mask) {
+// Exponent field all ones (mask: the field of the gradient format; 4-byte
+// elements when f32).
+bool nonfinite_scalar(const void* g, int64_t lo, int64_t hi, uint32_t mask, bool f32) {
     uint32_t any = 0;
-    for (int64_t k = lo; k < hi; ++k) any |= (g[k] & mask) == mask;
+    if (f32) {
+        const uint32_t* w = static_cast<const uint32_t*>(g);
+        for (int64_t k = lo; k < hi; ++k) any |= (w[k] & mask) == mask;
+    } else {
+        const uint16_t* h = static_cast<const uint16_t*>(g);
+        for (int64_t k = lo; k < hi; ++k) any |= (h[k] & mask) == mask;
+    }
     return any != 0;
 }
 
@@ -154,14 +175,18 @@ ZMI_AVX2 inline __m128i narrow16_avx2(__m256i x) {
 }
 
 template <int GDT, int PDT, bool ADAMW>
-ZMI_AVX2 void adam_block_avx2(const uint16_t* g, float* pp, float* mp, float* vp, uint16_t* par,
+ZMI_AVX2 void adam_block_avx2(const void* g, float* pp, float* mp, float* vp, uint16_t* par,
                               int n_param, const AdamScalars& c) {
-    const __m128i h = _mm_loadu_si128(reinterpret_cast<const __m128i*>(g));
     __m256 gf;
-    if (GDT == ZERO_F16) {
-        gf = _mm256_cvtph_ps(h);
+    if (GDT == ZERO_F32) {
+        gf = _mm256_loadu_ps(static_cast<const float*>(g));
     } else {
-        gf = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(h), 16));
+        const __m128i h = _mm_loadu_si128(static_cast<const __m128i*>(g));
+        if (GDT == ZERO_F16) {
+            gf = _mm256_cvtph_ps(h);
+        } else {
+            gf = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(h), 16));
+        }
     }
     __m256 p = _mm256_loadu_ps(pp);
     __m256 gu = _mm256_mul_ps(gf, _mm256_set1_ps(c.inv_scale));
@@ -199,19 +224,21 @@ ZMI_AVX2 void adam_block_avx2(const uint16_t* g, float* pp, float* mp, float* vp
 
 template <int GDT, int PDT, bool ADAMW>
 ZMI_AVX2 void adam_avx2(const CpuAdamArgs& a, int64_t lo, int64_t hi) {
+    constexpr int64_t esize = GDT == ZERO_F32 ? 4 : 2;
+    const char* g0 = static_cast<const char*>(a.g);
     int64_t k = lo;
     for (; k + 8 <= hi; k += 8) {
         const int64_t np = std::min<int64_t>(8, std::max<int64_t>(0, a.real - k));
-        adam_block_avx2<GDT, PDT, ADAMW>(a.g + k, a.p + k, a.m + k, a.v + k,
+        adam_block_avx2<GDT, PDT, ADAMW>(g0 + k * esize, a.p + k, a.m + k, a.v + k,
                                          a.param ? a.param + k : nullptr, static_cast<int>(np),
                                          a.sc);
     }
     if (k < hi) {  // tail: through zero-padded copies
         const int n = static_cast<int>(hi - k);
-        alignas(32) uint16_t g[8] = {0};
+        alignas(32) unsigned char g[32] = {0};
         alignas(32) float p[8] = {0}, m[8] = {0}, v[8] = {0};
         alignas(32) uint16_t par[8];
-        std::memcpy(g, a.g + k, n * 2);
+        std::memcpy(g, g0 + k * esize, static_cast<size_t>(n * esize));
         std::memcpy(p, a.p + k, n * 4);
         std::memcpy(m, a.m + k, n * 4);
         std::memcpy(v, a.v + k, n * 4);
@@ -225,15 +252,25 @@ ZMI_AVX2 void adam_avx2(const CpuAdamArgs& a, int64_t lo, int64_t hi) {
     _mm_sfence();  // streaming stores visible before the caller hands the buffer on
 }
 
-ZMI_AVX2 bool nonfinite_avx2(const uint16_t* g, int64_t lo, int64_t hi, uint32_t mask) {
-    const __m256i mk = _mm256_set1_epi16(static_cast<short>(mask));
+ZMI_AVX2 bool nonfinite_avx2(const void* g, int64_t lo, int64_t hi, uint32_t mask, bool f32) {
     __m256i acc = _mm256_setzero_si256();
     int64_t k = lo;
-    for (; k + 16 <= hi; k += 16) {
-        const __m256i x = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(g + k));
-        acc = _mm256_or_si256(acc, _mm256_cmpeq_epi16(_mm256_and_si256(x, mk), mk));
+    if (f32) {
+        const uint32_t* w = static_cast<const uint32_t*>(g);
+        const __m256i mk = _mm256_set1_epi32(static_cast<int>(mask));
+        for (; k + 8 <= hi; k += 8) {
+            const __m256i x = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(w + k));
+            acc = _mm256_or_si256(acc, _mm256_cmpeq_epi32(_mm256_and_si256(x, mk), mk));
+        }
+    } else {
+        const uint16_t* h = static_cast<const uint16_t*>(g);
+        const __m256i mk = _mm256_set1_epi16(static_cast<short>(mask));
+        for (; k + 16 <= hi; k += 16) {
+            const __m256i x = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(h + k));
+            acc = _mm256_or_si256(acc, _mm256_cmpeq_epi16(_mm256_and_si256(x, mk), mk));
+        }
     }
-    return !_mm256_testz_si256(acc, acc) || nonfinite_scalar(g, k, hi, mask);
+    return !_mm256_testz_si256(acc, acc) || nonfinite_scalar(g, k, hi, mask, f32);
 }
 
 // ------------------------------------------------------------ AVX-512
@@ -251,12 +288,16 @@ ZMI_AVX512 void adam_avx512(const CpuAdamArgs& a, int64_t lo, int64_t hi) {
         const int64_t left = hi - k;
         const __mmask16 mk = left >= 16 ? static_cast<__mmask16>(0xFFFF)
                                         : static_cast<__mmask16>((1u << left) - 1u);
-        const __m256i h = _mm256_maskz_loadu_epi16(mk, a.g + k);
         __m512 gf;
-        if (GDT == ZERO_F16) {
-            gf = _mm512_cvtph_ps(h);
+        if (GDT == ZERO_F32) {
+            gf = _mm512_maskz_loadu_ps(mk, static_cast<const float*>(a.g) + k);
         } else {
-            gf = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(h), 16));
+            const __m256i h = _mm256_maskz_loadu_epi16(mk, static_cast<const uint16_t*>(a.g) + k);
+            if (GDT == ZERO_F16) {
+                gf = _mm512_cvtph_ps(h);
+            } else {
+                gf = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(h), 16));
+            }
         }
         __m512 p = _mm512_maskz_loadu_ps(mk, a.p + k);
         __m512 gu = _mm512_mul_ps(gf, inv);
@@ -300,13 +341,28 @@ ZMI_AVX512 void adam_avx512(const CpuAdamArgs& a, int64_t lo, int64_t hi) {
     _mm_sfence();  // streaming stores visible before the caller hands the buffer on
 }
 
-ZMI_AVX512 bool nonfinite_avx512(const uint16_t* g, int64_t lo, int64_t hi, uint32_t mask) {
+ZMI_AVX512 bool nonfinite_avx512(const void* g, int64_t lo, int64_t hi, uint32_t mask,
+                                 bool f32) {
+    if (f32) {
+        const uint32_t* w = static_cast<const uint32_t*>(g);
+        const __m512i mk = _mm512_set1_epi32(static_cast<int>(mask));
+        __mmask16 acc = 0;
+        for (int64_t k = lo; k < hi; k += 16) {
+            const int64_t left = hi - k;
+            const __mmask16 lm = left >= 16 ? static_cast<__mmask16>(0xFFFF)
+                                            : static_cast<__mmask16>((1u << left) - 1u);
+            const __m512i x = _mm512_maskz_loadu_epi32(lm, w + k);
+            acc |= _mm512_mask_cmpeq_epi32_mask(lm, _mm512_and_si512(x, mk), mk);
+        }
+        return acc != 0;
+    }
+    const uint16_t* h = static_cast<const uint16_t*>(g);
     const __m512i mk = _mm512_set1_epi16(static_cast<short>(mask));
     __mmask32 acc = 0;
     for (int64_t k = lo; k < hi; k += 32) {
         const int64_t left = hi - k;
         const __mmask32 lm = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
-        const __m512i x = _mm512_maskz_loadu_epi16(lm, g + k);
+        const __m512i x = _mm512_maskz_loadu_epi16(lm, h + k);
         acc |= _mm512_mask_cmpeq_epi16_mask(lm, _mm512_and_si512(x, mk), mk);
     }
     return acc != 0;
@@ -349,6 +405,7 @@ RangeFn pick2(int pdt, bool adamw) {
 
 template <CpuIsa ISA>
 RangeFn pick1(int gdt, int pdt, bool adamw) {
+    if (gdt == ZERO_F32) return pick2<ISA, ZERO_F32>(pdt, adamw);
     return gdt == ZERO_F16 ? pick2<ISA, ZERO_F16>(pdt, adamw) : pick2<ISA, ZERO_BF16>(pdt, adamw);
 }
 
@@ -391,18 +448,19 @@ const char* cpu_isa_name(CpuIsa isa) {
 
 CpuIsa cpu_isa() { return detect_isa(); }
 
-bool cpu_nonfinite(const uint16_t* g, int64_t n, int gdt, int n_threads) {
+bool cpu_nonfinite(const void* g, int64_t n, int gdt, int n_threads) {
     if (n <= 0) return false;
-    const uint32_t mask = gdt == ZERO_F16 ? kF16ExpMask : kBf16ExpMask;
+    const bool f32 = gdt == ZERO_F32;
+    const uint32_t mask = f32 ? kF32ExpMask : gdt == ZERO_F16 ? kF16ExpMask : kBf16ExpMask;
     const CpuIsa isa = detect_isa();
     std::vector<char> hit(static_cast<size_t>(std::max(n_threads, 1)) + 1, 0);
     int64_t chunk = (n + std::max(n_threads, 1) - 1) / std::max(n_threads, 1);
     chunk = std::max<int64_t>(64, (chunk + 63) / 64 * 64);
     parallel_ranges(n, n_threads, [&](int64_t lo, int64_t hi) {
         bool bad;
-        if (isa == CpuIsa::kAvx512) bad = nonfinite_avx512(g, lo, hi, mask);
-        else if (isa == CpuIsa::kAvx2) bad = nonfinite_avx2(g, lo, hi, mask);
-        else bad = nonfinite_scalar(g, lo, hi, mask);
+        if (isa == CpuIsa::kAvx512) bad = nonfinite_avx512(g, lo, hi, mask, f32);
+        else if (isa == CpuIsa::kAvx2) bad = nonfinite_avx2(g, lo, hi, mask, f32);
+        else bad = nonfinite_scalar(g, lo, hi, mask, f32);
         hit[static_cast<size_t>(lo / chunk)] = bad ? 1 : 0;
     });
     return std::any_of(hit.begin(), hit.end(), [](char c) { return c != 0; });

@@ -151,7 +151,8 @@ int build_plan(const int64_t* numels, int32_t n, int32_t R, int32_t r, int64_t A
 // ---------------------------------------------------------------- kernels
 // One contiguous piece of the flat destination and where its source is:
 // element d of the flat shard (begin <= d < end) comes from
-// src_base + 2*d bytes, or is zero when src_base == 0.
+// src_base + esize*d bytes (esize 2 for half gradients, 4 for fp32 ones),
+// or is zero when src_base == 0.
 struct FlatPiece {
     int64_t begin;
     int64_t end;
@@ -160,12 +161,12 @@ struct FlatPiece {
 
 constexpr int kMaxPiecesPerLaunch = 64;
 
-hipError_t launch_flatten(const FlatPiece* pieces, int n, uint16_t* flat, int* flag,
-                          int grad_dtype, hipStream_t s);
-hipError_t launch_scan(const uint16_t* flat, int64_t n, int* flag, int grad_dtype, hipStream_t s);
+hipError_t launch_flatten(const FlatPiece* pieces, int n, void* flat, int* flag, int grad_dtype,
+                          hipStream_t s);
+hipError_t launch_scan(const void* flat, int64_t n, int* flag, int grad_dtype, hipStream_t s);
 // sc_dev == nullptr: the update uses the scalars passed by value in sc;
 // otherwise it reads them from device memory at sc_dev.
-hipError_t launch_adam(const uint16_t* g, float* master, float* m, float* v, uint16_t* param_at_0,
+hipError_t launch_adam(const void* g, float* master, float* m, float* v, uint16_t* param_at_0,
                        int64_t S, int64_t real, const int* flag, const AdamScalars& sc,
                        const AdamScalars* sc_dev, int grad_dtype, int param_dtype, bool adamw,
                        hipStream_t s);
@@ -189,7 +190,7 @@ enum class CpuIsa { kScalar = 0, kAvx2 = 1, kAvx512 = 2 };
 // update.  param points at shard element 0's destination (nullptr: no
 // parameter write); elements k >= real are never written to it.
 struct CpuAdamArgs {
-    const uint16_t* g;
+    const void* g;  // n gradients of dtype gdt (2 or 4 bytes each)
     float* p;
     float* m;
     float* v;
@@ -205,6 +206,9 @@ struct CpuAdamArgs {
 CpuIsa cpu_isa();
 const char* cpu_isa_name(CpuIsa isa);
 void cpu_adam(const CpuAdamArgs& a, int n_threads);
-bool cpu_nonfinite(const uint16_t* g, int64_t n, int gdt, int n_threads);
+bool cpu_nonfinite(const void* g, int64_t n, int gdt, int n_threads);
+
+// Bytes per gradient element.
+inline int grad_bytes(int gdt) { return gdt == ZERO_F32 ? 4 : 2; }
 
 }  // namespace zmi

@@ -19,11 +19,12 @@
 //     37.1 ms vs 38.2 ms for 256 threads x 1 element, 37.6 ms for 256 x 4
 //     and 38.1 ms for 64 x 2 (same box, same run).
 //   * non-temporal loads and stores (the streaming cache policy) on the
-//     three fp32 state arrays, plain accesses for the half gradient and
-//     parameter: +3-6% on the update.  Every byte of the state is touched
+//     three fp32 state arrays, plain accesses for the gradient (half, or
+//     fp32 when gradients are kept in fp32) and the half parameter: +3-6%
+//     on the update.  Every byte of the state is touched
 //     exactly once per step, so nothing is lost by not keeping it cached.
 //   * flatten and scan (one read and at most one write stream) move 16-byte
-//     vectors (8 halves), like a plain copy, with non-temporal stores, and
+//     vectors (8 halves or 4 fp32 gradients), like a plain copy, with non-temporal stores, and
 //     non-temporal loads where the source is 16-byte aligned (copy 6.19 ->
 //     6.44 TB/s, read 6.81 -> 7.07).  A flatten workgroup first searches
 //     the launch's piece table for its tile (a short chain of dependent
@@ -53,10 +54,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kVec = 8;                     // halves per 16-byte access
-constexpr int64_t kTile = kThreads * kVec;  // scan tile: 2048 elements
+constexpr int kVec = 8;                     // 16-bit words per 16-byte access
+constexpr int64_t kTile = kThreads * kVec;  // 2048 words per workgroup and vector
 constexpr int kFlatV = 2;                   // 16-byte vectors per thread in flatten
-constexpr int64_t kFlatTile = kTile * kFlatV;  // flatten tile: 4096 elements
+constexpr int64_t kFlatTile = kTile * kFlatV;  // flatten tile: 4096 16-bit words
 constexpr int64_t kGridX = 65536;           // x extent of the 2-D grids
 constexpr int kAdamThreads = 128;           // update: two waves per workgroup,
 constexpr int kAdamPer = 2;                 // two elements per thread,
@@ -75,19 +76,21 @@ dim3 grid_2d(int64_t blocks) {
     return dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
 }
 
-// ------------------------------------------------------------ half helpers
+// ------------------------------------------------------------ dtype helpers
 // Exponent field all ones <=> +-inf or NaN (binary16: bits 14..10,
-// bfloat16: bits 14..7).
+// bfloat16: bits 14..7, binary32: bits 30..23).  x holds one element.
 template <int DT>
-__device__ __forceinline__ bool half_nonfinite(uint32_t h) {
-    return DT == ZERO_F16 ? (h & 0x7C00u) == 0x7C00u : (h & 0x7F80u) == 0x7F80u;
+__device__ __forceinline__ bool elem_nonfinite(uint32_t x) {
+    if (DT == ZERO_F32) return (x & 0x7F800000u) == 0x7F800000u;
+    return DT == ZERO_F16 ? (x & 0x7C00u) == 0x7C00u : (x & 0x7F80u) == 0x7F80u;
 }
 
-// Branch-free ORs over the halves of a word / a 16-byte vector.
+// Branch-free ORs over the elements of a word / a 16-byte vector.
 template <int DT>
 __device__ __forceinline__ int word_nonfinite(uint32_t w) {
-    return static_cast<int>(half_nonfinite<DT>(w & 0xFFFFu)) |
-           static_cast<int>(half_nonfinite<DT>(w >> 16));
+    if (DT == ZERO_F32) return static_cast<int>(elem_nonfinite<DT>(w));
+    return static_cast<int>(elem_nonfinite<DT>(w & 0xFFFFu)) |
+           static_cast<int>(elem_nonfinite<DT>(w >> 16));
 }
 
 template <int DT>
@@ -97,7 +100,8 @@ __device__ __forceinline__ bool vec_nonfinite(const u32x4& q) {
 }
 
 template <int DT>
-__device__ __forceinline__ float half_to_f32(uint32_t h) {
+__device__ __forceinline__ float grad_to_f32(uint32_t h) {
+    if (DT == ZERO_F32) return __uint_as_float(h);
     if (DT == ZERO_BF16) return __uint_as_float(h << 16);
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
@@ -126,15 +130,19 @@ __device__ __forceinline__ void raise_flag_if_any(bool bad, int* flag) {
 }
 
 // ------------------------------------------------------------ flatten
+// The kernel copies 16-bit words: an fp32 element is two words at a 4-byte
+// aligned address, so the launcher gives fp32 pieces in word units and the
+// tile path is the same bit copy; only the nonfinite test (per 32-bit word)
+// and the element-wise edge path (4-byte elements) differ.
 struct FlattenArgs {
-    int64_t tile_first;  // tile t covers flat [t*kFlatTile, (t+1)*kFlatTile)
+    int64_t tile_first;  // tile t covers flat words [t*kFlatTile, (t+1)*kFlatTile)
     int64_t n_tiles;
     int32_t n;           // pieces, sorted by begin, disjoint
     int32_t _pad;
     uint64_t zero_mask;  // bit i: piece i is zero fill
     int64_t begin[kMaxPiecesPerLaunch];
     int64_t end[kMaxPiecesPerLaunch];
-    uint64_t src[kMaxPiecesPerLaunch];  // byte address of flat element 0's source
+    uint64_t src[kMaxPiecesPerLaunch];  // byte address of flat word 0's source
 };
 
 // 16 source bytes starting MIS bytes into the aligned pair (a, b).
@@ -235,11 +243,24 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
             const int64_t s0 = a.begin[p] > lo ? a.begin[p] : lo;
             const int64_t s1 = a.end[p] < hi ? a.end[p] : hi;
             const bool zero = (a.zero_mask >> p) & 1ull;
+            if (DT == ZERO_F32) {
+                // piece edges are even words (element edges): 4-byte elements
+                auto* flat32 = reinterpret_cast<uint32_t*>(flat);
+                for (int64_t d = (s0 >> 1) + threadIdx.x; d < (s1 >> 1); d += kThreads) {
+                    uint32_t w = 0;
+                    if (!zero) {
+                        w = *global_ptr<uint32_t>(a.src[p] + 4ull * static_cast<uint64_t>(d));
+                        bad |= elem_nonfinite<DT>(w);
+                    }
+                    flat32[d] = w;
+                }
+                continue;
+            }
             for (int64_t d = s0 + threadIdx.x; d < s1; d += kThreads) {
                 uint32_t h = 0;
                 if (!zero) {
                     h = *global_ptr<uint16_t>(a.src[p] + 2ull * static_cast<uint64_t>(d));
-                    bad |= half_nonfinite<DT>(h);
+                    bad |= elem_nonfinite<DT>(h);
                 }
                 flat[d] = static_cast<uint16_t>(h);
             }
@@ -249,19 +270,29 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
 }
 
 // ------------------------------------------------------------ scan
-// One workgroup per 2048 elements; 16-byte loads, element-wise at the tail.
+// Elements per 16-byte vector, and per workgroup (one vector per thread).
+template <int DT>
+constexpr int64_t scan_per() { return DT == ZERO_F32 ? 4 : kVec; }
+template <int DT>
+constexpr int64_t scan_span() { return kThreads * scan_per<DT>(); }
+
+// One 16-byte non-temporal load per thread, element-wise at the tail.
 template <int DT>
 __global__ void __launch_bounds__(kThreads)
-scan_kernel(const uint16_t* __restrict__ flat, int64_t n, int* __restrict__ flag) {
+scan_kernel(const void* __restrict__ flat, int64_t n, int* __restrict__ flag) {
+    constexpr int64_t per = scan_per<DT>();
     const int64_t blk = block_id();
-    if (blk * kTile >= n) return;  // the whole workgroup leaves together
-    const int64_t k0 = blk * kTile + static_cast<int64_t>(threadIdx.x) * kVec;
+    if (blk * scan_span<DT>() >= n) return;  // the whole workgroup leaves together
+    const int64_t k0 = blk * scan_span<DT>() + static_cast<int64_t>(threadIdx.x) * per;
     bool bad = false;
-    if (k0 + kVec <= n) {
+    if (k0 + per <= n) {
         bad = vec_nonfinite<DT>(
-            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(flat + k0)));
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(flat) + k0 / per));
     } else {
-        for (int64_t k = k0; k < n; ++k) bad |= half_nonfinite<DT>(flat[k]);
+        for (int64_t k = k0; k < n; ++k) {
+            bad |= elem_nonfinite<DT>(DT == ZERO_F32 ? static_cast<const uint32_t*>(flat)[k]
+                                                     : static_cast<const uint16_t*>(flat)[k]);
+        }
     }
     raise_flag_if_any(bad, flag);
 }
@@ -289,7 +320,7 @@ __device__ __forceinline__ void adam_elem(float g, float& p, float& m, float& v,
 // t + 128 and issues the loads of both before any arithmetic.
 template <int GDT, int PDT, bool ADAMW, bool DEVSC>
 __global__ void __launch_bounds__(kAdamThreads)
-adam_kernel(const uint16_t* __restrict__ g, float* __restrict__ master, float* __restrict__ mom,
+adam_kernel(const void* __restrict__ g, float* __restrict__ master, float* __restrict__ mom,
             float* __restrict__ var, uint16_t* __restrict__ param, int64_t S, int64_t real,
             const int* __restrict__ flag, const AdamScalars c_arg,
             const AdamScalars* __restrict__ c_dev) {
@@ -305,14 +336,15 @@ adam_kernel(const uint16_t* __restrict__ g, float* __restrict__ master, float* _
             p[j] = __builtin_nontemporal_load(master + k);
             m[j] = __builtin_nontemporal_load(mom + k);
             v[j] = __builtin_nontemporal_load(var + k);
-            h[j] = g[k];
+            h[j] = GDT == ZERO_F32 ? static_cast<const uint32_t*>(g)[k]
+                                   : static_cast<const uint16_t*>(g)[k];
         }
     }
 #pragma unroll
     for (int j = 0; j < kAdamPer; ++j) {
         const int64_t k = k0 + j * kAdamThreads;
         if (k < S) {
-            adam_elem<ADAMW>(half_to_f32<GDT>(h[j]), p[j], m[j], v[j], c);
+            adam_elem<ADAMW>(grad_to_f32<GDT>(h[j]), p[j], m[j], v[j], c);
             __builtin_nontemporal_store(p[j], master + k);
             __builtin_nontemporal_store(m[j], mom + k);
             __builtin_nontemporal_store(v[j], var + k);
@@ -381,7 +413,7 @@ __global__ void offload_snapshot_kernel(int* __restrict__ flag, DeviceStep* __re
 }
 
 template <int GDT, int PDT, bool ADAMW>
-hipError_t adam_dispatch_d(const AdamScalars* dsc, dim3 grid, hipStream_t s, const uint16_t* g,
+hipError_t adam_dispatch_d(const AdamScalars* dsc, dim3 grid, hipStream_t s, const void* g,
                            float* master, float* m, float* v, uint16_t* param, int64_t S,
                            int64_t real, const int* flag, const AdamScalars& sc) {
     if (dsc != nullptr) {
@@ -396,7 +428,7 @@ hipError_t adam_dispatch_d(const AdamScalars* dsc, dim3 grid, hipStream_t s, con
 
 template <int GDT, int PDT>
 hipError_t adam_dispatch_w(bool adamw, const AdamScalars* dsc, dim3 grid, hipStream_t s,
-                           const uint16_t* g, float* master, float* m, float* v, uint16_t* param,
+                           const void* g, float* master, float* m, float* v, uint16_t* param,
                            int64_t S, int64_t real, const int* flag, const AdamScalars& sc) {
     if (adamw) {
         return adam_dispatch_d<GDT, PDT, true>(dsc, grid, s, g, master, m, v, param, S, real,
@@ -408,7 +440,7 @@ hipError_t adam_dispatch_w(bool adamw, const AdamScalars* dsc, dim3 grid, hipStr
 
 template <int GDT>
 hipError_t adam_dispatch_p(int pdt, bool adamw, const AdamScalars* dsc, dim3 grid, hipStream_t s,
-                           const uint16_t* g, float* master, float* m, float* v, uint16_t* param,
+                           const void* g, float* master, float* m, float* v, uint16_t* param,
                            int64_t S, int64_t real, const int* flag, const AdamScalars& sc) {
     if (param == nullptr) {
         return adam_dispatch_w<GDT, 0>(adamw, dsc, grid, s, g, master, m, v, param, S, real, flag,
@@ -425,43 +457,55 @@ hipError_t adam_dispatch_p(int pdt, bool adamw, const AdamScalars* dsc, dim3 gri
 }  // namespace
 
 // ------------------------------------------------------------ launchers
-hipError_t launch_flatten(const FlatPiece* pieces, int n, uint16_t* flat, int* flag,
-                          int grad_dtype, hipStream_t s) {
+hipError_t launch_flatten(const FlatPiece* pieces, int n, void* flat, int* flag, int grad_dtype,
+                          hipStream_t s) {
     if (n <= 0) return hipSuccess;
+    // the kernel works in 16-bit words: an fp32 element is two
+    const int64_t words = grad_dtype == ZERO_F32 ? 2 : 1;
     FlattenArgs a{};
     a.n = n;
     a.zero_mask = 0;
     for (int i = 0; i < n; ++i) {
-        a.begin[i] = pieces[i].begin;
-        a.end[i] = pieces[i].end;
+        a.begin[i] = pieces[i].begin * words;
+        a.end[i] = pieces[i].end * words;
         a.src[i] = pieces[i].src_base;
         if (pieces[i].src_base == 0) a.zero_mask |= 1ull << i;
     }
-    const int64_t lo = pieces[0].begin, hi = pieces[n - 1].end;
+    const int64_t lo = a.begin[0], hi = a.end[n - 1];
     a.tile_first = lo / kFlatTile;
     a.n_tiles = (hi + kFlatTile - 1) / kFlatTile - a.tile_first;
     if (a.n_tiles <= 0) return hipSuccess;
     const dim3 grid = grid_2d(a.n_tiles);
+    auto* words16 = static_cast<uint16_t*>(flat);
     if (grad_dtype == ZERO_F16) {
-        hipLaunchKernelGGL(flatten_kernel<ZERO_F16>, grid, dim3(kThreads), 0, s, a, flat, flag);
+        hipLaunchKernelGGL(flatten_kernel<ZERO_F16>, grid, dim3(kThreads), 0, s, a, words16, flag);
+    } else if (grad_dtype == ZERO_BF16) {
+        hipLaunchKernelGGL(flatten_kernel<ZERO_BF16>, grid, dim3(kThreads), 0, s, a, words16, flag);
     } else {
-        hipLaunchKernelGGL(flatten_kernel<ZERO_BF16>, grid, dim3(kThreads), 0, s, a, flat, flag);
+        hipLaunchKernelGGL(flatten_kernel<ZERO_F32>, grid, dim3(kThreads), 0, s, a, words16, flag);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_scan(const uint16_t* flat, int64_t n, int* flag, int grad_dtype, hipStream_t s) {
+template <int DT>
+void scan_launch(const void* flat, int64_t n, int* flag, hipStream_t s) {
+    const dim3 grid = grid_2d((n + scan_span<DT>() - 1) / scan_span<DT>());
+    hipLaunchKernelGGL(scan_kernel<DT>, grid, dim3(kThreads), 0, s, flat, n, flag);
+}
+
+hipError_t launch_scan(const void* flat, int64_t n, int* flag, int grad_dtype, hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    const dim3 grid = grid_2d((n + kTile - 1) / kTile);
     if (grad_dtype == ZERO_F16) {
-        hipLaunchKernelGGL(scan_kernel<ZERO_F16>, grid, dim3(kThreads), 0, s, flat, n, flag);
+        scan_launch<ZERO_F16>(flat, n, flag, s);
+    } else if (grad_dtype == ZERO_BF16) {
+        scan_launch<ZERO_BF16>(flat, n, flag, s);
     } else {
-        hipLaunchKernelGGL(scan_kernel<ZERO_BF16>, grid, dim3(kThreads), 0, s, flat, n, flag);
+        scan_launch<ZERO_F32>(flat, n, flag, s);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_adam(const uint16_t* g, float* master, float* m, float* v, uint16_t* param_at_0,
+hipError_t launch_adam(const void* g, float* master, float* m, float* v, uint16_t* param_at_0,
                        int64_t S, int64_t real, const int* flag, const AdamScalars& sc,
                        const AdamScalars* sc_dev, int grad_dtype, int param_dtype, bool adamw,
                        hipStream_t s) {
@@ -469,6 +513,10 @@ hipError_t launch_adam(const uint16_t* g, float* master, float* m, float* v, uin
     const dim3 grid = grid_2d((S + kAdamSpan - 1) / kAdamSpan);
     if (grad_dtype == ZERO_F16) {
         return adam_dispatch_p<ZERO_F16>(param_dtype, adamw, sc_dev, grid, s, g, master, m, v,
+                                         param_at_0, S, real, flag, sc);
+    }
+    if (grad_dtype == ZERO_F32) {
+        return adam_dispatch_p<ZERO_F32>(param_dtype, adamw, sc_dev, grid, s, g, master, m, v,
                                          param_at_0, S, real, flag, sc);
     }
     return adam_dispatch_p<ZERO_BF16>(param_dtype, adamw, sc_dev, grid, s, g, master, m, v,

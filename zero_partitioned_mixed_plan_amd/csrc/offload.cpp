@@ -62,7 +62,7 @@ struct zero_offload {
     int n_threads = 1;
     int device = -1;
     // library-owned buffers
-    uint16_t* hgrad[2] = {nullptr, nullptr};   // pinned, S each
+    void* hgrad[2] = {nullptr, nullptr};       // pinned, S gradients each
     uint16_t* hparam[2] = {nullptr, nullptr};  // pinned, max(real, 1) each
     OffloadSlot* hslot = nullptr;              // pinned, 2 slots
     OffloadSlot* dslot = nullptr;              // device, 2 slots
@@ -271,8 +271,8 @@ int zero_offload_create(zero_plan_t* p, const zero_adam_hparams_t* hp, int32_t g
     if (out == nullptr) return fail(ZERO_ENULL, "out is NULL");
     *out = nullptr;
     if (p == nullptr || hp == nullptr) return fail(ZERO_ENULL, "plan or hparams is NULL");
-    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16) {
-        return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16");
+    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16 && grad_dtype != ZERO_F32) {
+        return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16, ZERO_BF16 or ZERO_F32");
     }
     if (param_dtype != 0 && param_dtype != ZERO_F16 && param_dtype != ZERO_BF16) {
         return fail(ZERO_EINVAL, "param_dtype must be 0, ZERO_F16 or ZERO_BF16");
@@ -301,7 +301,8 @@ int zero_offload_create(zero_plan_t* p, const zero_adam_hparams_t* hp, int32_t g
     o->v = exp_avg_sq;
     o->n_threads = n_threads;
     o->device = dev;
-    const size_t gbytes = 2 * static_cast<size_t>(p->S > 0 ? p->S : 1);
+    const size_t gbytes =
+        static_cast<size_t>(grad_bytes(grad_dtype)) * static_cast<size_t>(p->S > 0 ? p->S : 1);
     const size_t pbytes = 2 * static_cast<size_t>(p->real > 0 ? p->real : 1);
     for (int b = 0; b < 2 && e == hipSuccess; ++b) {
         e = hipHostMalloc(reinterpret_cast<void**>(&o->hgrad[b]), gbytes, hipHostMallocDefault);
@@ -370,7 +371,8 @@ int zero_offload_submit(zero_offload_t* o, const void* flat_grad, void* param, i
     hipError_t e = launch_offload_snapshot(p->dev.d_flag, st, o->dslot + b, s);
     if (e != hipSuccess) return hip_fail(e, "snapshot launch");
     if (p->S > 0) {
-        e = hipMemcpyAsync(o->hgrad[b], flat_grad, 2 * static_cast<size_t>(p->S),
+        e = hipMemcpyAsync(o->hgrad[b], flat_grad,
+                           static_cast<size_t>(grad_bytes(o->gdt)) * static_cast<size_t>(p->S),
                            hipMemcpyDeviceToHost, s);
         if (e != hipSuccess) return hip_fail(e, "gradient copy");
     }
