@@ -6,7 +6,8 @@
 // Case: a ragged 9-tensor model, data-parallel degree 3, rank 1, align 8,
 // fp16 gradients and parameters, dynamic loss scale from 1024 with a window
 // of 2, AdamW, 8 steps, +inf injected into step 3's gradients.  Then the
-// same with Adam-L2 and bf16.  Inputs come from the seeded generator
+// same with Adam-L2 and bf16, and with gradients kept in fp32 (fp16
+// parameters, dynamic scale).  Inputs come from the seeded generator
 // (synth/synth_host.c); the fp32 -> half rounding of the inputs uses the
 // compiler's _Float16 / __bf16 conversions (IEEE round to nearest even).
 //
@@ -29,6 +30,10 @@ int oracle_plan(const int64_t* numels, int64_t n, int64_t R, int64_t r, int64_t 
 void oracle_flatten(const uint16_t* const* grads, const int64_t* seg_tensor,
                     const int64_t* seg_tensor_off, const int64_t* seg_shard_off,
                     const int64_t* seg_numel, int64_t nseg, int64_t S, int64_t real, uint16_t* flat);
+void oracle_flatten_f32(const uint32_t* const* grads, const int64_t* seg_tensor,
+                        const int64_t* seg_tensor_off, const int64_t* seg_shard_off,
+                        const int64_t* seg_numel, int64_t nseg, int64_t S, int64_t real,
+                        uint32_t* flat);
 int oracle_adam_step(int64_t n, int64_t t, double scale, const void* flat, int gdt,
                      float* master, float* m, float* v, double lr, double b1, double b2,
                      double eps, double wd, int adamw);
@@ -74,7 +79,18 @@ uint16_t to_half(float x, int dt) {
     return h;
 }
 
-int run_case(int gdt, int adamw) {
+// The bits of one gradient element of dtype dt (fp32: the value as it is).
+uint32_t grad_word(float x, int dt) {
+    if (dt == ZERO_F32) {
+        uint32_t u;
+        std::memcpy(&u, &x, 4);
+        return u;
+    }
+    return to_half(x, dt);
+}
+
+int run_case(int gdt, int pdt, int adamw) {
+    const size_t esize = gdt == ZERO_F32 ? 4 : 2;
     const std::vector<int64_t> numels = {3000, 1, 7, 100003, 65, 2048, 511, 30000, 13};
     const int R = 3, r = 1, A = 8, steps = 8, inject_step = 3;
     const int64_t B = 20000;
@@ -105,10 +121,10 @@ int run_case(int gdt, int adamw) {
 
     // device buffers
     std::vector<void*> d_grads(n, nullptr);
-    for (int i = 0; i < n; ++i) HIP_OK(hipMalloc(&d_grads[i], 2 * numels[i]));
+    for (int i = 0; i < n; ++i) HIP_OK(hipMalloc(&d_grads[i], esize * numels[i]));
     void *d_flat, *d_param;
     float *d_master, *d_m, *d_v;
-    HIP_OK(hipMalloc(&d_flat, 2 * S));
+    HIP_OK(hipMalloc(&d_flat, esize * S));
     HIP_OK(hipMalloc(&d_param, 2 * P));
     HIP_OK(hipMalloc(reinterpret_cast<void**>(&d_master), 4 * S));
     HIP_OK(hipMalloc(reinterpret_cast<void**>(&d_m), 4 * S));
@@ -125,7 +141,7 @@ int run_case(int gdt, int adamw) {
     HIP_OK(hipMemcpy(d_param, o_param.data(), 2 * P, hipMemcpyHostToDevice));
 
     zero_adam_hparams_t hp = {1e-3, 0.9, 0.999, 1e-8, 0.05, adamw, 0};
-    const int dynamic = gdt == ZERO_F16;
+    const int dynamic = gdt != ZERO_BF16;
     zero_scaler_t scaler = {dynamic ? 1024.0 : 1.0, 1.0, 0.5, 2.0, 2, 0, dynamic, 0};
     double o_scale = scaler.scale;
     int32_t o_good = 0;
@@ -133,9 +149,11 @@ int run_case(int gdt, int adamw) {
     hipStream_t s;
     HIP_OK(hipStreamCreate(&s));
 
-    std::vector<std::vector<uint16_t>> grads(n);
-    std::vector<const uint16_t*> gptr(n);
-    std::vector<uint16_t> o_flat(S), g_flat(S), g_param(P);
+    std::vector<std::vector<uint32_t>> grads(n);      // element bits (fp16/bf16 in the low half)
+    std::vector<std::vector<unsigned char>> gbytes(n);  // the same, packed at esize bytes each
+    std::vector<const void*> gptr(n);
+    std::vector<unsigned char> o_flat(esize * S), g_flat(esize * S);
+    std::vector<uint16_t> g_param(P);
     std::vector<float> g_master(S), g_m(S), g_v(S), vals;
     for (int it = 1; it <= steps; ++it) {
         // this step's gradients, scaled by the current loss scale
@@ -144,33 +162,51 @@ int run_case(int gdt, int adamw) {
             synth_fill_f32(vals.data(), numels[i], synth_key(0, 1, it), off[i], 1e-2f,
                            static_cast<float>(o_scale), 0, 1.0f);
             grads[i].resize(numels[i]);
-            for (int64_t k = 0; k < numels[i]; ++k) grads[i][k] = to_half(vals[k], gdt);
-            gptr[i] = grads[i].data();
+            for (int64_t k = 0; k < numels[i]; ++k) grads[i][k] = grad_word(vals[k], gdt);
         }
         if (it == inject_step) {  // +inf in the middle of the shard's first segment
-            grads[st[0]][sto[0] + sn[0] / 2] = gdt == ZERO_F16 ? 0x7C00 : 0x7F80;
+            grads[st[0]][sto[0] + sn[0] / 2] =
+                gdt == ZERO_F32 ? 0x7F800000u : gdt == ZERO_F16 ? 0x7C00u : 0x7F80u;
         }
         for (int i = 0; i < n; ++i) {
-            HIP_OK(hipMemcpy(d_grads[i], grads[i].data(), 2 * numels[i], hipMemcpyHostToDevice));
+            gbytes[i].resize(esize * numels[i]);
+            for (int64_t k = 0; k < numels[i]; ++k) {
+                if (esize == 4) {
+                    std::memcpy(&gbytes[i][4 * k], &grads[i][k], 4);
+                } else {
+                    const uint16_t h = static_cast<uint16_t>(grads[i][k]);
+                    std::memcpy(&gbytes[i][2 * k], &h, 2);
+                }
+            }
+            gptr[i] = gbytes[i].data();
+            HIP_OK(hipMemcpy(d_grads[i], gbytes[i].data(), esize * numels[i],
+                             hipMemcpyHostToDevice));
         }
         // library: flatten all buckets, gated step, scaler
         std::vector<const void*> dg(d_grads.begin(), d_grads.end());
         ZERO_OK_OR_FAIL(zero_flatten_grads(plan, -1, dg.data(), gdt, d_flat, s));
         const double scale_used = scaler.scale;
         const int flag = zero_adam_step(plan, &hp, t + 1, scale_used, d_flat, gdt, d_master, d_m,
-                                        d_v, d_param, 0, P, gdt, s);
+                                        d_v, d_param, 0, P, pdt, s);
         ZERO_OK_OR_FAIL(flag);
         ZERO_OK_OR_FAIL(zero_update_loss_scale(&scaler, flag));
         if (!flag) ++t;
         // oracle
-        oracle_flatten(gptr.data(), st.data(), sto.data(), sso.data(), sn.data(), nseg, S, real,
-                       o_flat.data());
+        if (esize == 4) {
+            oracle_flatten_f32(reinterpret_cast<const uint32_t* const*>(gptr.data()), st.data(),
+                               sto.data(), sso.data(), sn.data(), nseg, S, real,
+                               reinterpret_cast<uint32_t*>(o_flat.data()));
+        } else {
+            oracle_flatten(reinterpret_cast<const uint16_t* const*>(gptr.data()), st.data(),
+                           sto.data(), sso.data(), sn.data(), nseg, S, real,
+                           reinterpret_cast<uint16_t*>(o_flat.data()));
+        }
         const int o_flag = oracle_adam_step(S, o_t + 1, o_scale, o_flat.data(), gdt,
                                             o_master.data(), o_m.data(), o_v.data(), hp.lr,
                                             hp.beta1, hp.beta2, hp.eps, hp.weight_decay, adamw);
         if (!o_flag) {
             ++o_t;
-            oracle_write_param(o_master.data(), real, begin, 0, o_param.data(), gdt);
+            oracle_write_param(o_master.data(), real, begin, 0, o_param.data(), pdt);
         }
         oracle_update_scale(&o_scale, &o_good, o_flag, dynamic, 1.0, 0.5, 2.0, 2);
         // compare
@@ -180,12 +216,12 @@ int run_case(int gdt, int adamw) {
                         o_scale);
             return 1;
         }
-        HIP_OK(hipMemcpy(g_flat.data(), d_flat, 2 * S, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(g_flat.data(), d_flat, esize * S, hipMemcpyDeviceToHost));
         HIP_OK(hipMemcpy(g_master.data(), d_master, 4 * S, hipMemcpyDeviceToHost));
         HIP_OK(hipMemcpy(g_m.data(), d_m, 4 * S, hipMemcpyDeviceToHost));
         HIP_OK(hipMemcpy(g_v.data(), d_v, 4 * S, hipMemcpyDeviceToHost));
         HIP_OK(hipMemcpy(g_param.data(), d_param, 2 * P, hipMemcpyDeviceToHost));
-        if (std::memcmp(g_flat.data(), o_flat.data(), 2 * S) != 0 ||
+        if (std::memcmp(g_flat.data(), o_flat.data(), esize * S) != 0 ||
             std::memcmp(g_master.data(), o_master.data(), 4 * S) != 0 ||
             std::memcmp(g_m.data(), o_m.data(), 4 * S) != 0 ||
             std::memcmp(g_v.data(), o_v.data(), 4 * S) != 0 ||
@@ -208,7 +244,8 @@ int run_case(int gdt, int adamw) {
     HIP_OK(hipFree(d_v));
     HIP_OK(hipStreamDestroy(s));
     zero_plan_destroy(plan);
-    std::printf("case gdt=%d adamw=%d: %d steps, %lld applied, scale %g\n", gdt, adamw, steps,
+    std::printf("case gdt=%d pdt=%d adamw=%d: %d steps, %lld applied, scale %g\n", gdt, pdt,
+                adamw, steps,
                 static_cast<long long>(t), scaler.scale);
     return 0;
 }
@@ -216,8 +253,9 @@ int run_case(int gdt, int adamw) {
 }  // namespace
 
 int main() {
-    if (run_case(ZERO_F16, 1) != 0) return 1;
-    if (run_case(ZERO_BF16, 0) != 0) return 1;
+    if (run_case(ZERO_F16, ZERO_F16, 1) != 0) return 1;
+    if (run_case(ZERO_BF16, ZERO_BF16, 0) != 0) return 1;
+    if (run_case(ZERO_F32, ZERO_F16, 1) != 0) return 1;
     std::printf("c-abi ok\n");
     return 0;
 }

@@ -1,5 +1,5 @@
 """The C ABI without Python: tests/c_abi_check (C++, hipMalloc'ed buffers,
-built by __graft_entry__.build()) runs two cases through include/zero_mi355x.h
+built by __graft_entry__.build()) runs three cases through include/zero_mi355x.h
 and compares every step with the C oracle bit for bit (see its header)."""
 import os
 import subprocess
