@@ -109,7 +109,10 @@ def setup(w, device):
     return plan, master, m, v, flat, param, z.GradList(plan, grads)
 
 
-def run_gpu(w, steps, warmup, device):
+def run_gpu(w, steps, warmup, device, step_log=None):
+    """The synchronous step, `steps` timed after `warmup`.  step_log: a file
+    that receives one JSON line per timed step (t, overflow, scale, kernel
+    times and rates)."""
     import torch
 
     import zero_partitioned_mixed_plan_amd as z
@@ -122,7 +125,8 @@ def run_gpu(w, steps, warmup, device):
 
     def one_step(times=None):
         z.zero_flatten_grads(plan, -1, grads, flat)
-        ovf = z.zero_adam_step(plan, hp, state["t"] + 1, scaler.scale, flat, master, m, v,
+        scale_used = scaler.scale
+        ovf = z.zero_adam_step(plan, hp, state["t"] + 1, scale_used, flat, master, m, v,
                                param, plan.begin)
         z.zero_update_loss_scale(scaler, ovf)
         if ovf:
@@ -130,20 +134,35 @@ def run_gpu(w, steps, warmup, device):
         else:
             state["t"] += 1
         if times is not None:
-            times["flatten"].append(plan.kernel_ms(0))
-            times["adam"].append(plan.kernel_ms(2))
+            # kernel statistics over applied steps only: a skipped step's update
+            # kernel returns at once (the per-step log keeps every step)
+            fl, ad = plan.kernel_ms(0), plan.kernel_ms(2)
+            if not ovf:
+                times["flatten"].append(fl)
+                times["adam"].append(ad)
+            times["rec"].append((state["t"], int(ovf), scale_used, scaler.scale, fl, ad))
 
     for i in range(warmup):
         one_step()
         log(f"[bench] warmup step {i + 1}/{warmup} done")
     torch.cuda.synchronize(device)
-    times = {"flatten": [], "adam": []}
+    times = {"flatten": [], "adam": [], "rec": []}
     t0 = time.perf_counter()
     for _ in range(steps):
         one_step(times)
     torch.cuda.synchronize(device)
     wall = time.perf_counter() - t0
     log(f"[bench] timed {steps} steps in {wall:.3f} s; skipped {state['skipped']}")
+    if step_log is not None:   # written after the timed region
+        ab, fb = adam_bytes(w.grad_dtype), flatten_bytes(w.grad_dtype)
+        for i, (t, ovf, sc_used, sc_next, fl, ad) in enumerate(times["rec"], 1):
+            gbs = ab * plan.S / (ad * 1e-3) / 1e9
+            step_log.write(json.dumps({
+                "step": i, "t": t, "overflow": ovf, "scale_used": sc_used, "scale_next": sc_next,
+                "flatten_ms": fl, "adam_ms": ad, "params_per_s": plan.S / (ad * 1e-3),
+                "adam_gbps": gbs, "adam_pct_peak": 100.0 * gbs / HBM_PEAK_GBS,
+                "flatten_gbps": fb * plan.S / (fl * 1e-3) / 1e9}) + "\n")
+        step_log.flush()
     return plan, wall, times, state, (plan, master, m, v, flat, param, grads, hp, scaler)
 
 
@@ -449,6 +468,9 @@ def main(argv=None):
                          "30 B/element in the update)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--step-log", default=None,
+                    help="write one JSON line per timed step (t, overflow, scale, kernel times "
+                         "and rates) to this file")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay measurement of the same step")
     ap.add_argument("--mode", choices=["device", "offload"], default="device",
@@ -495,12 +517,17 @@ def main(argv=None):
                        "real_elems": plan.real},
             "offload": res}), flush=True)
         return 0
-    plan, wall, times, state, bufs = run_gpu(w, args.steps, args.warmup, device)
+    step_log = open(args.step_log, "w") if args.step_log else None
+    plan, wall, times, state, bufs = run_gpu(w, args.steps, args.warmup, device, step_log)
+    if step_log is not None:
+        step_log.close()
     write_ms, scan_ms = time_standalone_kernels(bufs)
     graph_wall, devsc_ms = (None, None) if args.no_graph else run_graph(bufs, args.steps,
                                                                         args.warmup, device)
     S, real, begin = plan.S, plan.real, plan.begin
     ms_per_step = wall * 1000.0 / args.steps
+    if not times["adam"]:
+        raise SystemExit("every timed step was skipped (overflow): no update time to report")
     adam_ms = sum(times["adam"]) / len(times["adam"])
     flat_ms = sum(times["flatten"]) / len(times["flatten"])
     ab, fb = adam_bytes(w.grad_dtype), flatten_bytes(w.grad_dtype)
@@ -539,7 +566,8 @@ def main(argv=None):
             "scan": {"ms": scan_ms, "bytes_per_elem": GRAD_BYTES[w.grad_dtype],
                      "gbps": GRAD_BYTES[w.grad_dtype] * S / (scan_ms * 1e-3) / 1e9},
         },
-        "skipped_steps": state["skipped"],
+        "skipped_steps": state["skipped"],   # over warm-up and timed steps; kernel times
+                                             # above are over the applied timed steps
         "graph_replay": None if graph_wall is None else {
             "ms_per_step": graph_wall * 1000.0 / args.steps,
             "value": real / (graph_wall / args.steps),

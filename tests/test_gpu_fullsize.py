@@ -24,12 +24,12 @@ import oracle
 import synth
 import zero_partitioned_mixed_plan_amd as z
 from harness import (INF_BITS, REL_TOL, ULP_TOL, Case, flat_offsets, grad_key, log, master_key,
-                     max_rel, torch_dtype, ulp_diff)
+                     grad_bits_host, max_rel, torch_dtype, ulp_diff)
 from synth.workloads import get
 
 pytestmark = pytest.mark.gpu
 
-HALF_MAX = {"f16": 65504.0, "bf16": 3.3895313892515355e38}
+HALF_MAX = {"f16": 65504.0, "bf16": 3.3895313892515355e38, "f32": 3.4028234663852886e38}
 
 
 def _windows(op, case, n_random=8, rnd_len=32768, seed=1):
@@ -131,7 +131,7 @@ def _run_sampled(case, check_at, flatten_mode="all", label=""):
         vals = np.zeros(idx.size, np.float32)
         vals[in_real] = synth.host_gather(key, begin + idx[in_real], case.grad_sigma, scale,
                                           othresh, case.outlier_mult)
-        o_flat = synth.half_bits(vals, case.grad_dtype)
+        o_flat = synth.grad_bits(vals, case.grad_dtype)
         o_flat[~in_real] = 0
         if pos is not None:
             o_flat[np.searchsorted(idx, pos)] = INF_BITS[case.grad_dtype]
@@ -142,7 +142,7 @@ def _run_sampled(case, check_at, flatten_mode="all", label=""):
         g_t += 1 - g_ovf
         o_t += 1 - o_ovf
         skipped += o_ovf
-        got_flat = flat.index_select(0, d_idx).view(torch.int16).cpu().numpy().view(np.uint16)
+        got_flat = grad_bits_host(flat.index_select(0, d_idx), case.grad_dtype)
         assert np.array_equal(got_flat, o_flat), f"{label} it={it}: flat shard differs"
         if it in check_at or it == case.steps:
             gm = master.index_select(0, d_idx).cpu().numpy()
@@ -170,6 +170,12 @@ def _run_sampled(case, check_at, flatten_mode="all", label=""):
 def test_llama3_8b_rank3_bucketed_flatten():
     case = Case.from_workload(get("llama3_8b"))
     _run_sampled(case, check_at={1, 5, 10}, flatten_mode="buckets", label="llama3_8b")
+
+
+def test_llama3_8b_rank3_fp32_gradients():
+    # gradients kept in fp32 at full size: 4-byte flatten and update path
+    case = Case.from_workload(get("llama3_8b"), grad_dtype="f32", steps=6)
+    _run_sampled(case, check_at={1, 6}, label="llama3_8b fp32 grads")
 
 
 def test_dna_20b_rank2_dynamic_scale_with_injected_overflows():
