@@ -325,8 +325,14 @@ const char* zero_cpu_isa(void);
  * the host update of that step (zero_cpu_adam_step's arithmetic) and copies
  * the half parameters to the rank's offset on its own stream, ordered after
  * the caller's release of the previous parameters: the next submit, a
- * zero_offload_wait_params or zero_offload_drain.  At most two steps are in
- * flight; a submit waits (host) for the older one when needed.
+ * zero_offload_wait_params or zero_offload_drain.  The copies and the update
+ * go in pieces of at least 2^25 elements (at most 16 pieces): the update of
+ * a piece starts when its gradients have arrived, and its parameters go back
+ * at once when the release is already recorded (the serialised step), so a
+ * step's copies overlap its own update; the update never waits for the
+ * release.  (The environment variable ZERO_OFFLOAD_MIN_CHUNK, read at create,
+ * lowers the piece size, down to 64 elements, for tests.)  At most two
+ * steps are in flight; a submit waits (host) for the older one when needed.
  *
  * A training loop with the delayed update:
  *   for each step: zero_offload_wait_params(o, 1, s);   forward(s); backward(s);
@@ -364,7 +370,8 @@ typedef struct {
  * library's thread until zero_offload_drain returns.  param_dtype: 0 for no
  * parameter write-back.  grad_dtype: ZERO_F16, ZERO_BF16 or ZERO_F32.
  * Allocates two pinned gradient buffers (S elements of grad_dtype each),
- * two pinned parameter buffers (2 real bytes each), a transfer
+ * two pinned parameter buffers (2 real bytes each), a pool of n_threads - 1
+ * host threads (kept for the pipeline's life), a transfer
  * stream and a worker thread.  Errors: ZERO_ENULL, ZERO_EINVAL, ZERO_ESTATE,
  * ZERO_EHIP, ZERO_ENOMEM. */
 int zero_offload_create(zero_plan_t* plan, const zero_adam_hparams_t* hp, int32_t grad_dtype,

@@ -1,6 +1,7 @@
 // Host paths of libzero_mi355x under AddressSanitizer + UndefinedBehavior-
-// Sanitizer: the planner, the ABI's argument checks, the loss-scale policy
-// and the host (offload) update, each against the C oracle
+// Sanitizer (or ThreadSanitizer): the planner, the ABI's argument checks, the
+// loss-scale policy, the host (offload) update and its thread pool, each
+// against the C oracle
 // (oracle/zero_oracle.c, test infrastructure), bit for bit.
 //
 // Built by tests/test_host_sanitizers.py with g++ from the library's host
@@ -17,6 +18,7 @@
 #include <string>
 #include <vector>
 
+#include "internal.h"  // HostPool, cpu_adam (the host update's internals)
 #include "zero_mi355x.h"
 
 extern "C" {
@@ -171,6 +173,51 @@ bool check_cpu_step(std::mt19937_64& rng, int64_t n, int R, int r, int gdt, int 
     return true;
 }
 
+// The offload pipeline's thread pool: many jobs in a row (each must see
+// every index exactly once), and the host update run on it equal, bit for
+// bit, to the update on threads started per call.
+bool check_pool(std::mt19937_64& rng) {
+    for (int n : {1, 2, 5}) {
+        zmi::HostPool pool(n);
+        std::vector<int> hits(static_cast<size_t>(n), 0);
+        for (int job = 0; job < 200; ++job) {
+            pool.run([&](int i) { hits[static_cast<size_t>(i)] += 1; });
+        }
+        for (int i = 0; i < n; ++i) CHECK(hits[i] == 200, "pool %d: index %d ran %d times", n, i, hits[i]);
+        const int64_t len = 5000 + static_cast<int64_t>(rng() % 3000);
+        std::normal_distribution<float> nd(0.0f, 1.0f);
+        std::vector<float> gf(len), p0(len), m0(len), v0(len);
+        for (int64_t k = 0; k < len; ++k) {
+            gf[k] = 1e-2f * nd(rng);
+            p0[k] = 0.02f * nd(rng);
+            m0[k] = 1e-3f * nd(rng);
+            v0[k] = 1e-6f * std::fabs(nd(rng));
+        }
+        std::vector<uint16_t> g(len);
+        oracle_float_to_half_n(gf.data(), len, ZERO_BF16, g.data());
+        std::vector<float> pa = p0, ma = m0, va = v0, pb = p0, mb = m0, vb = v0;
+        std::vector<uint16_t> para(len, 0), parb(len, 0);
+        zmi::CpuAdamArgs a;
+        a.g = g.data();
+        a.n = len;
+        a.real = len - 7;
+        a.sc = zmi::make_scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, 1, 3.0, 1.0);
+        a.gdt = ZERO_BF16;
+        a.pdt = ZERO_BF16;
+        a.adamw = true;
+        a.p = pa.data(); a.m = ma.data(); a.v = va.data(); a.param = para.data();
+        zmi::cpu_adam(a, n, &pool);
+        a.p = pb.data(); a.m = mb.data(); a.v = vb.data(); a.param = parb.data();
+        zmi::cpu_adam(a, n, nullptr);
+        CHECK(std::memcmp(pa.data(), pb.data(), 4 * len) == 0 &&
+                  std::memcmp(ma.data(), mb.data(), 4 * len) == 0 &&
+                  std::memcmp(va.data(), vb.data(), 4 * len) == 0 &&
+                  std::memcmp(para.data(), parb.data(), 2 * len) == 0,
+              "pool %d: pooled update differs", n);
+    }
+    return true;
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -203,7 +250,7 @@ int main(int argc, char** argv) {
             if (!check_plan(numels, Rr, r, Aa, Bb, "random")) return 1;
         }
     }
-    if (!check_errors() || !check_scaler(rng)) return 1;
+    if (!check_errors() || !check_scaler(rng) || !check_pool(rng)) return 1;
     int steps = 0;
     for (int64_t sz : {int64_t(1), int64_t(7), int64_t(16), int64_t(17), int64_t(63),
                        int64_t(1000), int64_t(4099)}) {

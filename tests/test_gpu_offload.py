@@ -118,6 +118,22 @@ def test_offload_fp32_gradients(lag):
     assert _offload_run(case, lag, f"fp32 grads lag={lag}") == 1
 
 
+@pytest.mark.parametrize("lag", [1, 0])
+def test_offload_in_many_pieces(lag, monkeypatch):
+    """Copies and update in 16 pieces (the piece size lowered for the test):
+    a short last piece, pieces past the real range (padding rank), parameter
+    copies sent piece by piece (lag 0) or after the update (lag 1), and a
+    skipped step in between."""
+    monkeypatch.setenv("ZERO_OFFLOAD_MIN_CHUNK", "4096")
+    case = Case(numels=RAGGED, world_size=3, rank=2, grad_dtype="f16", param_dtype="f16",
+                steps=7, dynamic=True, init_scale=1024.0, window=2, grad_sigma=1e-2,
+                inject={4: 99999})
+    assert _offload_run(case, lag, f"pieces lag={lag}") == 1
+    case = Case(numels=RAGGED, world_size=2, rank=1, grad_dtype="f32", param_dtype="bf16",
+                steps=4, grad_sigma=1e-2)
+    assert _offload_run(case, lag, f"pieces fp32 lag={lag}") == 0
+
+
 def test_offload_gpt2_small():
     case = Case.from_workload(get("gpt2_small"), steps=6)
     _offload_run(case, 1, "gpt2_small", n_threads=8)

@@ -417,26 +417,96 @@ RangeFn pick(CpuIsa isa, int gdt, int pdt, bool adamw) {
     }
 }
 
-// Runs fn over [0, n) split into n_threads contiguous chunks (multiples of
-// 64 elements); the calling thread takes the first chunk.
+// Contiguous per-thread ranges of [0, n): multiples of 64 elements.
+int64_t range_chunk(int64_t n, int n_threads) {
+    const int64_t chunk = (n + n_threads - 1) / n_threads;
+    return std::max<int64_t>(64, (chunk + 63) / 64 * 64);
+}
+
+// Runs fn over [0, n) split into n_threads contiguous ranges; the calling
+// thread takes the first.  With a pool its threads run the others, else
+// threads are started for this call.
 template <typename Fn>
-void parallel_ranges(int64_t n, int n_threads, Fn fn) {
+void parallel_ranges(int64_t n, int n_threads, HostPool* pool, Fn fn) {
+    if (pool != nullptr) n_threads = pool->size();
     if (n_threads < 1) n_threads = 1;
-    int64_t chunk = (n + n_threads - 1) / n_threads;
-    chunk = (chunk + 63) / 64 * 64;
-    if (chunk < 64) chunk = 64;
-    std::vector<std::thread> pool;
+    const int64_t chunk = range_chunk(n, n_threads);
+    if (pool != nullptr) {
+        pool->run([&](int t) {
+            const int64_t lo = t * chunk;
+            if (lo < n) fn(lo, std::min(n, lo + chunk));
+        });
+        return;
+    }
+    std::vector<std::thread> threads;
     for (int t = 1; t < n_threads; ++t) {
         const int64_t lo = t * chunk;
         if (lo >= n) break;
         const int64_t hi = std::min(n, lo + chunk);
-        pool.emplace_back([=] { fn(lo, hi); });
+        threads.emplace_back([=] { fn(lo, hi); });
     }
     fn(0, std::min(n, chunk));
-    for (auto& th : pool) th.join();
+    for (auto& th : threads) th.join();
 }
 
 }  // namespace
+
+HostPool::HostPool(int n_threads) : n_(n_threads < 1 ? 1 : n_threads) {
+    threads_.reserve(static_cast<size_t>(n_ - 1));
+    try {
+        for (int i = 1; i < n_; ++i) threads_.emplace_back(&HostPool::worker, this, i);
+    } catch (...) {
+        {
+            std::lock_guard<std::mutex> g(mu_);
+            stop_ = true;
+        }
+        go_.notify_all();
+        for (auto& t : threads_) t.join();
+        throw;
+    }
+}
+
+HostPool::~HostPool() {
+    {
+        std::lock_guard<std::mutex> g(mu_);
+        stop_ = true;
+    }
+    go_.notify_all();
+    for (auto& t : threads_) t.join();
+}
+
+void HostPool::worker(int idx) {
+    uint64_t seen = 0;
+    for (;;) {
+        const std::function<void(int)>* job;
+        {
+            std::unique_lock<std::mutex> lk(mu_);
+            go_.wait(lk, [&] { return stop_ || gen_ != seen; });
+            if (stop_) return;
+            seen = gen_;
+            job = job_;
+        }
+        (*job)(idx);
+        {
+            std::lock_guard<std::mutex> g(mu_);
+            if (--pending_ == 0) done_.notify_all();
+        }
+    }
+}
+
+void HostPool::run(const std::function<void(int)>& fn) {
+    {
+        std::lock_guard<std::mutex> g(mu_);
+        job_ = &fn;
+        pending_ = n_ - 1;
+        ++gen_;
+    }
+    go_.notify_all();
+    fn(0);
+    std::unique_lock<std::mutex> lk(mu_);
+    done_.wait(lk, [&] { return pending_ == 0; });
+    job_ = nullptr;
+}
 
 const char* cpu_isa_name(CpuIsa isa) {
     switch (isa) {
@@ -454,9 +524,8 @@ bool cpu_nonfinite(const void* g, int64_t n, int gdt, int n_threads) {
     const uint32_t mask = f32 ? kF32ExpMask : gdt == ZERO_F16 ? kF16ExpMask : kBf16ExpMask;
     const CpuIsa isa = detect_isa();
     std::vector<char> hit(static_cast<size_t>(std::max(n_threads, 1)) + 1, 0);
-    int64_t chunk = (n + std::max(n_threads, 1) - 1) / std::max(n_threads, 1);
-    chunk = std::max<int64_t>(64, (chunk + 63) / 64 * 64);
-    parallel_ranges(n, n_threads, [&](int64_t lo, int64_t hi) {
+    const int64_t chunk = range_chunk(n, std::max(n_threads, 1));
+    parallel_ranges(n, n_threads, nullptr, [&](int64_t lo, int64_t hi) {
         bool bad;
         if (isa == CpuIsa::kAvx512) bad = nonfinite_avx512(g, lo, hi, mask, f32);
         else if (isa == CpuIsa::kAvx2) bad = nonfinite_avx2(g, lo, hi, mask, f32);
@@ -466,10 +535,10 @@ bool cpu_nonfinite(const void* g, int64_t n, int gdt, int n_threads) {
     return std::any_of(hit.begin(), hit.end(), [](char c) { return c != 0; });
 }
 
-void cpu_adam(const CpuAdamArgs& a, int n_threads) {
+void cpu_adam(const CpuAdamArgs& a, int n_threads, HostPool* pool) {
     if (a.n <= 0) return;
     const RangeFn fn = pick(detect_isa(), a.gdt, a.param ? a.pdt : 0, a.adamw);
-    parallel_ranges(a.n, n_threads, [&](int64_t lo, int64_t hi) { fn(a, lo, hi); });
+    parallel_ranges(a.n, n_threads, pool, [&](int64_t lo, int64_t hi) { fn(a, lo, hi); });
 }
 
 }  // namespace zmi

@@ -6,7 +6,11 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <condition_variable>
+#include <functional>
+#include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "zero_mi355x.h"
@@ -203,9 +207,34 @@ struct CpuAdamArgs {
     bool adamw;
 };
 
+// A fixed set of host threads that runs one job at a time: run(fn) calls
+// fn(i) for i in [0, size()) -- i = 0 on the calling thread -- and returns
+// when all have finished.  One caller at a time.
+class HostPool {
+public:
+    explicit HostPool(int n_threads);
+    ~HostPool();
+    HostPool(const HostPool&) = delete;
+    HostPool& operator=(const HostPool&) = delete;
+    int size() const { return n_; }
+    void run(const std::function<void(int)>& fn);
+
+private:
+    void worker(int idx);
+    int n_;
+    std::vector<std::thread> threads_;
+    std::mutex mu_;
+    std::condition_variable go_, done_;
+    const std::function<void(int)>* job_ = nullptr;
+    uint64_t gen_ = 0;
+    int pending_ = 0;
+    bool stop_ = false;
+};
+
 CpuIsa cpu_isa();
 const char* cpu_isa_name(CpuIsa isa);
-void cpu_adam(const CpuAdamArgs& a, int n_threads);
+// pool == nullptr: n_threads threads are started for this call.
+void cpu_adam(const CpuAdamArgs& a, int n_threads, HostPool* pool = nullptr);
 bool cpu_nonfinite(const void* g, int64_t n, int gdt, int n_threads);
 
 // Bytes per gradient element.

@@ -12,21 +12,28 @@
 //   snapshot kernel   flag, t + 1 and the scale of step i -> device slot i%2;
 //                     loss-scale policy applied to the device state; flag
 //                     cleared (so the next backward already sees the new scale)
-//   D2H               flat gradient shard -> pinned host buffer i%2, slot -> host
+//   D2H               slot -> host, then the flat gradient shard -> pinned host
+//                     buffer i%2 in chunks (up to kMaxChunks, an event after each)
 // Worker thread, steps in order:
-//   wait for the D2H; skipped step: nothing else.  Otherwise the host update
-//   (cpu_adam, same arithmetic as the device update) writes master / moments
-//   in host memory and the half parameters into pinned buffer i%2; then, on
-//   the library's transfer stream, once the caller has released the device
-//   parameters of step i (event recorded by the next submit, by
-//   zero_offload_wait_params or by zero_offload_drain), H2D of the parameters
-//   to the rank's offset.
+//   wait for the slot; skipped step: nothing else.  Otherwise, chunk by chunk
+//   as each arrives, the host update (cpu_adam on the pipeline's thread pool,
+//   same arithmetic as the device update) writes master / moments in host
+//   memory and the half parameters into pinned buffer i%2.  The parameters
+//   go back to the rank's offset on the library's transfer stream once the
+//   caller has released the device parameters of step i (event recorded by
+//   the next submit, by zero_offload_wait_params or by zero_offload_drain):
+//   chunk by chunk while the update runs if the release is already there
+//   (the serialised step, lag 0), otherwise all at once after the update --
+//   the update never waits for the release.  So the copies of a step overlap
+//   its own update instead of running before and after it.
 // zero_offload_wait_params(lag) makes the caller's stream wait until the
 // parameters of every submitted step but the last `lag` are on the device:
 // lag = 1 is the one-step delayed update (the host work of step i runs while
 // the GPU computes step i + 1), lag = 0 the plain, serialised step.
+#include <algorithm>
 #include <chrono>
 #include <condition_variable>
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 #include <mutex>
@@ -52,6 +59,13 @@ struct Pending {
 
 using namespace zmi;
 
+namespace zmi {
+namespace {
+constexpr int kMaxChunks = 16;                       // gradient / parameter copy pieces
+constexpr int64_t kMinChunkElems = int64_t(1) << 25;  // per piece (64-128 MB of gradients)
+}  // namespace
+}  // namespace zmi
+
 struct zero_offload {
     zero_plan* plan = nullptr;
     zero_adam_hparams_t hp{};
@@ -61,13 +75,17 @@ struct zero_offload {
     float* v = nullptr;
     int n_threads = 1;
     int device = -1;
+    HostPool* pool = nullptr;
+    int n_chunks = 0;   // pieces of the shard for the copies and the update
+    int64_t chunk = 0;  // elements per piece (a multiple of 64; the last may be short)
     // library-owned buffers
     void* hgrad[2] = {nullptr, nullptr};       // pinned, S gradients each
     uint16_t* hparam[2] = {nullptr, nullptr};  // pinned, max(real, 1) each
     OffloadSlot* hslot = nullptr;              // pinned, 2 slots
     OffloadSlot* dslot = nullptr;              // device, 2 slots
     hipStream_t xfer = nullptr;
-    hipEvent_t ev_d2h[2] = {}, ev_free[2] = {}, ev_h2d[2] = {};
+    hipEvent_t ev_slot[2] = {}, ev_free[2] = {}, ev_h2d[2] = {};
+    hipEvent_t ev_d2h[2][kMaxChunks] = {};
     bool h2d_recorded[2] = {false, false};  // written under mu; the worker also reads it unlocked
     // steps
     Pending rec[2];
@@ -112,9 +130,58 @@ int worker_hip(zero_offload* o, hipError_t e, const char* what) {
     return ZERO_EHIP;
 }
 
+// Enqueues the parameter copies of chunks [*sent, upto) of step buffer b on
+// the transfer stream, gated once on the caller's release of the device
+// parameters.  block = false: does nothing until that release is recorded.
+// Returns ZERO_OK, or ZERO_ESTATE when stopped while waiting, or the HIP error.
+int send_params(zero_offload* o, int b, int upto, bool block, int* sent, bool* gated,
+                double* wait_release) {
+    const zero_plan* p = o->plan;
+    if (o->pdt == 0 || p->real <= 0) {
+        *sent = upto;
+        return ZERO_OK;
+    }
+    uint16_t* dst = nullptr;
+    {
+        std::unique_lock<std::mutex> lk(o->mu);
+        if (!o->rec[b].free_recorded) {
+            if (!block) return ZERO_OK;
+            const auto tw = Clock::now();
+            o->cv.wait(lk, [&] { return o->stop || o->rec[b].free_recorded; });
+            if (!o->rec[b].free_recorded) return ZERO_ESTATE;
+            *wait_release += ms_since(tw);
+        }
+        dst = o->rec[b].param_dst;
+    }
+    if (dst == nullptr) {
+        *sent = upto;
+        return ZERO_OK;
+    }
+    if (!*gated) {
+        if (worker_hip(o, hipStreamWaitEvent(o->xfer, o->ev_free[b], 0), "wait") != ZERO_OK) {
+            return ZERO_EHIP;
+        }
+        *gated = true;
+    }
+    for (int c = *sent; c < upto; ++c) {
+        const int64_t lo = c * o->chunk;
+        const int64_t hi = std::min(p->real, lo + o->chunk);
+        if (hi <= lo) continue;
+        if (worker_hip(o, hipMemcpyAsync(dst + lo, o->hparam[b] + lo,
+                                         2 * static_cast<size_t>(hi - lo),
+                                         hipMemcpyHostToDevice, o->xfer),
+                       "parameter copy") != ZERO_OK) {
+            return ZERO_EHIP;
+        }
+    }
+    *sent = upto;
+    return ZERO_OK;
+}
+
 void worker_main(zero_offload* o) {
     if (worker_hip(o, hipSetDevice(o->device), "hipSetDevice") != ZERO_OK) return;
     const zero_plan* p = o->plan;
+    const size_t esize = static_cast<size_t>(grad_bytes(o->gdt));
     for (int64_t j = 0;; ++j) {
         const int b = static_cast<int>(j & 1);
         auto tw = Clock::now();
@@ -125,11 +192,11 @@ void worker_main(zero_offload* o) {
         }
         const double wait_submit = ms_since(tw);
         tw = Clock::now();
-        if (worker_hip(o, hipEventSynchronize(o->ev_d2h[b]), "gradient copy") != ZERO_OK) return;
-        double wait_grad = ms_since(tw), wait_h2d = 0, wait_release = 0;
+        if (worker_hip(o, hipEventSynchronize(o->ev_slot[b]), "slot copy") != ZERO_OK) return;
+        double wait_grad = ms_since(tw), wait_h2d = 0, wait_release = 0, host_ms = 0;
         const OffloadSlot slot = o->hslot[b];
         bool applied = false;
-        bool sent = false;
+        bool gated = false;
         if (slot.flag == 0) {
             // the pinned parameter buffer b was last sent by step j - 2
             tw = Clock::now();
@@ -139,54 +206,61 @@ void worker_main(zero_offload* o) {
             }
             wait_h2d = ms_since(tw);
             CpuAdamArgs a;
-            a.g = o->hgrad[b];
-            a.p = o->master;
-            a.m = o->m;
-            a.v = o->v;
-            a.param = o->pdt ? o->hparam[b] : nullptr;
-            a.n = p->S;
-            a.real = p->real;
             a.sc = make_scalars(o->hp.lr, o->hp.beta1, o->hp.beta2, o->hp.eps,
                                 o->hp.weight_decay, o->hp.adamw, static_cast<double>(slot.t),
                                 slot.scale);
             a.gdt = o->gdt;
             a.pdt = o->pdt;
             a.adamw = o->hp.adamw != 0;
-            const auto t0 = Clock::now();
-            try {
-                cpu_adam(a, o->n_threads);
-            } catch (const std::exception& ex) {
-                set_worker_error(o, ZERO_ENOMEM, std::string("host update: ") + ex.what());
-                return;
-            }
-            const double ms = ms_since(t0);
-            applied = true;
-            uint16_t* dst = nullptr;
-            {
-                std::unique_lock<std::mutex> lk(o->mu);
-                o->host_ms_last = ms;
-                o->host_ms_total += ms;
+            int sent = 0;
+            for (int c = 0; c < o->n_chunks; ++c) {
+                const int64_t lo = c * o->chunk;
+                const int64_t hi = std::min(p->S, lo + o->chunk);
                 tw = Clock::now();
-                o->cv.wait(lk, [&] { return o->stop || o->rec[b].free_recorded; });
-                if (!o->rec[b].free_recorded) return;
-                wait_release = ms_since(tw);
-                dst = o->rec[b].param_dst;
-            }
-            if (o->pdt != 0 && p->real > 0 && dst != nullptr) {
-                if (worker_hip(o, hipStreamWaitEvent(o->xfer, o->ev_free[b], 0), "wait") !=
-                        ZERO_OK ||
-                    worker_hip(o, hipMemcpyAsync(dst, o->hparam[b], 2 * static_cast<size_t>(p->real),
-                                                 hipMemcpyHostToDevice, o->xfer),
-                               "parameter copy") != ZERO_OK ||
-                    worker_hip(o, hipEventRecord(o->ev_h2d[b], o->xfer), "hipEventRecord") !=
-                        ZERO_OK) {
+                if (worker_hip(o, hipEventSynchronize(o->ev_d2h[b][c]), "gradient copy") !=
+                    ZERO_OK) {
                     return;
                 }
-                sent = true;
+                wait_grad += ms_since(tw);
+                a.g = static_cast<const char*>(o->hgrad[b]) + esize * static_cast<size_t>(lo);
+                a.p = o->master + lo;
+                a.m = o->m + lo;
+                a.v = o->v + lo;
+                a.param = o->pdt ? o->hparam[b] + lo : nullptr;
+                a.n = hi - lo;
+                a.real = std::max<int64_t>(0, std::min(p->real, hi) - lo);
+                const auto t0 = Clock::now();
+                cpu_adam(a, o->n_threads, o->pool);
+                host_ms += ms_since(t0);
+                // this chunk's parameters go back now if the caller has released
+                if (send_params(o, b, c + 1, false, &sent, &gated, &wait_release) != ZERO_OK) {
+                    return;
+                }
             }
+            applied = true;
+            if (send_params(o, b, o->n_chunks, true, &sent, &gated, &wait_release) != ZERO_OK) {
+                return;  // stopped, or a HIP error (recorded)
+            }
+            if (gated &&
+                worker_hip(o, hipEventRecord(o->ev_h2d[b], o->xfer), "hipEventRecord") != ZERO_OK) {
+                return;
+            }
+        } else if (o->n_chunks > 0) {
+            // skipped: nothing reads the gradients, but buffer b is reused (or
+            // freed) once this step counts as processed, so its copies must end
+            tw = Clock::now();
+            if (worker_hip(o, hipEventSynchronize(o->ev_d2h[b][o->n_chunks - 1]),
+                           "gradient copy") != ZERO_OK) {
+                return;
+            }
+            wait_grad += ms_since(tw);
         }
         std::lock_guard<std::mutex> g(o->mu);
-        if (sent) o->h2d_recorded[b] = true;
+        if (gated) o->h2d_recorded[b] = true;
+        if (applied) {
+            o->host_ms_last = host_ms;
+            o->host_ms_total += host_ms;
+        }
         o->wait_submit_ms += wait_submit;
         o->wait_grad_ms += wait_grad;
         o->wait_h2d_ms += wait_h2d;
@@ -249,10 +323,15 @@ void release_all(zero_offload* o) {
         o->worker.join();
     }
     if (o->xfer) (void)hipStreamSynchronize(o->xfer);
+    delete o->pool;
+    o->pool = nullptr;
     for (int b = 0; b < 2; ++b) {
         if (o->hgrad[b]) (void)hipHostFree(o->hgrad[b]);
         if (o->hparam[b]) (void)hipHostFree(o->hparam[b]);
-        if (o->ev_d2h[b]) (void)hipEventDestroy(o->ev_d2h[b]);
+        if (o->ev_slot[b]) (void)hipEventDestroy(o->ev_slot[b]);
+        for (int c = 0; c < kMaxChunks; ++c) {
+            if (o->ev_d2h[b][c]) (void)hipEventDestroy(o->ev_d2h[b][c]);
+        }
         if (o->ev_free[b]) (void)hipEventDestroy(o->ev_free[b]);
         if (o->ev_h2d[b]) (void)hipEventDestroy(o->ev_h2d[b]);
     }
@@ -301,6 +380,20 @@ int zero_offload_create(zero_plan_t* p, const zero_adam_hparams_t* hp, int32_t g
     o->v = exp_avg_sq;
     o->n_threads = n_threads;
     o->device = dev;
+    // copy / update pieces: at least kMinChunkElems each (ZERO_OFFLOAD_MIN_CHUNK
+    // overrides it, down to 64, so tests can cover many pieces on small
+    // shards), at most kMaxChunks
+    if (p->S > 0) {
+        int64_t min_chunk = kMinChunkElems;
+        if (const char* env = std::getenv("ZERO_OFFLOAD_MIN_CHUNK")) {
+            const long long v = std::atoll(env);
+            if (v >= 64) min_chunk = v;
+        }
+        const int64_t want = (p->S + min_chunk - 1) / min_chunk;
+        const int64_t pieces = std::max<int64_t>(1, std::min<int64_t>(kMaxChunks, want));
+        o->chunk = ((p->S + pieces - 1) / pieces + 63) / 64 * 64;
+        o->n_chunks = static_cast<int>((p->S + o->chunk - 1) / o->chunk);
+    }
     const size_t gbytes =
         static_cast<size_t>(grad_bytes(grad_dtype)) * static_cast<size_t>(p->S > 0 ? p->S : 1);
     const size_t pbytes = 2 * static_cast<size_t>(p->real > 0 ? p->real : 1);
@@ -309,7 +402,10 @@ int zero_offload_create(zero_plan_t* p, const zero_adam_hparams_t* hp, int32_t g
         if (e == hipSuccess) {
             e = hipHostMalloc(reinterpret_cast<void**>(&o->hparam[b]), pbytes, hipHostMallocDefault);
         }
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&o->ev_d2h[b], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&o->ev_slot[b], hipEventDisableTiming);
+        for (int c = 0; c < o->n_chunks && e == hipSuccess; ++c) {
+            e = hipEventCreateWithFlags(&o->ev_d2h[b][c], hipEventDisableTiming);
+        }
         if (e == hipSuccess) e = hipEventCreateWithFlags(&o->ev_free[b], hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&o->ev_h2d[b], hipEventDisableTiming);
     }
@@ -326,6 +422,7 @@ int zero_offload_create(zero_plan_t* p, const zero_adam_hparams_t* hp, int32_t g
         return rc == ZERO_EHIP && e == hipErrorOutOfMemory ? ZERO_ENOMEM : rc;
     }
     try {
+        o->pool = new HostPool(n_threads);
         o->worker = std::thread(worker_main, o);
     } catch (const std::exception& ex) {
         release_all(o);
@@ -370,16 +467,21 @@ int zero_offload_submit(zero_offload_t* o, const void* flat_grad, void* param, i
                                                    kStateOffset);
     hipError_t e = launch_offload_snapshot(p->dev.d_flag, st, o->dslot + b, s);
     if (e != hipSuccess) return hip_fail(e, "snapshot launch");
-    if (p->S > 0) {
-        e = hipMemcpyAsync(o->hgrad[b], flat_grad,
-                           static_cast<size_t>(grad_bytes(o->gdt)) * static_cast<size_t>(p->S),
-                           hipMemcpyDeviceToHost, s);
-        if (e != hipSuccess) return hip_fail(e, "gradient copy");
-    }
     e = hipMemcpyAsync(o->hslot + b, o->dslot + b, sizeof(OffloadSlot), hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return hip_fail(e, "slot copy");
-    e = hipEventRecord(o->ev_d2h[b], s);
+    e = hipEventRecord(o->ev_slot[b], s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    const size_t esize = static_cast<size_t>(grad_bytes(o->gdt));
+    for (int c = 0; c < o->n_chunks; ++c) {
+        const int64_t lo = c * o->chunk;
+        const int64_t hi = std::min(p->S, lo + o->chunk);
+        e = hipMemcpyAsync(static_cast<char*>(o->hgrad[b]) + esize * static_cast<size_t>(lo),
+                           static_cast<const char*>(flat_grad) + esize * static_cast<size_t>(lo),
+                           esize * static_cast<size_t>(hi - lo), hipMemcpyDeviceToHost, s);
+        if (e != hipSuccess) return hip_fail(e, "gradient copy");
+        e = hipEventRecord(o->ev_d2h[b][c], s);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
     {
         std::lock_guard<std::mutex> g(o->mu);
         Pending& r = o->rec[b];
