@@ -111,6 +111,29 @@ def test_f32_overflow_skips_and_leaves_state_untouched(isa):
     assert z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, flat, *z0) == 0
 
 
+def test_fp32_subnormals_are_kept(isa):
+    """g*g and the variance in the fp32 subnormal range, a master of subnormals:
+    no flush to zero on any path, bit for bit with the oracle."""
+    n = 4099
+    plan = z.zero_partition_plan([n], 1, 0, 1)
+    rng = np.random.default_rng(9)
+    g = (rng.normal(0, 1e-20, n)).astype(np.float32)
+    m0 = (rng.normal(0, 1e-39, n)).astype(np.float32)
+    tiny = np.finfo(np.float32).tiny
+    assert np.any((np.abs(m0) > 0) & (np.abs(m0) < tiny))
+    gm, gmo, gv = m0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    om, omo, ov = m0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, 4):
+        # lr 1e-25: the master moves by subnormal amounts and stays subnormal
+        assert z.zero_cpu_adam_step(plan, z.AdamHParams(lr=1e-25, weight_decay=0.1), t, 1.0, g,
+                                    gm, gmo, gv, grad_dtype="f32", n_threads=3) == 0
+        assert oracle.adam_step(t, 1.0, g, "f32", om, omo, ov, lr=1e-25, wd=0.1) == 0
+    for x in (ov, om):
+        assert np.any((np.abs(x) > 0) & (np.abs(x) < tiny)), "no fp32 subnormals reached"
+    for a, b in ((gm, om), (gmo, omo), (gv, ov)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 @pytest.mark.parametrize("pdt", ["f16", "bf16"])
 def test_parameter_cast_sweep(isa, pdt):
     """lr = 0 and zero gradients leave the master unchanged, so the written

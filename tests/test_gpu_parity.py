@@ -108,6 +108,37 @@ def test_fp32_gradients_gpt2_small():
     assert worst["bit_exact"]
 
 
+def _has_subnormals(x):
+    import numpy as np
+    a = np.abs(x)
+    return bool(np.any((a > 0) & (a < np.finfo(np.float32).tiny)))
+
+
+@pytest.mark.parametrize("gdt,scale,sigma", [("f32", 1.0, 1e-20), ("f16", 2.0 ** 40, 1e-20),
+                                             ("bf16", 1.0, 1e-20)])
+def test_fp32_subnormals_are_kept(gdt, scale, sigma):
+    """Gradients so small that g*g and the variance are fp32 subnormals, and a
+    master of subnormals: the update must keep them (no flush to zero), as the
+    oracle does, bit for bit."""
+    from harness import GpuRun, OracleRun, compare_state
+    # lr 1e-25: each step moves the master by a subnormal amount, so it stays
+    # subnormal and every step computes on subnormals
+    case = Case(numels=RAGGED, world_size=2, rank=0, grad_dtype=gdt, param_dtype="bf16",
+                steps=3, grad_sigma=sigma, master_sigma=1e-39, init_scale=scale,
+                weight_decay=0.1, adamw=(gdt != "bf16"), lr=1e-25)
+    orc, gpu = OracleRun(case), GpuRun(case)
+    worst = dict(master=0.0, m=0.0, v=0.0, param_ulp=0, bit_exact=True, skipped=0)
+    for it in range(1, case.steps + 1):
+        o_ovf, grads, _ = orc.step(it)
+        g_ovf, _ = gpu.step(it, grads)
+        assert g_ovf == o_ovf == 0
+        compare_state(gpu, orc, worst, f"subnormals {gdt} it={it}")
+    assert _has_subnormals(orc.v) and _has_subnormals(orc.master), \
+        "the case no longer reaches fp32 subnormals"
+    assert worst["bit_exact"]
+    log(f"[parity] subnormals {gdt}: {worst}")
+
+
 def test_gpt2_small_full_shard_all_steps():
     w = get("gpt2_small")
     case = Case.from_workload(w)
