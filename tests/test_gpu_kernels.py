@@ -351,3 +351,48 @@ def test_partial_flatten_makes_the_step_scan(dt):
         assert flag == oflag == (1 if plant else 0)
         assert np.array_equal(master.cpu().numpy().view(np.uint32), om.view(np.uint32))
         assert np.array_equal(va.cpu().numpy().view(np.uint32), ov.view(np.uint32))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_flatten_independent_of_bucket_size_and_order(dt):
+    """The flat shard does not depend on the bucket size (from one element --
+    every tensor its own bucket -- to one bucket for the whole model) or on
+    the order buckets are flattened in."""
+    import torch
+    numels = [5000, 4099, 2048, 3, 70000, 1, 2047, 9000, 4097, 12345, 600, 8191, 0, 77]
+    rng = np.random.default_rng(21)
+    host = [synth.grad_bits(rng.normal(0, 1e-2, n).astype(np.float32), dt) for n in numels]
+    grads = [_to_dev_half(h, dt) for h in host]
+    for r in range(3):
+        expect = None
+        for B in (1, 1000, 1 << 20, 1 << 25, sum(numels)):
+            op = oracle.plan(numels, 3, r, 8, bucket_elems=B)
+            plan = z.zero_partition_plan(numels, 3, r, 8, B)
+            want = oracle.flatten(op, host)
+            if expect is None:
+                expect = want
+            assert np.array_equal(want, expect), (r, B)   # the oracle's own invariance
+            tb = plan.tensor_buckets()
+            for order in (range(plan.n_buckets), reversed(range(plan.n_buckets))):
+                flat = torch.full((op.S,), float("nan"), dtype=torch_dtype(dt), device=DEV)
+                for b in order:
+                    z.zero_flatten_grads(plan, b, [g if tb[i] == b else None
+                                                   for i, g in enumerate(grads)], flat)
+                assert np.array_equal(_bits(flat), expect), (dt, r, B)
+
+
+def test_two_runs_are_bit_identical():
+    """The same case run twice from scratch gives the same bits (no atomics or
+    reductions whose order could change a value)."""
+    case = Case(numels=[3000, 1, 7, 100003, 65, 2048, 511, 300000, 13, 0, 4099, 77777],
+                world_size=3, rank=1, grad_dtype="f16", param_dtype="f16", steps=4,
+                grad_sigma=1e-2, dynamic=True, init_scale=1024.0, window=2, inject={3: 4321},
+                flatten_mode="buckets_shuffled", bucket_elems=50000)
+    states = []
+    for _ in range(2):
+        orc, gpu = OracleRun(case), GpuRun(case)
+        for it in range(1, case.steps + 1):
+            gpu.step(it, orc.step(it)[1])
+        states.append(gpu.state_host())
+    for a, b in zip(*states):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
