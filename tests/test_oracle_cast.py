@@ -1,9 +1,10 @@
 """Pins of the oracle's half <-> fp32 conversions and overflow test (CPU only).
 
-Checked against library conversions (numpy float16, torch bfloat16), which
-implement IEEE 754 round-to-nearest-even, over every half bit pattern and
+Checked against library conversions (numpy float16, torch float16 / bfloat16),
+which implement IEEE 754 round-to-nearest-even, over every half bit pattern,
 over a structured sweep of fp32 patterns that hits every exponent, both
-parities of the last kept bit, exact ties and their neighbours.
+parities of the last kept bit, exact ties and their neighbours, and over all
+2^32 fp32 bit patterns (the last two tests, run in chunks on all cores).
 """
 import numpy as np
 import pytest
@@ -117,3 +118,47 @@ def test_nonfinite_f32_sweep():
         arr = np.zeros(1000, dtype=np.uint32)
         arr[999] = w
         assert oracle.nonfinite(arr, "f32")
+
+
+def _all_2_32(dt, ref_fn):
+    """oracle.float_to_half over all 2^32 fp32 patterns against ref_fn, in
+    2^24-pattern chunks on a thread pool (ctypes and torch release the GIL).
+    Non-NaN inputs must match bit for bit; NaN must give a quiet NaN of the
+    same sign."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    chunk = 1 << 24
+    emask, quiet = (0x7C00, 0x0200) if dt == "f16" else (0x7F80, 0x0040)
+
+    def run(c):
+        u = (np.arange(chunk, dtype=np.uint64) + c * chunk).astype(np.uint32)
+        x = u.view(np.float32)
+        got = oracle.float_to_half(x, dt)
+        ref = ref_fn(x)
+        nan = np.isnan(x)
+        bad = np.flatnonzero((got != ref) & ~nan)
+        gn = got[nan]
+        nan_ok = bool(np.all((gn & emask) == emask) and np.all((gn & quiet) != 0) and
+                      np.array_equal(gn >> 15, (u[nan] >> 31).astype(np.uint16)))
+        return [hex(int(u[i])) for i in bad[:4]], int(bad.size), nan_ok
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with ThreadPoolExecutor(workers) as ex:
+            results = list(ex.map(run, range((1 << 32) // chunk)))
+    finally:
+        torch.set_num_threads(threads)
+    mismatches = sum(r[1] for r in results)
+    assert mismatches == 0, [r[0] for r in results if r[1]][:4]
+    assert all(r[2] for r in results)
+
+
+def test_f32_to_f16_all_2_32_patterns():
+    _all_2_32("f16", lambda x: torch.from_numpy(x).to(torch.float16).view(torch.int16)
+              .numpy().view(np.uint16))
+
+
+def test_f32_to_bf16_all_2_32_patterns():
+    _all_2_32("bf16", _f32_to_bf16_torch)

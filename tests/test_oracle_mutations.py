@@ -100,9 +100,11 @@ def _build(tmp_path, text, name):
 
 def _pins_pass(lib):
     env = dict(os.environ, ZERO_ORACLE_LIB=lib)
+    # the exhaustive 2^32 cast checks are left out here: the structured sweeps
+    # before them catch the rounding mutants in a fraction of the time
     r = subprocess.run([sys.executable, "-m", "pytest", *PIN_FILES, "-x", "-q",
-                        "-p", "no:cacheprovider"], cwd=ROOT, env=env, capture_output=True,
-                       text=True, timeout=900)
+                        "-k", "not all_2_32", "-p", "no:cacheprovider"], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=900)
     return r.returncode == 0, r.stdout[-2000:]
 
 
