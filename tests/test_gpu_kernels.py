@@ -396,3 +396,36 @@ def test_two_runs_are_bit_identical():
         states.append(gpu.state_host())
     for a, b in zip(*states):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_write_param_cast_all_2_32_patterns(dt):
+    """The GPU's fp32 -> half cast (write_param; the fused update uses the same
+    conversion) over all 2^32 fp32 bit patterns, in 2^28-pattern chunks,
+    against the oracle computed beside it on the host's cores: every non-NaN
+    input bit for bit, NaN to a NaN."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    import torch
+    chunk = 1 << 28
+    plan = z.zero_partition_plan([chunk], 1, 0, 1)
+    master = torch.empty(chunk, dtype=torch.float32, device=DEV)
+    param = torch.empty(chunk, dtype=torch_dtype(dt), device=DEV)
+    emask, frac = (0x7C00, 0x03FF) if dt == "f16" else (0x7F80, 0x007F)
+    workers = max(1, min(16, os.cpu_count() or 1))
+    sub = chunk // workers
+    with ThreadPoolExecutor(workers) as ex:
+        for c in range((1 << 32) // chunk):
+            u = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint32)
+            x = u.view(np.float32)
+            master.copy_(torch.from_numpy(x))
+            z.zero_write_param_shard(plan, master, param, 0)
+            got = _bits(param)
+            exp = np.concatenate(list(ex.map(
+                lambda i: oracle.float_to_half(x[i * sub:(i + 1) * sub], dt), range(workers))))
+            nan = np.isnan(x)
+            bad = np.flatnonzero((got != exp) & ~nan)
+            assert bad.size == 0, (dt, [hex(int(u[i])) for i in bad[:4]])
+            gn = got[nan]
+            assert np.all((gn & emask) == emask) and np.all((gn & frac) != 0), (dt, c)
+    log(f"[cast] {dt}: all 2^32 fp32 patterns match the oracle")
