@@ -179,3 +179,51 @@ def test_argument_errors():
     with pytest.raises(ValueError):
         z.zero_cpu_adam_step(plan, z.AdamHParams(), 1, 1.0, g[:10], f, f.copy(), f.copy(),
                              grad_dtype="bf16")
+
+
+@pytest.mark.skipif(os.environ.get("ZERO_EXHAUSTIVE") != "1",
+                    reason="about 4 minutes on 8 cores; set ZERO_EXHAUSTIVE=1 to run")
+@pytest.mark.parametrize("pdt", ["f16", "bf16"])
+def test_parameter_cast_all_2_32_patterns(pdt, monkeypatch):
+    """The host update's half cast on every instruction-set path over all 2^32
+    fp32 patterns (lr = 0 and zero gradients leave the master as it is, so the
+    parameters are its cast), against the oracle computed once per chunk on
+    all cores: every non-NaN input bit for bit, NaN to a NaN.  Opt-in: the
+    4.2M-pattern sweep above covers every sign / exponent / high-fraction
+    pattern with the tie and neighbour low bits of both formats by default."""
+    from concurrent.futures import ThreadPoolExecutor
+    chunk = 1 << 26
+    workers = max(1, min(16, os.cpu_count() or 1))
+    sub = chunk // workers
+    plan = z.zero_partition_plan([chunk], 1, 0, 1)
+    hp = z.AdamHParams(lr=0.0, weight_decay=0.0)
+    flat = np.zeros(chunk, np.uint16)
+    mo = np.zeros(chunk, np.float32)
+    va = np.zeros(chunk, np.float32)
+    param = np.empty(chunk, np.uint16)
+    emask, frac = (0x7C00, 0x03FF) if pdt == "f16" else (0x7F80, 0x007F)
+    isas = [i for i in ISAS if i == "scalar" or _has_isa(i, monkeypatch)]
+    with ThreadPoolExecutor(workers) as ex:
+        for c in range((1 << 32) // chunk):
+            u = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint32)
+            x = u.view(np.float32)
+            exp = np.concatenate(list(ex.map(
+                lambda i: oracle.float_to_half(x[i * sub:(i + 1) * sub], pdt), range(workers))))
+            nan = np.isnan(x)
+            for isa in isas:
+                monkeypatch.setenv("ZERO_CPU_ISA", isa)
+                master = x.copy()
+                assert z.zero_cpu_adam_step(plan, hp, 1, 1.0, flat, master, mo, va, param,
+                                            grad_dtype="bf16", param_dtype=pdt, overflow=0,
+                                            n_threads=workers) == 0
+                bad = np.flatnonzero((param != exp) & ~nan)
+                assert bad.size == 0, (isa, pdt, [hex(int(u[i])) for i in bad[:4]])
+                pn = param[nan]
+                assert np.all((pn & emask) == emask) and np.all((pn & frac) != 0), (isa, c)
+
+
+def _has_isa(isa, monkeypatch):
+    monkeypatch.setenv("ZERO_CPU_ISA", isa)
+    ok = z.zero_cpu_isa() == isa
+    monkeypatch.delenv("ZERO_CPU_ISA")
+    return ok
