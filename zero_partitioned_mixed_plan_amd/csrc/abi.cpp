@@ -64,21 +64,36 @@ int ensure_device(zero_plan* p) {
         }
         return ZERO_OK;
     }
+    // on any failure below, release what was created so a later call starts over
+    auto undo = [&d](hipError_t err, const char* what) {
+        for (int i = 0; i < kTimers; ++i) {
+            if (d.ev_start[i]) (void)hipEventDestroy(d.ev_start[i]);
+            if (d.ev_stop[i]) (void)hipEventDestroy(d.ev_stop[i]);
+            d.ev_start[i] = d.ev_stop[i] = nullptr;
+        }
+        if (d.h_flag) (void)hipHostFree(d.h_flag);
+        if (d.d_flag) (void)hipFree(d.d_flag);
+        d.h_flag = nullptr;
+        d.d_flag = nullptr;
+        return hip_fail(err, what);
+    };
     e = hipMalloc(reinterpret_cast<void**>(&d.d_flag), kBlockBytes);
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(device block)");
+    if (e != hipSuccess) {
+        d.d_flag = nullptr;
+        return undo(e, "hipMalloc(device block)");
+    }
     e = hipHostMalloc(reinterpret_cast<void**>(&d.h_flag), kBlockBytes, hipHostMallocDefault);
     if (e != hipSuccess) {
-        (void)hipFree(d.d_flag);
-        d.d_flag = nullptr;
-        return hip_fail(e, "hipHostMalloc(device block mirror)");
+        d.h_flag = nullptr;
+        return undo(e, "hipHostMalloc(device block mirror)");
     }
     std::memset(d.h_flag, 0, kBlockBytes);
     e = hipMemset(d.d_flag, 0, kBlockBytes);
-    if (e != hipSuccess) return hip_fail(e, "hipMemset(device block)");
+    if (e != hipSuccess) return undo(e, "hipMemset(device block)");
     for (int i = 0; i < kTimers; ++i) {
         e = hipEventCreate(&d.ev_start[i]);
         if (e == hipSuccess) e = hipEventCreate(&d.ev_stop[i]);
-        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        if (e != hipSuccess) return undo(e, "hipEventCreate");
     }
     d.device = dev;
     d.ready = true;
@@ -115,12 +130,11 @@ int param_target(const zero_plan* p, void* param, int64_t base, int64_t numel, i
     if ((reinterpret_cast<uintptr_t>(param) & 1u) != 0) {
         return fail(ZERO_EALIGN, "param must be 2-byte aligned");
     }
-    if (p->real > 0) {
-        if (base < 0 || numel < 0 || p->begin < base || p->begin + p->real - base > numel) {
-            return fail(ZERO_EINVAL, "param window [param_base, param_base + param_numel) must "
-                                     "contain the shard's flat range [shard_begin, shard_begin + "
-                                     "real)");
-        }
+    if (p->real <= 0) return ZERO_OK;  // a shard of padding writes no parameter
+    if (base < 0 || numel < 0 || p->begin < base || p->begin + p->real - base > numel) {
+        return fail(ZERO_EINVAL, "param window [param_base, param_base + param_numel) must "
+                                 "contain the shard's flat range [shard_begin, shard_begin + "
+                                 "real)");
     }
     *out = static_cast<uint16_t*>(param) + (p->begin - base);
     return ZERO_OK;
