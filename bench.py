@@ -257,21 +257,29 @@ def run_offload(w, steps, warmup, device, n_threads):
         for _ in range(warmup):
             step()
         off.drain()
-        s0 = off.stats()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step()
-        off.drain()
-        wall = time.perf_counter() - t0
+        # short steps: time enough of them (>= 0.5 s) that refilling the
+        # pipeline after the drain does not weigh on the average
+        n = steps
+        while True:
+            s0 = off.stats()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                step()
+            off.drain()
+            wall = time.perf_counter() - t0
+            if wall >= 0.5 or n >= 5000:
+                break
+            n = min(5000, max(n + 1, int(n * 0.6 / max(wall, 1e-6))))
         st = off.stats()
-        host_ms = (st["host_ms_total"] - s0["host_ms_total"]) / steps
+        host_ms = (st["host_ms_total"] - s0["host_ms_total"]) / n
         off.close()
-        out[f"lag{lag}"] = {"ms_per_step": wall * 1000.0 / steps, "host_update_ms": host_ms,
-                            "value": real / (wall / steps),
+        out[f"lag{lag}"] = {"timed_steps": n,
+                            "ms_per_step": wall * 1000.0 / n, "host_update_ms": host_ms,
+                            "value": real / (wall / n),
                             "host_update_params_per_s": S / (host_ms * 1e-3),
                             "host_update_gbps": adam_bytes(w.grad_dtype) * S / (host_ms * 1e-3) / 1e9,
                             # per step: where the worker and the caller wait
-                            "waits_ms": {k[:-len("_ms_total")]: (st[k] - s0[k]) / steps
+                            "waits_ms": {k[:-len("_ms_total")]: (st[k] - s0[k]) / n
                                          for k in ("wait_submit_ms_total",
                                                    "wait_grad_ms_total", "wait_h2d_ms_total",
                                                    "wait_release_ms_total",
