@@ -2,8 +2,9 @@
 
 The GPU runs the whole shard exactly as bench.py does (same library calls,
 same launch shapes).  The oracle recomputes fixed windows of the shard --
-its head and tail, +-2048 elements around every segment edge, +-64 around
-every injected +inf, and seeded random windows -- from the host generator;
+its head and tail, +-4096 elements around every segment edge, +-64 around
+every injected +inf, and 16 seeded random windows of 2^20 elements -- from
+the host generator;
 the update is elementwise, so a window evolves exactly as it does inside
 the whole shard.  The overflow decision is global: the windows contain every
 injected position, and the generator's support (|z| <= 2*sqrt(3)) keeps
@@ -32,11 +33,11 @@ pytestmark = pytest.mark.gpu
 HALF_MAX = {"f16": 65504.0, "bf16": 3.3895313892515355e38, "f32": 3.4028234663852886e38}
 
 
-def _windows(op, case, n_random=8, rnd_len=32768, seed=1):
+def _windows(op, case, n_random=16, rnd_len=1 << 20, seed=1):
     S, real = op.S, op.real
     ranges = [(0, 4096), (max(real - 4096, 0), S)]
     for so in op.seg_shard_off.tolist():
-        ranges.append((so - 2048, so + 2048))
+        ranges.append((so - 4096, so + 4096))
     for it in range(1, case.steps + 1):
         pos = case.injection(it, real)
         if pos is not None:
