@@ -221,7 +221,7 @@ class OracleRun:
         return self.param
 
 
-class GpuRun:
+class DeviceRun:
     """The GPU side of a case (small and medium sizes: inputs copied from host).
 
     mode "sync":  zero_adam_step returns the flag; the host runs the scaler.
@@ -315,7 +315,7 @@ def compare_full(case: Case, steps: Optional[int] = None, check_every: int = 1,
     Returns a summary (exact-match flags and the max errors seen)."""
     steps = case.steps if steps is None else steps
     orc = OracleRun(case)
-    gpu = GpuRun(case, mode=mode)
+    gpu = DeviceRun(case, mode=mode)
     assert (gpu.plan.S, gpu.plan.begin, gpu.plan.real) == (orc.plan.S, orc.plan.begin,
                                                            orc.plan.real)
     worst = dict(master=0.0, m=0.0, v=0.0, param_ulp=0, bit_exact=True, skipped=0)
@@ -333,7 +333,7 @@ def compare_full(case: Case, steps: Optional[int] = None, check_every: int = 1,
     return worst
 
 
-def compare_state(gpu: "GpuRun", orc: OracleRun, worst: dict, where: str) -> None:
+def compare_state(gpu: "DeviceRun", orc: OracleRun, worst: dict, where: str) -> None:
     """Compare the GPU's flat shard, master, moments and parameters with the
     oracle's after the same steps; update the worst-error summary."""
     case = orc.case

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import zero_partitioned_mixed_plan_amd as z
-from harness import (Case, GpuRun, OracleRun, compare_full, compare_state, log, to_device_grad,
+from harness import (Case, DeviceRun, OracleRun, compare_full, compare_state, log, to_device_grad,
                      torch_dtype)
 from synth.workloads import get
 
@@ -79,7 +79,7 @@ def _graph_run(case, label, check_every=1):
     device state back and compare with the oracle."""
     import torch
     orc = OracleRun(case)
-    gpu = GpuRun(case, mode="async")
+    gpu = DeviceRun(case, mode="async")
     p = gpu.plan
     gdt = torch_dtype(case.grad_dtype)
     touched = sorted({int(t) for t in orc.plan.seg_tensor})

@@ -9,7 +9,7 @@ import pytest
 import oracle
 import synth
 import zero_partitioned_mixed_plan_amd as z
-from harness import Case, GpuRun, OracleRun, compare_full, log, to_device_grad, torch_dtype
+from harness import Case, DeviceRun, OracleRun, compare_full, log, to_device_grad, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -183,20 +183,20 @@ def test_resume_is_bit_identical():
                 param_dtype="f16", steps=8, dynamic=True, init_scale=512.0, window=3,
                 inject={3: 77})
     orc = OracleRun(case)
-    straight = GpuRun(case)
+    straight = DeviceRun(case)
     grads_per_it = {}
     for it in range(1, 9):
         _, grads, _ = orc.step(it)
         grads_per_it[it] = grads
         straight.step(it, grads)
-    a = GpuRun(case)
+    a = DeviceRun(case)
     for it in range(1, 5):
         a.step(it, grads_per_it[it])
     saved = dict(master=a.master.clone(), m=a.m.clone(), v=a.v.clone(),
                  param=a.param_full.clone(), t=a.t, scale=a.scaler.scale,
                  good=a.scaler.good_steps)
     del a
-    b = GpuRun(case)
+    b = DeviceRun(case)
     b.master.copy_(saved["master"])
     b.m.copy_(saved["m"])
     b.v.copy_(saved["v"])
@@ -257,7 +257,7 @@ def test_timing_entry_points():
     import torch
     case = Case(numels=[1 << 20, 12345], world_size=2, rank=0, grad_dtype="bf16",
                 param_dtype="bf16", steps=1)
-    g = GpuRun(case)
+    g = DeviceRun(case)
     with pytest.raises(z.ZeroError):
         g.plan.kernel_ms(2)
     g.plan.set_timing(True)
@@ -390,7 +390,7 @@ def test_two_runs_are_bit_identical():
                 flatten_mode="buckets_shuffled", bucket_elems=50000)
     states = []
     for _ in range(2):
-        orc, gpu = OracleRun(case), GpuRun(case)
+        orc, gpu = OracleRun(case), DeviceRun(case)
         for it in range(1, case.steps + 1):
             gpu.step(it, orc.step(it)[1])
         states.append(gpu.state_host())

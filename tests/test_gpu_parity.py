@@ -120,13 +120,13 @@ def test_fp32_subnormals_are_kept(gdt, scale, sigma):
     """Gradients so small that g*g and the variance are fp32 subnormals, and a
     master of subnormals: the update must keep them (no flush to zero), as the
     oracle does, bit for bit."""
-    from harness import GpuRun, OracleRun, compare_state
+    from harness import DeviceRun, OracleRun, compare_state
     # lr 1e-25: each step moves the master by a subnormal amount, so it stays
     # subnormal and every step computes on subnormals
     case = Case(numels=RAGGED, world_size=2, rank=0, grad_dtype=gdt, param_dtype="bf16",
                 steps=3, grad_sigma=sigma, master_sigma=1e-39, init_scale=scale,
                 weight_decay=0.1, adamw=(gdt != "bf16"), lr=1e-25)
-    orc, gpu = OracleRun(case), GpuRun(case)
+    orc, gpu = OracleRun(case), DeviceRun(case)
     worst = dict(master=0.0, m=0.0, v=0.0, param_ulp=0, bit_exact=True, skipped=0)
     for it in range(1, case.steps + 1):
         o_ovf, grads, _ = orc.step(it)
