@@ -206,7 +206,7 @@ __device__ __forceinline__ void load_tile(uint64_t src0, u32x4 (&q)[kFlatV]) {
     }
 }
 
-// One workgroup per kFlatTile-element tile of the flat shard.
+// One workgroup per tile of kFlatTile 16-bit words of the flat shard.
 template <int DT>
 __global__ void __launch_bounds__(kThreads)
 flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict__ flag) {
@@ -223,7 +223,7 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
     }
     int p = pl;
     if (p < a.n && a.begin[p] <= lo && a.end[p] >= hi) {
-        // whole tile inside one piece: kFlatV x 8 elements per thread,
+        // whole tile inside one piece: kFlatV x 16 bytes per thread,
         // 16-byte aligned stores, realigned 16-byte loads
         u32x4 q[kFlatV];
         if (!((a.zero_mask >> p) & 1ull)) {
