@@ -51,8 +51,12 @@ int bad_grad_dtype() {
     return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16, ZERO_BF16 or ZERO_F32");
 }
 
-// Binds the plan to the current device on first use and creates its flag.
-int ensure_device(zero_plan* p) {
+// Binds the plan to the current device on first use and creates its device
+// block.  The overflow flag is cleared by a one-thread kernel on the first
+// call that brings a stream (stream-ordered before that call's own work; no
+// memset and nothing on the null stream, so even a captured first call is
+// fine); the rest of the block is written before it is read.
+int ensure_device(zero_plan* p, hipStream_t s, bool have_stream = true) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -61,6 +65,11 @@ int ensure_device(zero_plan* p) {
         if (dev != d.device) {
             return fail(ZERO_ESTATE, "plan is bound to device " + std::to_string(d.device) +
                                          " but device " + std::to_string(dev) + " is current");
+        }
+        if (have_stream && !d.flag_cleared) {
+            e = launch_flag_clear(d.d_flag, s);
+            if (e != hipSuccess) return hip_fail(e, "flag clear");
+            d.flag_cleared = true;
         }
         return ZERO_OK;
     }
@@ -88,12 +97,15 @@ int ensure_device(zero_plan* p) {
         return undo(e, "hipHostMalloc(device block mirror)");
     }
     std::memset(d.h_flag, 0, kBlockBytes);
-    e = hipMemset(d.d_flag, 0, kBlockBytes);
-    if (e != hipSuccess) return undo(e, "hipMemset(device block)");
     for (int i = 0; i < kTimers; ++i) {
         e = hipEventCreate(&d.ev_start[i]);
         if (e == hipSuccess) e = hipEventCreate(&d.ev_stop[i]);
         if (e != hipSuccess) return undo(e, "hipEventCreate");
+    }
+    if (have_stream) {
+        e = launch_flag_clear(d.d_flag, s);
+        if (e != hipSuccess) return undo(e, "flag clear");
+        d.flag_cleared = true;
     }
     d.device = dev;
     d.ready = true;
@@ -321,7 +333,7 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
         pieces.push_back(FlatPiece{g.shard_off, g.shard_off + g.numel, base});
     }
     if (p->S > p->real) pieces.push_back(FlatPiece{p->real, p->S, 0});
-    int rc = ensure_device(p);
+    int rc = ensure_device(p, static_cast<hipStream_t>(stream));
     if (rc != ZERO_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = timer_start(p, kTimerFlatten, s)) != ZERO_OK) return rc;
@@ -371,7 +383,7 @@ int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, 
     uint16_t* param0 = nullptr;
     rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
     if (rc != ZERO_OK) return rc;
-    rc = ensure_device(p);
+    rc = ensure_device(p, static_cast<hipStream_t>(stream));
     if (rc != ZERO_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -409,7 +421,7 @@ int zero_state_upload(zero_plan_t* p, int64_t applied_steps, const zero_scaler_t
     if (applied_steps < 0) return fail(ZERO_EINVAL, "applied_steps must be >= 0");
     int rc = check_scaler(scaler);
     if (rc != ZERO_OK) return rc;
-    rc = ensure_device(p);
+    rc = ensure_device(p, static_cast<hipStream_t>(stream));
     if (rc != ZERO_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // stage in the pinned mirror; the stream is drained before returning, so
@@ -443,7 +455,7 @@ int zero_state_download(zero_plan_t* p, int64_t* applied_steps, zero_scaler_t* s
     if (!p->dev.ready || !p->dev.state_ready) {
         return fail(ZERO_ESTATE, "no device state: call zero_state_upload first");
     }
-    int rc = ensure_device(p);
+    int rc = ensure_device(p, static_cast<hipStream_t>(stream));
     if (rc != ZERO_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* mirror = reinterpret_cast<char*>(p->dev.h_flag);
@@ -495,7 +507,7 @@ int zero_adam_step_async(zero_plan_t* p, const zero_adam_hparams_t* hp, const vo
     if (!p->dev.ready || !p->dev.state_ready) {
         return fail(ZERO_ESTATE, "no device state: call zero_state_upload first");
     }
-    rc = ensure_device(p);
+    rc = ensure_device(p, static_cast<hipStream_t>(stream));
     if (rc != ZERO_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!flatten_covered(p, flat_grad, grad_dtype)) {
@@ -546,7 +558,7 @@ int zero_write_param_shard(zero_plan_t* p, const float* master, void* param, int
     uint16_t* param0 = nullptr;
     int rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
     if (rc != ZERO_OK) return rc;
-    rc = ensure_device(p);
+    rc = ensure_device(p, static_cast<hipStream_t>(stream));
     if (rc != ZERO_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = timer_start(p, kTimerWrite, s)) != ZERO_OK) return rc;
@@ -613,7 +625,7 @@ const char* zero_last_error(void) { return g_last_error.c_str(); }
 int zero_plan_set_timing(zero_plan_t* p, int32_t on) {
     if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");
     if (on) {
-        int rc = ensure_device(p);
+        int rc = ensure_device(p, nullptr, false);
         if (rc != ZERO_OK) return rc;
     }
     p->dev.timing = on != 0;

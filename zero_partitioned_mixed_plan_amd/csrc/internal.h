@@ -115,6 +115,7 @@ __host__ __device__ inline AdamScalars make_scalars(double lr, double beta1, dou
 
 struct DeviceState {
     bool ready = false;
+    bool flag_cleared = false;  // the flag's clear is enqueued (on the first call's stream)
     bool state_ready = false;   // zero_state_upload has run
     int device = -1;
     int* d_flag = nullptr;      // device block: overflow flag at offset 0
