@@ -139,6 +139,23 @@ def test_fp32_subnormals_are_kept(gdt, scale, sigma):
     log(f"[parity] subnormals {gdt}: {worst}")
 
 
+@pytest.mark.parametrize("label,hp", [
+    ("no momentum (beta1 = beta2 = 0)", dict(beta1=0.0, beta2=0.0)),
+    ("lr = 0 (AdamW leaves the master as it is)", dict(lr=0.0)),
+    ("lr = 0, Adam-L2", dict(lr=0.0, adamw=False, weight_decay=0.5)),
+    ("no decay (wd = 0)", dict(weight_decay=0.0)),
+    ("large eps (1.0)", dict(eps=1.0)),
+    ("beta2 close to 1", dict(beta2=0.999999)),
+])
+def test_degenerate_hyperparameters(label, hp):
+    """Boundary settings the update must still compute exactly as the oracle."""
+    base = dict(numels=RAGGED, world_size=2, rank=1, grad_dtype="bf16", param_dtype="bf16",
+                steps=3, grad_sigma=1e-2)
+    base.update(hp)
+    worst = _run(Case(**base), label)
+    assert worst["bit_exact"]
+
+
 def test_gpt2_small_full_shard_all_steps():
     w = get("gpt2_small")
     case = Case.from_workload(w)
