@@ -230,7 +230,6 @@ def run_offload(w, steps, warmup, device, n_threads):
     import numpy as np
     import torch
 
-    import synth
     import zero_partitioned_mixed_plan_amd as z
 
     plan, dmaster, dm, dv, flat, param, grads = setup(w, device)

@@ -10,7 +10,6 @@ read-back) between replays and check every replay.
 """
 import ctypes
 
-import numpy as np
 import pytest
 
 import zero_partitioned_mixed_plan_amd as z

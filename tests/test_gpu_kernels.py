@@ -9,7 +9,7 @@ import pytest
 import oracle
 import synth
 import zero_partitioned_mixed_plan_amd as z
-from harness import Case, DeviceRun, OracleRun, compare_full, log, to_device_grad, torch_dtype
+from harness import Case, DeviceRun, OracleRun, log, to_device_grad, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -178,7 +178,6 @@ def test_write_param_cast_sweep(dt):
 def test_resume_is_bit_identical():
     """k steps, save (master, m, v, t, scale, good_steps), restore into fresh
     buffers and plan, continue: identical to the uninterrupted run."""
-    import torch
     case = Case(numels=[3000, 1, 100003, 65, 4099], world_size=2, rank=0, grad_dtype="f16",
                 param_dtype="f16", steps=8, dynamic=True, init_scale=512.0, window=3,
                 inject={3: 77})

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import zero_partitioned_mixed_plan_amd as z
-from harness import Case, OracleRun, host_model_grads, init_master_host, init_param_host, log, \
+from harness import Case, OracleRun, init_master_host, init_param_host, log, \
     to_device_grad, torch_dtype
 from synth.workloads import get
 
