@@ -9,6 +9,7 @@
 // path exercised here reaches the GPU).  Argument: a workload file, one line
 // per workload: "<name> <R> <A> <B> <n> <numel_0> ... <numel_{n-1}>".
 // Prints "sanitize ok" and exits 0 on success.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -16,6 +17,7 @@
 #include <fstream>
 #include <random>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "internal.h"  // HostPool, cpu_adam (the host update's internals)
@@ -37,7 +39,7 @@ void oracle_float_to_half_n(const float* x, int64_t n, int dt, uint16_t* out);
 
 namespace {
 
-int failures = 0;
+std::atomic<int> failures{0};
 
 #define CHECK(cond, ...)                                  \
     do {                                                  \
@@ -218,6 +220,39 @@ bool check_pool(std::mt19937_64& rng) {
     return true;
 }
 
+// zero_cpu_adam_step from several threads at once, each on its own buffers
+// and with its own thread count: the callers share one kept pool (the others
+// start their own threads), which is recreated when the count changes.  Each
+// result must still equal the oracle's.  Also a pool with more threads than
+// the host has, which does not spin.
+bool check_concurrent_host_steps() {
+    std::vector<std::thread> callers;
+    std::atomic<int> bad{0};
+    for (int c = 0; c < 4; ++c) {
+        callers.emplace_back([c, &bad] {
+            std::mt19937_64 rng(1000 + c);
+            for (int it = 0; it < 6; ++it) {
+                const int64_t n = 1 + static_cast<int64_t>(rng() % 6000);
+                const int threads = 1 + static_cast<int>((c + it) % 3);
+                if (!check_cpu_step(rng, n, 2, it % 2, ZERO_BF16, ZERO_BF16, it % 2, threads,
+                                    it == 3)) {
+                    bad.fetch_add(1);
+                }
+            }
+        });
+    }
+    for (auto& t : callers) t.join();
+    CHECK(bad.load() == 0, "concurrent host steps: %d callers failed", bad.load());
+    const int over = static_cast<int>(std::thread::hardware_concurrency()) + 2;
+    zmi::HostPool pool(over);
+    std::vector<std::atomic<int>> hits(static_cast<size_t>(over));
+    for (int job = 0; job < 20; ++job) pool.run([&](int i) { hits[static_cast<size_t>(i)]++; });
+    for (int i = 0; i < over; ++i) {
+        CHECK(hits[static_cast<size_t>(i)].load() == 20, "oversubscribed pool: index %d", i);
+    }
+    return true;
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -266,8 +301,9 @@ int main(int argc, char** argv) {
             }
         }
     }
+    if (!check_concurrent_host_steps()) return 1;
     if (failures) {
-        std::printf("%d failures\n", failures);
+        std::printf("%d failures\n", failures.load());
         return 1;
     }
     std::printf("sanitize ok: %d workloads, 300 random plans, %d host steps, isa %s\n", workloads,

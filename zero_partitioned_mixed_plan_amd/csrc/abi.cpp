@@ -3,6 +3,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <memory>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -198,6 +200,31 @@ bool flatten_covered(const zero_plan* p, const void* flat_grad, int32_t grad_dty
         }
     }
     return covered;
+}
+
+// Host threads kept for zero_cpu_adam_step across calls (starting threads
+// per call costs about a millisecond on a 16-thread share).  One caller at a
+// time uses it; a concurrent caller starts threads of its own instead.
+std::mutex g_host_pool_mu;
+std::unique_ptr<HostPool> g_host_pool;
+
+// The overflow test (overflow < 0) and the update, on the kept threads when
+// they are free.  Returns 1 when the step is skipped.
+int run_host_step(const CpuAdamArgs& a, int32_t overflow, int n_threads) {
+    std::unique_lock<std::mutex> lk(g_host_pool_mu, std::try_to_lock);
+    HostPool* pool = nullptr;
+    if (lk.owns_lock()) {
+        if (!g_host_pool || g_host_pool->size() != n_threads) {
+            g_host_pool.reset();
+            g_host_pool.reset(new HostPool(n_threads));
+        }
+        pool = g_host_pool.get();
+    }
+    const bool skip =
+        overflow < 0 ? cpu_nonfinite(a.g, a.n, a.gdt, n_threads, pool) : overflow != 0;
+    if (skip) return 1;
+    cpu_adam(a, n_threads, pool);
+    return 0;
 }
 
 void reset_flatten_bookkeeping(zero_plan* p) {
@@ -594,11 +621,8 @@ int zero_cpu_adam_step(const zero_plan_t* p, const zero_adam_hparams_t* hp, int6
     uint16_t* param0 = nullptr;
     rc = param_target(p, param, param_base, param_numel, param_dtype, &param0);
     if (rc != ZERO_OK) return rc;
-    const void* g = flat_grad;
-    const bool skip = overflow < 0 ? cpu_nonfinite(g, p->S, grad_dtype, n_threads) : overflow != 0;
-    if (skip) return 1;
     CpuAdamArgs a;
-    a.g = g;
+    a.g = flat_grad;
     a.p = master;
     a.m = exp_avg;
     a.v = exp_avg_sq;
@@ -611,11 +635,10 @@ int zero_cpu_adam_step(const zero_plan_t* p, const zero_adam_hparams_t* hp, int6
     a.pdt = param_dtype;
     a.adamw = hp->adamw != 0;
     try {
-        cpu_adam(a, n_threads);
+        return run_host_step(a, overflow, n_threads);
     } catch (const std::exception& ex) {
         return fail(ZERO_ENOMEM, std::string("host update failed: ") + ex.what());
     }
-    return 0;
 }
 
 const char* zero_cpu_isa(void) { return cpu_isa_name(cpu_isa()); }

@@ -25,6 +25,7 @@
 #include <immintrin.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -451,14 +452,26 @@ void parallel_ranges(int64_t n, int n_threads, HostPool* pool, Fn fn) {
 
 }  // namespace
 
-HostPool::HostPool(int n_threads) : n_(n_threads < 1 ? 1 : n_threads) {
+namespace {
+// How long idle pool threads, and a caller waiting for them, spin before
+// sleeping on the condition variable.  A pool with more threads than the
+// host has hardware threads does not spin: there a spinning thread takes
+// the core from one that has work.
+constexpr auto kSpin = std::chrono::microseconds(50);
+}  // namespace
+
+HostPool::HostPool(int n_threads)
+    : n_(n_threads < 1 ? 1 : n_threads),
+      spin_(static_cast<unsigned>(n_) <= std::max(1u, std::thread::hardware_concurrency())
+                ? std::chrono::duration_cast<std::chrono::nanoseconds>(kSpin)
+                : std::chrono::nanoseconds(0)) {
     threads_.reserve(static_cast<size_t>(n_ - 1));
     try {
         for (int i = 1; i < n_; ++i) threads_.emplace_back(&HostPool::worker, this, i);
     } catch (...) {
         {
             std::lock_guard<std::mutex> g(mu_);
-            stop_ = true;
+            stop_.store(true);
         }
         go_.notify_all();
         for (auto& t : threads_) t.join();
@@ -469,7 +482,7 @@ HostPool::HostPool(int n_threads) : n_(n_threads < 1 ? 1 : n_threads) {
 HostPool::~HostPool() {
     {
         std::lock_guard<std::mutex> g(mu_);
-        stop_ = true;
+        stop_.store(true);
     }
     go_.notify_all();
     for (auto& t : threads_) t.join();
@@ -478,34 +491,45 @@ HostPool::~HostPool() {
 void HostPool::worker(int idx) {
     uint64_t seen = 0;
     for (;;) {
-        const std::function<void(int)>* job;
-        {
-            std::unique_lock<std::mutex> lk(mu_);
-            go_.wait(lk, [&] { return stop_ || gen_ != seen; });
-            if (stop_) return;
-            seen = gen_;
-            job = job_;
+        // a new job is published by bumping gen_ (under mu_, after job_)
+        const auto t0 = std::chrono::steady_clock::now();
+        while (gen_.load(std::memory_order_acquire) == seen &&
+               !stop_.load(std::memory_order_acquire) &&
+               std::chrono::steady_clock::now() - t0 < spin_) {
+            _mm_pause();
         }
-        (*job)(idx);
-        {
+        if (gen_.load(std::memory_order_acquire) == seen) {
+            std::unique_lock<std::mutex> lk(mu_);
+            go_.wait(lk, [&] { return stop_.load() || gen_.load() != seen; });
+        }
+        if (stop_.load(std::memory_order_acquire)) return;
+        seen = gen_.load(std::memory_order_acquire);
+        (*job_.load(std::memory_order_acquire))(idx);
+        if (pending_.fetch_sub(1, std::memory_order_acq_rel) == 1) {
             std::lock_guard<std::mutex> g(mu_);
-            if (--pending_ == 0) done_.notify_all();
+            done_.notify_all();
         }
     }
 }
 
 void HostPool::run(const std::function<void(int)>& fn) {
+    job_.store(&fn, std::memory_order_release);
+    pending_.store(n_ - 1, std::memory_order_release);
     {
         std::lock_guard<std::mutex> g(mu_);
-        job_ = &fn;
-        pending_ = n_ - 1;
-        ++gen_;
+        gen_.fetch_add(1, std::memory_order_acq_rel);
     }
     go_.notify_all();
     fn(0);
-    std::unique_lock<std::mutex> lk(mu_);
-    done_.wait(lk, [&] { return pending_ == 0; });
-    job_ = nullptr;
+    const auto t0 = std::chrono::steady_clock::now();
+    while (pending_.load(std::memory_order_acquire) != 0 &&
+           std::chrono::steady_clock::now() - t0 < spin_) {
+        _mm_pause();
+    }
+    if (pending_.load(std::memory_order_acquire) != 0) {
+        std::unique_lock<std::mutex> lk(mu_);
+        done_.wait(lk, [&] { return pending_.load() == 0; });
+    }
 }
 
 const char* cpu_isa_name(CpuIsa isa) {
@@ -518,14 +542,15 @@ const char* cpu_isa_name(CpuIsa isa) {
 
 CpuIsa cpu_isa() { return detect_isa(); }
 
-bool cpu_nonfinite(const void* g, int64_t n, int gdt, int n_threads) {
+bool cpu_nonfinite(const void* g, int64_t n, int gdt, int n_threads, HostPool* pool) {
     if (n <= 0) return false;
     const bool f32 = gdt == ZERO_F32;
     const uint32_t mask = f32 ? kF32ExpMask : gdt == ZERO_F16 ? kF16ExpMask : kBf16ExpMask;
     const CpuIsa isa = detect_isa();
+    if (pool != nullptr) n_threads = pool->size();
     std::vector<char> hit(static_cast<size_t>(std::max(n_threads, 1)) + 1, 0);
     const int64_t chunk = range_chunk(n, std::max(n_threads, 1));
-    parallel_ranges(n, n_threads, nullptr, [&](int64_t lo, int64_t hi) {
+    parallel_ranges(n, n_threads, pool, [&](int64_t lo, int64_t hi) {
         bool bad;
         if (isa == CpuIsa::kAvx512) bad = nonfinite_avx512(g, lo, hi, mask, f32);
         else if (isa == CpuIsa::kAvx2) bad = nonfinite_avx2(g, lo, hi, mask, f32);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <functional>
@@ -210,7 +212,9 @@ struct CpuAdamArgs {
 
 // A fixed set of host threads that runs one job at a time: run(fn) calls
 // fn(i) for i in [0, size()) -- i = 0 on the calling thread -- and returns
-// when all have finished.  One caller at a time.
+// when all have finished.  One caller at a time.  Idle threads (and a
+// waiting caller) spin for a short while before sleeping, so jobs that come
+// back to back do not pay a wake-up each; an oversubscribed pool does not spin.
 class HostPool {
 public:
     explicit HostPool(int n_threads);
@@ -223,20 +227,21 @@ public:
 private:
     void worker(int idx);
     int n_;
+    std::chrono::nanoseconds spin_;
     std::vector<std::thread> threads_;
     std::mutex mu_;
     std::condition_variable go_, done_;
-    const std::function<void(int)>* job_ = nullptr;
-    uint64_t gen_ = 0;
-    int pending_ = 0;
-    bool stop_ = false;
+    std::atomic<const std::function<void(int)>*> job_{nullptr};
+    std::atomic<uint64_t> gen_{0};
+    std::atomic<int> pending_{0};
+    std::atomic<bool> stop_{false};
 };
 
 CpuIsa cpu_isa();
 const char* cpu_isa_name(CpuIsa isa);
 // pool == nullptr: n_threads threads are started for this call.
 void cpu_adam(const CpuAdamArgs& a, int n_threads, HostPool* pool = nullptr);
-bool cpu_nonfinite(const void* g, int64_t n, int gdt, int n_threads);
+bool cpu_nonfinite(const void* g, int64_t n, int gdt, int n_threads, HostPool* pool = nullptr);
 
 // Bytes per gradient element.
 inline int grad_bytes(int gdt) { return gdt == ZERO_F32 ? 4 : 2; }
