@@ -303,8 +303,9 @@ int zero_adam_step_async(zero_plan_t* plan, const zero_adam_hparams_t* hp, const
  * overflow: 1 = skip (nothing written), 0 = apply, -1 = test flat_grad for
  * inf/NaN here first.  n_threads (1..1024): host threads, taken from a pool
  * the library keeps between calls (a call made while another one holds that
- * pool starts threads of its own); the result does not depend on it.  Calls
- * on disjoint buffers may run concurrently.  Returns 0 applied, 1 skipped, or a negative error
+ * pool starts threads of its own; a process made by fork() builds a pool of
+ * its own); the result does not depend on it.  Calls on disjoint buffers
+ * may run concurrently.  Returns 0 applied, 1 skipped, or a negative error
  * (ZERO_ENULL, ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOMEM).  Needs no GPU. */
 int zero_cpu_adam_step(const zero_plan_t* plan, const zero_adam_hparams_t* hp, int64_t step,
                        double loss_scale, const void* flat_grad, int32_t grad_dtype,

@@ -227,3 +227,53 @@ def _has_isa(isa, monkeypatch):
     ok = z.zero_cpu_isa() == isa
     monkeypatch.delenv("ZERO_CPU_ISA")
     return ok
+
+
+
+def _forked_host_step(conn, flats):
+    """Runs in a child made by fork(): repeat the parent's host steps and
+    send back the resulting state."""
+    try:
+        conn.send(_pool_steps(flats))
+    finally:
+        conn.close()
+
+
+def _pool_steps(flats):
+    plan = z.zero_partition_plan([flats[0].size], 1, 0, 1)
+    master = np.random.default_rng(5).normal(0, 0.02, plan.S).astype(np.float32)
+    mo, v = np.zeros_like(master), np.zeros_like(master)
+    param = np.zeros(plan.S, np.uint16)
+    for t, (flat, threads) in enumerate(zip(flats, (4, 4, 2)), 1):
+        assert z.zero_cpu_adam_step(plan, z.AdamHParams(), t, 1.0, flat, master, mo, v, param,
+                                    grad_dtype="bf16", param_dtype="bf16",
+                                    n_threads=threads) == 0
+    return master.view(np.uint32), mo.view(np.uint32), v.view(np.uint32), param
+
+
+def test_host_step_in_a_forked_child():
+    # The library keeps a pool of host threads between calls.  A child made
+    # by fork() inherits that pool without its threads: it must build its
+    # own (not wait on threads that are not there) and compute the same.
+    # The child makes no torch call (torch's own threads do not survive a
+    # fork either); the gradients are drawn here.
+    import multiprocessing as mp
+    rng = np.random.default_rng(6)
+    flats = [_grads(rng, 70001, "bf16", 1.0) for _ in range(3)]
+    want = _pool_steps(flats)     # the parent now holds a 2-thread pool
+    ctx = mp.get_context("fork")
+    parent, child = ctx.Pipe(duplex=False)
+    proc = ctx.Process(target=_forked_host_step, args=(child, flats))
+    proc.start()
+    child.close()
+    try:
+        assert parent.poll(60), "host step in the forked child did not finish"
+        got = parent.recv()
+    finally:
+        proc.join(10)
+        if proc.is_alive():
+            proc.kill()
+            proc.join()
+    assert proc.exitcode == 0
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)

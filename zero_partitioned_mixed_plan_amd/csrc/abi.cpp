@@ -3,10 +3,11 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
-#include <memory>
 #include <mutex>
 #include <new>
 #include <string>
+
+#include <unistd.h>
 
 #include "internal.h"
 
@@ -205,8 +206,13 @@ bool flatten_covered(const zero_plan* p, const void* flat_grad, int32_t grad_dty
 // Host threads kept for zero_cpu_adam_step across calls (starting threads
 // per call costs about a millisecond on a 16-thread share).  One caller at a
 // time uses it; a concurrent caller starts threads of its own instead.
+// The pool is never destroyed at exit, and a process made by fork() does not
+// use the one it inherited: that copy's threads were not copied, so joining
+// or waiting for them would never end.  A child that inherits the mutex
+// locked only ever starts threads of its own.
 std::mutex g_host_pool_mu;
-std::unique_ptr<HostPool> g_host_pool;
+HostPool* g_host_pool = nullptr;
+pid_t g_host_pool_pid = 0;
 
 // The overflow test (overflow < 0) and the update, on the kept threads when
 // they are free.  Returns 1 when the step is skipped.
@@ -214,11 +220,16 @@ int run_host_step(const CpuAdamArgs& a, int32_t overflow, int n_threads) {
     std::unique_lock<std::mutex> lk(g_host_pool_mu, std::try_to_lock);
     HostPool* pool = nullptr;
     if (lk.owns_lock()) {
-        if (!g_host_pool || g_host_pool->size() != n_threads) {
-            g_host_pool.reset();
-            g_host_pool.reset(new HostPool(n_threads));
+        if (g_host_pool != nullptr && g_host_pool_pid != getpid()) g_host_pool = nullptr;
+        if (g_host_pool != nullptr && g_host_pool->size() != n_threads) {
+            delete g_host_pool;
+            g_host_pool = nullptr;
         }
-        pool = g_host_pool.get();
+        if (g_host_pool == nullptr) {
+            g_host_pool = new HostPool(n_threads);
+            g_host_pool_pid = getpid();
+        }
+        pool = g_host_pool;
     }
     const bool skip =
         overflow < 0 ? cpu_nonfinite(a.g, a.n, a.gdt, n_threads, pool) : overflow != 0;
