@@ -39,7 +39,6 @@ int check_hparams(const zero_adam_hparams_t* hp) {
     return ZERO_OK;
 }
 
-
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

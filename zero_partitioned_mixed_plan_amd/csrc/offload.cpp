@@ -54,17 +54,13 @@ struct Pending {
     bool applied = false;
 };
 
+constexpr int kMaxChunks = 16;                       // gradient / parameter copy pieces
+constexpr int64_t kMinChunkElems = int64_t(1) << 25;  // per piece (64-128 MB of gradients)
+
 }  // namespace
 }  // namespace zmi
 
 using namespace zmi;
-
-namespace zmi {
-namespace {
-constexpr int kMaxChunks = 16;                       // gradient / parameter copy pieces
-constexpr int64_t kMinChunkElems = int64_t(1) << 25;  // per piece (64-128 MB of gradients)
-}  // namespace
-}  // namespace zmi
 
 struct zero_offload {
     zero_plan* plan = nullptr;
@@ -571,16 +567,24 @@ void zero_offload_destroy(zero_offload_t* o) {
     int cur = -1;
     (void)hipGetDevice(&cur);
     if (cur != o->device) (void)hipSetDevice(o->device);
-    // let the worker finish what was submitted, then stop it
+    // let the worker finish what was submitted, then stop it; if a release
+    // point cannot be recorded, stop it at once (it would wait for that
+    // release forever)
     {
         std::unique_lock<std::mutex> lk(o->mu);
         for (int b = 0; b < 2; ++b) {
             if (o->rec[b].idx >= 0 && !o->rec[b].free_recorded) {
-                if (hipEventRecord(o->ev_free[b], nullptr) == hipSuccess) o->rec[b].free_recorded = true;
+                if (hipEventRecord(o->ev_free[b], nullptr) == hipSuccess) {
+                    o->rec[b].free_recorded = true;
+                } else {
+                    o->stop = true;
+                }
             }
         }
         o->cv.notify_all();
-        o->cv.wait(lk, [&] { return o->err != ZERO_OK || o->processed >= o->submitted; });
+        o->cv.wait(lk, [&] {
+            return o->stop || o->err != ZERO_OK || o->processed >= o->submitted;
+        });
     }
     release_all(o);
     if (cur != o->device && cur >= 0) (void)hipSetDevice(cur);
