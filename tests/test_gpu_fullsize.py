@@ -1,4 +1,5 @@
-"""GPU vs oracle parity at the workloads' full sizes, on sampled windows.
+"""GPU vs oracle parity at the workloads' full sizes (and one tensor past 2^31
+elements), on sampled windows.
 
 The GPU runs the whole shard exactly as bench.py does (same library calls,
 same launch shapes).  The oracle recomputes fixed windows of the shard --
@@ -193,3 +194,20 @@ def test_llama2_70b_rank7_full_shard():
         pytest.skip(f"needs ~160 GB of free device memory, {free / 1e9:.0f} GB free")
     case = Case.from_workload(get("llama2_70b"))
     _run_sampled(case, check_at={1, 3}, label="llama2_70b")
+
+
+def test_tensor_beyond_2_31_elements():
+    # Rank 1 of 2 over tensors of 3, 4,999,999,990 and 7 elements: the shard
+    # starts 2,499,999,997 elements into the middle tensor (past 2^31, and 10
+    # bytes past a 16-byte boundary), so the flatten's source offsets need 64
+    # bits and take the realigned path; the 7-element tensor puts a piece
+    # edge inside the last tile.  The +inf of iteration 2 sits past 2^31 in
+    # the shard.  About 50 GB of device memory.
+    import torch
+    free, _ = torch.cuda.mem_get_info()
+    if free < 60e9:
+        pytest.skip(f"needs ~50 GB of free device memory, {free / 1e9:.0f} GB free")
+    case = Case(numels=[3, 4_999_999_990, 7], world_size=2, rank=1, grad_dtype="bf16",
+                param_dtype="bf16", steps=3, inject={2: 2_300_000_000})
+    skipped = _run_sampled(case, check_at={1, 3}, label="5e9-element tensor")
+    assert skipped == 1
