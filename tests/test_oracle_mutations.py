@@ -101,9 +101,13 @@ def _build(tmp_path, text, name):
 def _pins_pass(lib):
     env = dict(os.environ, ZERO_ORACLE_LIB=lib)
     # the exhaustive 2^32 cast checks are left out here: the structured sweeps
-    # before them catch the rounding mutants in a fraction of the time
+    # before them catch the rounding mutants in a fraction of the time.  So is
+    # the GPT-2-small partitioned-equals-unpartitioned check (about 40 s): the
+    # same invariant runs on the tiny model in every run, and no change to
+    # the arithmetic can break it.
     r = subprocess.run([sys.executable, "-m", "pytest", *PIN_FILES, "-x", "-q",
-                        "-k", "not all_2_32", "-p", "no:cacheprovider"], cwd=ROOT, env=env,
+                        "-k", "not all_2_32 and not gpt2_small", "-p", "no:cacheprovider"],
+                       cwd=ROOT, env=env,
                        capture_output=True, text=True, timeout=900)
     return r.returncode == 0, r.stdout[-2000:]
 

@@ -133,10 +133,9 @@ def _run_partitioned(numels, R, grads_per_step, pdt, gdt, scale, steps, A=8):
     P = sum(numels)
     param = np.zeros(P, np.uint16)
     masters = []
+    full_master = np.random.default_rng(1000).normal(0, 0.02, P).astype(np.float32)
     for r in range(R):
         p = oracle.plan(numels, R, r, A)
-        rng = np.random.default_rng(1000)
-        full_master = rng.normal(0, 0.02, P).astype(np.float32)
         master = np.zeros(p.S, np.float32)
         master[:p.real] = full_master[p.begin:p.begin + p.real]
         m = np.zeros(p.S, np.float32)
@@ -163,6 +162,24 @@ def test_partitioned_step_equals_unpartitioned(R):
     assert np.array_equal(part_param, full_param)
     assert np.array_equal(part_master.view(np.uint32), full_master.view(np.uint32))
     assert part_master.size == sum(numels)
+
+
+def test_partitioned_gpt2_small_equals_unpartitioned():
+    # the same invariant at GPT-2-small's 148 tensors over 8 ranks (A = 64,
+    # bf16): rank 0's shard lies inside the token embedding, the others cut
+    # through the layers.  One step (the tiny case above takes three): the
+    # invariant is about where each element lives, not about t.
+    w = get("gpt2_small")
+    rng = np.random.default_rng(6)
+    steps = 1
+    grads = [_model_grads(w.numels, rng, "bf16") for _ in range(steps)]
+    part_param, part_master = _run_partitioned(w.numels, 8, grads, "bf16", "bf16", 1.0, steps,
+                                               A=64)
+    full_param, full_master = _run_partitioned(w.numels, 1, grads, "bf16", "bf16", 1.0, steps,
+                                               A=64)
+    assert part_master.size == sum(w.numels) == 124_439_808
+    assert np.array_equal(part_param, full_param)
+    assert np.array_equal(part_master.view(np.uint32), full_master.view(np.uint32))
 
 
 @pytest.mark.parametrize("pdt", ["f16", "bf16"])
