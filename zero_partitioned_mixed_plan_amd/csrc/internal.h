@@ -166,7 +166,7 @@ struct FlatPiece {
     uintptr_t src_base;
 };
 
-constexpr int kMaxPiecesPerLaunch = 64;
+constexpr int kMaxPiecesPerLaunch = 96;
 
 hipError_t launch_flatten(const FlatPiece* pieces, int n, void* flat, int* flag, int grad_dtype,
                           hipStream_t s);

@@ -139,11 +139,13 @@ struct FlattenArgs {
     int64_t n_tiles;
     int32_t n;           // pieces, sorted by begin, disjoint
     int32_t _pad;
-    uint64_t zero_mask;  // bit i: piece i is zero fill
+    uint64_t zero_mask[2];  // bit i % 64 of word i / 64: piece i is zero fill
     int64_t begin[kMaxPiecesPerLaunch];
     int64_t end[kMaxPiecesPerLaunch];
     uint64_t src[kMaxPiecesPerLaunch];  // byte address of flat word 0's source
 };
+static_assert(kMaxPiecesPerLaunch <= 128, "zero_mask holds 128 pieces");
+static_assert(sizeof(FlattenArgs) <= 4096, "flatten kernel arguments");
 
 // 16 source bytes starting MIS bytes into the aligned pair (a, b).
 template <int MIS>
@@ -226,7 +228,7 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
         // whole tile inside one piece: kFlatV x 16 bytes per thread,
         // 16-byte aligned stores, realigned 16-byte loads
         u32x4 q[kFlatV];
-        if (!((a.zero_mask >> p) & 1ull)) {
+        if (!((a.zero_mask[p >> 6] >> (p & 63)) & 1ull)) {
             load_tile(a.src[p] + 2ull * static_cast<uint64_t>(lo), q);
 #pragma unroll
             for (int j = 0; j < kFlatV; ++j) bad |= vec_nonfinite<DT>(q[j]);
@@ -242,7 +244,7 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
         for (; p < a.n && a.begin[p] < hi; ++p) {
             const int64_t s0 = a.begin[p] > lo ? a.begin[p] : lo;
             const int64_t s1 = a.end[p] < hi ? a.end[p] : hi;
-            const bool zero = (a.zero_mask >> p) & 1ull;
+            const bool zero = (a.zero_mask[p >> 6] >> (p & 63)) & 1ull;
             if (DT == ZERO_F32) {
                 // piece edges are even words (element edges): 4-byte elements
                 auto* flat32 = reinterpret_cast<uint32_t*>(flat);
@@ -464,12 +466,12 @@ hipError_t launch_flatten(const FlatPiece* pieces, int n, void* flat, int* flag,
     const int64_t words = grad_dtype == ZERO_F32 ? 2 : 1;
     FlattenArgs a{};
     a.n = n;
-    a.zero_mask = 0;
+    a.zero_mask[0] = a.zero_mask[1] = 0;
     for (int i = 0; i < n; ++i) {
         a.begin[i] = pieces[i].begin * words;
         a.end[i] = pieces[i].end * words;
         a.src[i] = pieces[i].src_base;
-        if (pieces[i].src_base == 0) a.zero_mask |= 1ull << i;
+        if (pieces[i].src_base == 0) a.zero_mask[i >> 6] |= 1ull << (i & 63);
     }
     const int64_t lo = a.begin[0], hi = a.end[n - 1];
     a.tile_first = lo / kFlatTile;
