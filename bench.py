@@ -223,10 +223,41 @@ def time_standalone_kernels(bufs):
     return write_ms, scan_ms
 
 
-def run_offload(w, steps, warmup, device, n_threads):
+def forward_stand_in(forward_ms, device):
+    """A fixed amount of GPU work that stands in for a step's forward and
+    backward passes: a chain of 8192 x 8192 x 8192 bf16 products on the
+    current stream, sized from a timed sample to take about forward_ms.
+    Returns (run, gemms, measured ms per run)."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device=device, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=device, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=device, dtype=torch.bfloat16)
+
+    def gemms(k):
+        for _ in range(k):
+            torch.mm(a, b, out=c)
+
+    def timed(k):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gemms(k)
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1)
+
+    gemms(3)
+    per = timed(20) / 20
+    k = max(1, round(forward_ms / per))
+    return (lambda: gemms(k)), k, timed(k)
+
+
+def run_offload(w, steps, warmup, device, n_threads, forward_ms=0.0):
     """ZeRO-Offload: fp32 master / moments in host memory, the update on the
     host cores, gradients and parameters crossing PCIe; timed with the
-    one-step delayed update (lag 1) and serialised (lag 0)."""
+    one-step delayed update (lag 1) and serialised (lag 0).  forward_ms > 0
+    puts a stand-in for the forward and backward passes on the GPU before
+    each step, which the delayed update overlaps with the host update."""
     import numpy as np
     import torch
 
@@ -241,6 +272,12 @@ def run_offload(w, steps, warmup, device, n_threads):
     torch.cuda.empty_cache()
     hp = z.AdamHParams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.adamw)
     out = {"isa": z.zero_cpu_isa(), "host_threads": n_threads}
+    forward = None
+    if forward_ms > 0:
+        forward, k, measured = forward_stand_in(forward_ms, device)
+        out["forward"] = {"what": "8192^3 bf16 torch.mm chain before each step, standing in "
+                                  "for the forward and backward passes",
+                          "gemms_per_step": k, "ms_alone": measured}
     for lag in (1, 0):
         m = np.zeros(S, np.float32)
         v = np.zeros(S, np.float32)
@@ -250,6 +287,8 @@ def run_offload(w, steps, warmup, device, n_threads):
 
         def step():
             off.wait_params(lag)
+            if forward is not None:
+                forward()
             z.zero_flatten_grads(plan, -1, grads, flat)
             off.submit(flat, param, begin)
 
@@ -487,6 +526,10 @@ def main(argv=None):
                     help="threads of the offload host update (default: the usable CPUs "
                          "less one, which the caller and the HIP runtime need while the "
                          "delayed update runs)")
+    ap.add_argument("--forward-ms", type=float, default=0.0,
+                    help="offload mode: run about this many ms of bf16 products on the GPU "
+                         "before each step, a stand-in for the forward and backward passes "
+                         "that the one-step delayed update overlaps")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run only a plain copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
@@ -513,7 +556,7 @@ def main(argv=None):
         w = dataclasses.replace(w, grad_dtype=args.grad_dtype)
     if args.mode == "offload":
         threads = args.host_threads or max(1, host_info()["usable_cpus"] - 1)
-        plan, res = run_offload(w, args.steps, args.warmup, device, threads)
+        plan, res = run_offload(w, args.steps, args.warmup, device, threads, args.forward_ms)
         print(json.dumps({
             "metric": METRIC, "value": res["lag1"]["value"], "unit": "params/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["lag1"]["ms_per_step"],
