@@ -44,6 +44,8 @@ def adam_bytes(gdt: str) -> int:
 
 def flatten_bytes(gdt: str) -> int:
     return 2 * GRAD_BYTES[gdt]
+
+
 METRIC = "shard params/sec per Adam step + achieved HBM GB/s (% of peak), 1 GPU"
 
 
