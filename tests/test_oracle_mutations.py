@@ -29,6 +29,16 @@ MUTATIONS = [
      "float c_step = (float)(lr / (1.0 - pow(b1, (double)t)));", "float c_step = (float)lr;"),
     ("bias correction of v dropped",
      "float c_rsbc2 = (float)(1.0 / sqrt(1.0 - pow(b2, (double)t)));", "float c_rsbc2 = 1.0f;"),
+    ("bias correction of v without its square root",
+     "float c_rsbc2 = (float)(1.0 / sqrt(1.0 - pow(b2, (double)t)));",
+     "float c_rsbc2 = (float)(1.0 / (1.0 - pow(b2, (double)t)));"),
+    ("bias correction of m one step ahead",
+     "float c_step = (float)(lr / (1.0 - pow(b1, (double)t)));",
+     "float c_step = (float)(lr / (1.0 - pow(b1, (double)(t + 1))));"),
+    ("momentum weighs the gradient by beta1",
+     "float c_omb1 = (float)(1.0 - b1);", "float c_omb1 = (float)b1;"),
+    ("decoupled decay applied to the updated weight",
+     "p = p * c_decay - c_step * u;", "p = (p - c_step * u) * c_decay;"),
     ("eps inside the square root",
      "float d = sqrtf(vk) * c_rsbc2 + c_eps;", "float d = sqrtf(vk + c_eps) * c_rsbc2;"),
     ("decoupled decay with the wrong sign",
