@@ -137,3 +137,26 @@ def test_offload_in_many_pieces(lag, monkeypatch):
 def test_offload_gpt2_small():
     case = Case.from_workload(get("gpt2_small"), steps=6)
     _offload_run(case, 1, "gpt2_small", n_threads=8)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_offload_random_configuration(seed, monkeypatch):
+    """The seeded random configurations of the device parity sweep, through
+    the offload pipeline, with a random lag, parameter write-back or not,
+    1-6 host threads and a random piece size (so 1 to 16 pieces)."""
+    import random
+
+    from test_gpu_random_parity import random_case
+    rnd = random.Random(10_000 + seed)
+    case = random_case(seed)
+    lag = rnd.choice([0, 1])
+    write_params = rnd.random() < 0.8
+    threads = rnd.randint(1, 6)
+    piece = rnd.choice([64, 256, 4096, None])
+    if piece is not None:
+        monkeypatch.setenv("ZERO_OFFLOAD_MIN_CHUNK", str(piece))
+    label = (f"offload random seed={seed} numels={case.numels} R={case.world_size} "
+             f"r={case.rank} A={case.align} grads={case.grad_dtype} params={case.param_dtype} "
+             f"adamw={case.adamw} inject_p={case.inject_p} lag={lag} write={write_params} "
+             f"threads={threads} piece={piece}")
+    _offload_run(case, lag, label, write_params=write_params, n_threads=threads)
