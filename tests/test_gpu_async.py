@@ -91,7 +91,13 @@ def _graph_run(case, label, check_every=1):
 
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        z.zero_flatten_grads(p, -1, grads_dev, gpu.flat)
+        if case.flatten_mode == "buckets":
+            tb = p.tensor_buckets()
+            for b in range(p.n_buckets):
+                z.zero_flatten_grads(p, b, [g if (g is not None and tb[i] == b) else None
+                                            for i, g in enumerate(grads_dev)], gpu.flat)
+        else:
+            z.zero_flatten_grads(p, -1, grads_dev, gpu.flat)
         z.zero_adam_step_async(p, gpu.hp, gpu.flat, gpu.master, gpu.m, gpu.v, param, base)
     log(f"[graph] {label}: captured; S={p.S} real={p.real} segments={p.n_segments}")
 
@@ -163,3 +169,20 @@ def test_async_needs_uploaded_state():
     bad = z.LossScaler(0.0)
     with pytest.raises(z.ZeroError):
         z.zero_state_upload(plan, 0, bad)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_graph_replay_random_configuration(seed):
+    """The seeded random configurations of the device parity sweep, captured
+    once (flatten of all buckets, or bucket by bucket in order, inside the
+    capture) and replayed step by step."""
+    import dataclasses
+
+    from test_gpu_random_parity import random_case
+    case = random_case(seed)
+    case = dataclasses.replace(case, flatten_mode="buckets" if seed % 2 else "all")
+    label = (f"graph random seed={seed} numels={case.numels} R={case.world_size} "
+             f"r={case.rank} A={case.align} grads={case.grad_dtype} params={case.param_dtype} "
+             f"param={case.param_mode} flatten={case.flatten_mode}")
+    worst = _graph_run(case, label)
+    assert worst["bit_exact"], worst
