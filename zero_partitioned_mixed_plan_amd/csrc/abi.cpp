@@ -351,7 +351,11 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
     // pieces of this call: the bucket's segments, then the padding tail
     const uintptr_t esize = static_cast<uintptr_t>(grad_bytes(grad_dtype));
     std::vector<FlatPiece> pieces;
-    pieces.reserve(static_cast<size_t>(s_last - s_first) + 1);
+    try {
+        pieces.reserve(static_cast<size_t>(s_last - s_first) + 1);
+    } catch (const std::bad_alloc&) {
+        return fail(ZERO_ENOMEM, "flatten piece table allocation failed");
+    }
     for (int64_t s = s_first; s < s_last; ++s) {
         const Segment& g = p->segs[s];
         const void* src = grads[g.tensor];
