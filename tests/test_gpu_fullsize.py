@@ -16,6 +16,11 @@ Bar, after every step: flags, loss scale and applied-step counter equal;
 the flat gradient shard bit-identical on the windows; master / moments
 within 1e-6 relative error and parameters within 1 ulp on the windows at
 checkpoints (expected: identical bits).
+
+step_mode="graph" runs the step as bench.py's graph line does: flatten +
+zero_adam_step_async captured once into a HIP graph and replayed every
+iteration, with t and the loss scale held on the device (read back after
+each replay only to compare with the oracle).
 """
 import gc
 
@@ -58,7 +63,7 @@ def _windows(op, case, n_random=16, rnd_len=1 << 20, seed=1):
     return merged, idx
 
 
-def _run_sampled(case, check_at, flatten_mode="all", label=""):
+def _run_sampled(case, check_at, flatten_mode="all", label="", step_mode="sync"):
     import torch
     dev = torch.device("cuda:0")
     gdt, pdt = torch_dtype(case.grad_dtype), torch_dtype(case.param_dtype)
@@ -96,6 +101,26 @@ def _run_sampled(case, check_at, flatten_mode="all", label=""):
     tb = plan.tensor_buckets()
     d_idx = torch.from_numpy(idx).to(dev)
 
+    def flatten():
+        if flatten_mode == "buckets":
+            for b in range(plan.n_buckets):
+                z.zero_flatten_grads(plan, b, [g if (g is not None and tb[i] == b) else None
+                                               for i, g in enumerate(grads)], flat)
+        else:
+            z.zero_flatten_grads(plan, -1, grads, flat)
+
+    graph = None
+    if step_mode == "graph":
+        z.zero_state_upload(plan, 0, g_scaler)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            flatten()
+            z.zero_adam_step_async(plan, hp, flat, master, mom, var, param, begin)
+        log(f"[full] {label}: flatten + asynchronous step captured")
+    else:
+        assert step_mode == "sync", step_mode
+
     # ---- oracle state (windows)
     in_real = idx < real
     o_master = np.zeros(idx.size, np.float32)
@@ -109,7 +134,12 @@ def _run_sampled(case, check_at, flatten_mode="all", label=""):
     skipped = 0
     for it in range(1, case.steps + 1):
         scale = o_scaler.value
-        assert g_scaler.scale == scale, f"{label} it={it}: scale {g_scaler.scale} vs {scale}"
+        if graph is not None:
+            st = z.zero_state_download(plan)
+            assert st.applied_steps == o_t, f"{label} it={it}: t {st.applied_steps} vs {o_t}"
+            assert st.scale == scale, f"{label} it={it}: device scale {st.scale} vs {scale}"
+        else:
+            assert g_scaler.scale == scale, f"{label} it={it}: scale {g_scaler.scale} vs {scale}"
         key = grad_key(case, it)
         pos = case.injection(it, real)
         # GPU inputs: every segment of the shard, drawn on the device
@@ -121,14 +151,16 @@ def _run_sampled(case, check_at, flatten_mode="all", label=""):
             s = int(np.searchsorted(op.seg_shard_off, pos, side="right") - 1)
             t = int(op.seg_tensor[s])
             grads[t][int(op.seg_tensor_off[s] + pos - op.seg_shard_off[s])] = float("inf")
-        if flatten_mode == "buckets":
-            for b in range(plan.n_buckets):
-                z.zero_flatten_grads(plan, b, [g if (g is not None and tb[i] == b) else None
-                                               for i, g in enumerate(grads)], flat)
+        if graph is not None:
+            graph.replay()
+            st = z.zero_state_download(plan)
+            g_ovf = int(st.last_flag)
+            assert st.skipped_steps == skipped + g_ovf, f"{label} it={it}: skip count"
         else:
-            z.zero_flatten_grads(plan, -1, grads, flat)
-        g_ovf = z.zero_adam_step(plan, hp, g_t + 1, scale, flat, master, mom, var, param, begin)
-        z.zero_update_loss_scale(g_scaler, g_ovf)
+            flatten()
+            g_ovf = z.zero_adam_step(plan, hp, g_t + 1, scale, flat, master, mom, var, param,
+                                     begin)
+            z.zero_update_loss_scale(g_scaler, g_ovf)
         # oracle inputs: the same values at the window positions, from the host
         vals = np.zeros(idx.size, np.float32)
         vals[in_real] = synth.host_gather(key, begin + idx[in_real], case.grad_sigma, scale,
@@ -162,8 +194,11 @@ def _run_sampled(case, check_at, flatten_mode="all", label=""):
                 du = ulp_diff(gp, op_bits)
                 assert du <= ULP_TOL, f"{label} it={it}: params differ by {du} ulp"
             log(f"[full] {label}: it={it} t={o_t} scale={scale} ok")
+    if graph is not None:
+        st = z.zero_state_download(plan)
+        assert (st.applied_steps, st.scale) == (o_t, o_scaler.value), f"{label}: final state"
     log(f"[full] {label}: done, skipped {skipped} of {case.steps}")
-    del master, mom, var, flat, param, grads, d_idx
+    del graph, master, mom, var, flat, param, grads, d_idx
     gc.collect()
     torch.cuda.empty_cache()
     return skipped
@@ -187,6 +222,19 @@ def test_dna_20b_rank2_dynamic_scale_with_injected_overflows():
     assert skipped == expect and skipped >= 1
 
 
+def test_llama3_8b_rank3_graph_replayed_step():
+    case = Case.from_workload(get("llama3_8b"))
+    _run_sampled(case, check_at={1, 10}, label="llama3_8b graph", step_mode="graph")
+
+
+def test_dna_20b_rank2_graph_replayed_step_with_device_scaler():
+    # the loss-scale policy runs on the device: skips and halvings at full size
+    case = Case.from_workload(get("dna_20b"))
+    skipped = _run_sampled(case, check_at={1, 25}, label="dna_20b graph", step_mode="graph")
+    expect = sum(case.injection(it, 2_498_481_408) is not None for it in range(1, case.steps + 1))
+    assert skipped == expect and skipped >= 1
+
+
 def test_llama2_70b_rank7_full_shard():
     import torch
     free, _ = torch.cuda.mem_get_info()
@@ -194,6 +242,15 @@ def test_llama2_70b_rank7_full_shard():
         pytest.skip(f"needs ~160 GB of free device memory, {free / 1e9:.0f} GB free")
     case = Case.from_workload(get("llama2_70b"))
     _run_sampled(case, check_at={1, 3}, label="llama2_70b")
+
+
+def test_llama2_70b_rank7_graph_replayed_step():
+    import torch
+    free, _ = torch.cuda.mem_get_info()
+    if free < 170e9:
+        pytest.skip(f"needs ~160 GB of free device memory, {free / 1e9:.0f} GB free")
+    case = Case.from_workload(get("llama2_70b"))
+    _run_sampled(case, check_at={1, 5}, label="llama2_70b graph", step_mode="graph")
 
 
 def test_tensor_beyond_2_31_elements():
