@@ -268,3 +268,118 @@ def test_tensor_beyond_2_31_elements():
                 param_dtype="bf16", steps=3, inject={2: 2_300_000_000})
     skipped = _run_sampled(case, check_at={1, 3}, label="5e9-element tensor")
     assert skipped == 1
+
+
+def _offload_sampled(case, lag, label, n_threads=8):
+    """The ZeRO-Offload pipeline over a full-size shard, checked on the same
+    sampled windows: each iteration's stand-in forward must see exactly the
+    oracle's parameters after iteration it - 1 - lag, and after the drain the
+    host master / moments and the device parameters must equal the oracle's
+    bit for bit there."""
+    import torch
+    dev = torch.device("cuda:0")
+    gdt, pdt = torch_dtype(case.grad_dtype), torch_dtype(case.param_dtype)
+    op = oracle.plan(case.numels, case.world_size, case.rank, case.align, case.bucket_elems)
+    plan = z.zero_partition_plan(case.numels, case.world_size, case.rank, case.align,
+                                 case.bucket_elems)
+    S, real, begin = op.S, op.real, op.begin
+    assert (plan.S, plan.begin, plan.real) == (S, begin, real)
+    windows, idx = _windows(op, case)
+    in_real = idx < real
+    ridx = idx[in_real]
+    log(f"[full] {label}: S={S} real={real} lag={lag} threads={n_threads} "
+        f"windows={len(windows)} sampled={idx.size}")
+    offs = flat_offsets(case.numels)
+
+    # ---- host state of the offloaded step (drawn by the device generator,
+    # cross-checked against the host one elsewhere), device buffers
+    dm = torch.zeros(S, dtype=torch.float32, device=dev)
+    synth.dev_fill_f32(dm[:real], master_key(case), begin, case.master_sigma)
+    master = dm.cpu().numpy()
+    del dm
+    mom = np.zeros(S, np.float32)
+    var = np.zeros(S, np.float32)
+    param = torch.zeros(max(real, 1), dtype=pdt, device=dev)   # window at shard_begin
+    flat = torch.empty(S, dtype=gdt, device=dev)
+    grads = [None] * len(case.numels)
+    for s in range(op.n_segments):
+        t = int(op.seg_tensor[s])
+        if grads[t] is None:
+            grads[t] = torch.empty(case.numels[t], dtype=gdt, device=dev)
+    hp = z.AdamHParams(case.lr, case.beta1, case.beta2, case.eps, case.weight_decay, case.adamw)
+    z.zero_state_upload(plan, 0, z.LossScaler(case.init_scale, dynamic=case.dynamic,
+                                              window=case.window))
+    off = z.Offload(plan, hp, case.grad_dtype, case.param_dtype, master, mom, var,
+                    n_threads=n_threads)
+    d_ridx = torch.from_numpy(ridx).to(dev)
+
+    # ---- oracle state (windows)
+    o_master = np.zeros(idx.size, np.float32)
+    o_master[in_real] = synth.host_gather(master_key(case), begin + ridx, case.master_sigma)
+    o_m = np.zeros(idx.size, np.float32)
+    o_v = np.zeros(idx.size, np.float32)
+    o_scaler = oracle.Scaler(case.init_scale, dynamic=case.dynamic, window=case.window)
+    o_t = skipped = 0
+    othresh = synth.outlier_thresh(case.outlier_p)
+    hist = [np.zeros(ridx.size, np.uint16)]   # the windows' parameters after iteration k
+    for it in range(1, case.steps + 1):
+        off.wait_params(lag)
+        seen = param.index_select(0, d_ridx).view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(seen, hist[max(it - 1 - lag, 0)]), \
+            f"{label} it={it}: the forward saw other parameters than iteration {it - 1 - lag}'s"
+        scale = o_scaler.value
+        st = z.zero_state_download(plan)
+        assert st.scale == scale, f"{label} it={it}: device scale {st.scale} vs {scale}"
+        key = grad_key(case, it)
+        pos = case.injection(it, real)
+        for s in range(op.n_segments):
+            t, a, n = int(op.seg_tensor[s]), int(op.seg_tensor_off[s]), int(op.seg_numel[s])
+            synth.dev_fill_half(grads[t][a:a + n], key, int(offs[t]) + a, case.grad_sigma, scale,
+                                othresh, case.outlier_mult)
+        if pos is not None:
+            s = int(np.searchsorted(op.seg_shard_off, pos, side="right") - 1)
+            t = int(op.seg_tensor[s])
+            grads[t][int(op.seg_tensor_off[s] + pos - op.seg_shard_off[s])] = float("inf")
+        z.zero_flatten_grads(plan, -1, grads, flat)
+        off.submit(flat, param, begin)
+        vals = np.zeros(idx.size, np.float32)
+        vals[in_real] = synth.host_gather(key, begin + ridx, case.grad_sigma, scale, othresh,
+                                          case.outlier_mult)
+        o_flat = synth.grad_bits(vals, case.grad_dtype)
+        o_flat[~in_real] = 0
+        if pos is not None:
+            o_flat[np.searchsorted(idx, pos)] = INF_BITS[case.grad_dtype]
+        o_ovf = oracle.adam_step(o_t + 1, scale, o_flat, case.grad_dtype, o_master, o_m, o_v,
+                                 **case.hparams())
+        o_scaler.update(o_ovf)
+        o_t += 1 - o_ovf
+        skipped += o_ovf
+        hist.append(hist[-1] if o_ovf else oracle.float_to_half(o_master[in_real],
+                                                                case.param_dtype))
+        log(f"[full] {label}: it={it} submitted, oracle overflow {o_ovf}")
+    off.drain()
+    stats = off.stats()
+    assert stats["applied"] == o_t and stats["skipped"] == skipped, stats
+    st = z.zero_state_download(plan)
+    assert (st.applied_steps, st.skipped_steps, st.scale) == (o_t, skipped, o_scaler.value)
+    for name, a, b in (("master", master[idx], o_master), ("m", mom[idx], o_m),
+                       ("v", var[idx], o_v)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), \
+            f"{label}: {name} differs (max rel err {max_rel(a, b)})"
+    final = param.index_select(0, d_ridx).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(final, hist[-1]), f"{label}: final parameters differ"
+    off.close()
+    log(f"[full] {label}: ok, applied {o_t}, skipped {skipped}, "
+        f"host ms last {stats['host_ms_last']:.1f}")
+    del param, flat, grads, d_ridx, master, mom, var
+    gc.collect()
+    torch.cuda.empty_cache()
+    return skipped
+
+
+@pytest.mark.parametrize("lag", [1, 0])
+def test_llama3_8b_rank3_offload(lag):
+    # bench.py's offload workload at its full size (16 pieces of the shard),
+    # with a +inf at iteration 3 so one step is skipped
+    case = Case.from_workload(get("llama3_8b"), steps=5, inject={3: 700_000_001})
+    assert _offload_sampled(case, lag, f"llama3_8b offload lag={lag}") == 1
