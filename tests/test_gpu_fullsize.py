@@ -30,8 +30,8 @@ import pytest
 import oracle
 import synth
 import zero_partitioned_mixed_plan_amd as z
-from harness import (INF_BITS, REL_TOL, ULP_TOL, Case, flat_offsets, grad_key, log, master_key,
-                     grad_bits_host, max_rel, torch_dtype, ulp_diff)
+from harness import (INF_BITS, PARAM_FILL, REL_TOL, ULP_TOL, Case, flat_offsets, grad_key, log,
+                     master_key, grad_bits_host, max_rel, torch_dtype, ulp_diff)
 from synth.workloads import get
 
 pytestmark = pytest.mark.gpu
@@ -251,6 +251,83 @@ def test_llama2_70b_rank7_graph_replayed_step():
         pytest.skip(f"needs ~160 GB of free device memory, {free / 1e9:.0f} GB free")
     case = Case.from_workload(get("llama2_70b"))
     _run_sampled(case, check_at={1, 5}, label="llama2_70b graph", step_mode="graph")
+
+
+def test_llama2_70b_rank7_standalone_cast_and_scan():
+    """The two kernels bench.py also times on their own, at the 70B shard's
+    size: zero_write_param_shard, and the scan that zero_adam_step runs when
+    its gradient buffer did not come from zero_flatten_grads (here it is
+    filled directly).  A +inf 12,345 elements before the shard's end (past
+    2^33) must skip the step with every sampled state and parameter bit
+    unchanged; without it the step must match the oracle."""
+    import torch
+    free, _ = torch.cuda.mem_get_info()
+    if free < 150e9:
+        pytest.skip(f"needs ~140 GB of free device memory, {free / 1e9:.0f} GB free")
+    dev = torch.device("cuda:0")
+    w = get("llama2_70b")
+    op = oracle.plan(w.numels, w.world_size, w.rank, w.align, w.bucket_elems)
+    S, real, begin = op.S, op.real, op.begin
+    pos = S - 12_345
+    assert pos > 1 << 33 and S == real
+    case = Case.from_workload(w, steps=1, inject={1: pos})
+    plan = z.zero_partition_plan(w.numels, w.world_size, w.rank, w.align, w.bucket_elems)
+    windows, idx = _windows(op, case)
+    log(f"[full] 70b cast+scan: S={S} windows={len(windows)} sampled={idx.size}")
+    d_idx = torch.from_numpy(idx).to(dev)
+    pdt, gdt = torch_dtype(w.param_dtype), torch_dtype(w.grad_dtype)
+
+    master = torch.empty(S, dtype=torch.float32, device=dev)
+    synth.dev_fill_f32(master, master_key(case), begin, case.master_sigma)
+    mom = torch.zeros(S, dtype=torch.float32, device=dev)
+    var = torch.zeros(S, dtype=torch.float32, device=dev)
+    fill = int(np.array(PARAM_FILL, np.uint16).view(np.int16))
+    param = torch.full((S,), fill, dtype=torch.int16, device=dev).view(pdt)
+    o_master = synth.host_gather(master_key(case), begin + idx, case.master_sigma)
+    o_m = np.zeros(idx.size, np.float32)
+    o_v = np.zeros(idx.size, np.float32)
+
+    def bits16(t):
+        return t.index_select(0, d_idx).view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def bits32(t):
+        return t.index_select(0, d_idx).cpu().numpy().view(np.uint32)
+
+    # standalone cast of the fp32 master shard to its window of the parameters
+    z.zero_write_param_shard(plan, master, param, begin)
+    want_p = oracle.float_to_half(o_master, w.param_dtype)
+    assert np.array_equal(bits16(param), want_p), "standalone cast differs"
+    log("[full] 70b cast+scan: standalone cast ok")
+
+    # gradients written straight into the flat buffer: the step must scan
+    key = grad_key(case, 1)
+    flat = torch.empty(S, dtype=gdt, device=dev)
+    synth.dev_fill_half(flat, key, begin, case.grad_sigma)
+    good = flat[pos].clone()
+    flat[pos] = float("inf")
+    hp = z.AdamHParams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.adamw)
+    before = (bits32(master), bits32(mom), bits32(var))
+    assert z.zero_adam_step(plan, hp, 1, 1.0, flat, master, mom, var, param, begin) == 1
+    for name, a, b in zip(("master", "m", "v"), before, (bits32(master), bits32(mom),
+                                                         bits32(var))):
+        assert np.array_equal(a, b), f"skipped step changed {name}"
+    assert np.array_equal(bits16(param), want_p), "skipped step changed the parameters"
+    log("[full] 70b cast+scan: +inf found by the scan, step skipped")
+
+    flat[pos] = good
+    assert z.zero_adam_step(plan, hp, 1, 1.0, flat, master, mom, var, param, begin) == 0
+    o_flat = synth.grad_bits(synth.host_gather(key, begin + idx, case.grad_sigma), w.grad_dtype)
+    assert np.array_equal(bits16(flat), o_flat)
+    assert oracle.adam_step(1, 1.0, o_flat, w.grad_dtype, o_master, o_m, o_v,
+                            **case.hparams()) == 0
+    for name, a, b in (("master", bits32(master), o_master), ("m", bits32(mom), o_m),
+                       ("v", bits32(var), o_v)):
+        assert np.array_equal(a, b.view(np.uint32)), f"{name} differs after the scanned step"
+    assert np.array_equal(bits16(param), oracle.float_to_half(o_master, w.param_dtype))
+    log("[full] 70b cast+scan: scanned step ok")
+    del master, mom, var, param, flat, d_idx
+    gc.collect()
+    torch.cuda.empty_cache()
 
 
 def test_tensor_beyond_2_31_elements():
