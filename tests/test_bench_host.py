@@ -8,8 +8,6 @@ import re
 import subprocess
 import sys
 
-import pytest
-
 import bench
 import zero_partitioned_mixed_plan_amd as z
 from synth.workloads import get
