@@ -460,3 +460,160 @@ def test_llama3_8b_rank3_offload(lag):
     # with a +inf at iteration 3 so one step is skipped
     case = Case.from_workload(get("llama3_8b"), steps=5, inject={3: 700_000_001})
     assert _offload_sampled(case, lag, f"llama3_8b offload lag={lag}") == 1
+
+
+def _host_threads():
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:   # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _whole_shard(case, label):
+    """Every element of the shard after every step: the flat gradients,
+    master, moments and parameters bit for bit, and the overflow flag and
+    loss scale.  The oracle runs over contiguous chunks of the shard on host
+    threads (the step is elementwise once the overflow decision, taken over
+    the whole shard first, is known); its gradients come from the host
+    generator at the same flat indices as the device's, with the same +inf."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+    dev = torch.device("cuda:0")
+    gdt, pdt = torch_dtype(case.grad_dtype), torch_dtype(case.param_dtype)
+    op = oracle.plan(case.numels, case.world_size, case.rank, case.align, case.bucket_elems)
+    plan = z.zero_partition_plan(case.numels, case.world_size, case.rank, case.align,
+                                 case.bucket_elems)
+    S, real, begin = op.S, op.real, op.begin
+    assert (plan.S, plan.begin, plan.real) == (S, begin, real)
+    chunk = 1 << 24
+    chunks = [(lo, min(S, lo + chunk)) for lo in range(0, S, chunk)]
+    pool = ThreadPoolExecutor(_host_threads())
+    log(f"[whole] {label}: S={S} real={real} chunks={len(chunks)} threads={pool._max_workers}")
+    offs = flat_offsets(case.numels)
+    othresh = synth.outlier_thresh(case.outlier_p)
+
+    master = torch.zeros(S, dtype=torch.float32, device=dev)
+    synth.dev_fill_f32(master[:real], master_key(case), begin, case.master_sigma)
+    mom = torch.zeros(S, dtype=torch.float32, device=dev)
+    var = torch.zeros(S, dtype=torch.float32, device=dev)
+    flat = torch.empty(S, dtype=gdt, device=dev)
+    param = torch.empty(max(real, 1), dtype=pdt, device=dev)   # window at shard_begin
+    grads = [None] * len(case.numels)
+    for s in range(op.n_segments):
+        t = int(op.seg_tensor[s])
+        if grads[t] is None:
+            grads[t] = torch.empty(case.numels[t], dtype=gdt, device=dev)
+    hp = z.AdamHParams(case.lr, case.beta1, case.beta2, case.eps, case.weight_decay, case.adamw)
+    g_scaler = z.LossScaler(case.init_scale, dynamic=case.dynamic, window=case.window)
+
+    o_master = np.zeros(S, np.float32)
+    o_m = np.zeros(S, np.float32)
+    o_v = np.zeros(S, np.float32)
+    bits = np.zeros(S, np.uint16)
+
+    def init(c):
+        lo, hi = c[0], min(c[1], real)
+        if hi > lo:
+            o_master[lo:hi] = synth.host_values(master_key(case), begin + lo, hi - lo,
+                                                case.master_sigma)
+
+    list(pool.map(init, chunks))
+    o_scaler = oracle.Scaler(case.init_scale, dynamic=case.dynamic, window=case.window)
+    g_t = o_t = skipped = 0
+    for it in range(1, case.steps + 1):
+        scale = o_scaler.value
+        assert g_scaler.scale == scale, f"{label} it={it}: scale {g_scaler.scale} vs {scale}"
+        key = grad_key(case, it)
+        pos = case.injection(it, real)
+        for s in range(op.n_segments):
+            t, a, n = int(op.seg_tensor[s]), int(op.seg_tensor_off[s]), int(op.seg_numel[s])
+            synth.dev_fill_half(grads[t][a:a + n], key, int(offs[t]) + a, case.grad_sigma, scale,
+                                othresh, case.outlier_mult)
+        if pos is not None:
+            s = int(np.searchsorted(op.seg_shard_off, pos, side="right") - 1)
+            t = int(op.seg_tensor[s])
+            grads[t][int(op.seg_tensor_off[s] + pos - op.seg_shard_off[s])] = float("inf")
+        z.zero_flatten_grads(plan, -1, grads, flat)
+        g_ovf = z.zero_adam_step(plan, hp, g_t + 1, scale, flat, master, mom, var, param, begin)
+        z.zero_update_loss_scale(g_scaler, g_ovf)
+
+        def gen(c):
+            lo, hi = c[0], min(c[1], real)
+            if hi > lo:
+                bits[lo:hi] = synth.grad_bits(
+                    synth.host_values(key, begin + lo, hi - lo, case.grad_sigma, scale, othresh,
+                                      case.outlier_mult), case.grad_dtype)
+                if pos is not None and lo <= pos < hi:
+                    bits[pos] = INF_BITS[case.grad_dtype]
+            return oracle.nonfinite(bits[c[0]:c[1]], case.grad_dtype)
+
+        o_ovf = int(any(list(pool.map(gen, chunks))))
+        if not o_ovf:
+            def upd(c):
+                lo, hi = c
+                oracle.adam_update(o_t + 1, scale, bits[lo:hi], case.grad_dtype,
+                                   o_master[lo:hi], o_m[lo:hi], o_v[lo:hi], **case.hparams())
+            list(pool.map(upd, chunks))
+        o_scaler.update(o_ovf)
+        assert g_ovf == o_ovf, f"{label} it={it}: overflow {g_ovf} vs oracle {o_ovf}"
+        g_t += 1 - g_ovf
+        o_t += 1 - o_ovf
+        skipped += o_ovf
+        torch.cuda.synchronize(dev)
+
+        def check(c):
+            lo, hi = c
+            bad = []
+            got = flat[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16)
+            if not np.array_equal(got, bits[lo:hi]):
+                bad.append("flat")
+            for name, d, o in (("master", master, o_master), ("m", mom, o_m), ("v", var, o_v)):
+                got = d[lo:hi].cpu().numpy()
+                if not np.array_equal(got.view(np.uint32), o[lo:hi].view(np.uint32)):
+                    bad.append(f"{name} (max rel err {max_rel(got, o[lo:hi])})")
+            hi = min(hi, real)
+            if o_t > 0 and hi > lo:
+                got = param[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16)
+                if not np.array_equal(got, oracle.float_to_half(o_master[lo:hi],
+                                                                case.param_dtype)):
+                    bad.append("param")
+            return (lo, bad) if bad else None
+
+        wrong = [r for r in pool.map(check, chunks) if r is not None]
+        assert not wrong, f"{label} it={it}: chunks differ: {wrong[:4]}"
+        log(f"[whole] {label}: it={it} t={o_t} scale={scale} overflow={o_ovf}: "
+            f"every element equal")
+    pool.shutdown()
+    del master, mom, var, flat, param, grads
+    gc.collect()
+    torch.cuda.empty_cache()
+    return skipped
+
+
+def test_llama3_8b_rank3_whole_shard_every_step():
+    case = Case.from_workload(get("llama3_8b"), steps=4)
+    assert _whole_shard(case, "llama3_8b") == 0
+
+
+def test_dna_20b_rank2_whole_shard_every_step():
+    # fp16 gradients at the dynamic scale, 300 pieces, a +inf at iteration 2
+    case = Case.from_workload(get("dna_20b"), steps=3, inject_p=0.0,
+                              inject={2: 2_000_000_017})
+    assert _whole_shard(case, "dna_20b") == 1
+
+
+def test_llama2_70b_rank7_whole_shard_every_step():
+    # about 125 GB of host memory for the oracle's state: opt-in
+    import os
+
+    import torch
+    if os.environ.get("ZERO_WHOLE_70B") != "1":
+        pytest.skip("opt-in (ZERO_WHOLE_70B=1): the oracle holds ~125 GB of host state")
+    free, _ = torch.cuda.mem_get_info()
+    if free < 170e9:
+        pytest.skip(f"needs ~160 GB of free device memory, {free / 1e9:.0f} GB free")
+    case = Case.from_workload(get("llama2_70b"), steps=2)
+    assert _whole_shard(case, "llama2_70b") == 0
