@@ -471,13 +471,15 @@ def _host_threads():
     return max(1, min(16, n))
 
 
-def _whole_shard(case, label):
+def _whole_shard(case, label, step_mode="sync"):
     """Every element of the shard after every step: the flat gradients,
     master, moments and parameters bit for bit, and the overflow flag and
     loss scale.  The oracle runs over contiguous chunks of the shard on host
     threads (the step is elementwise once the overflow decision, taken over
     the whole shard first, is known); its gradients come from the host
-    generator at the same flat indices as the device's, with the same +inf."""
+    generator at the same flat indices as the device's, with the same +inf.
+    step_mode="graph": flatten + zero_adam_step_async replayed from a HIP
+    graph, t and the scale on the device."""
     from concurrent.futures import ThreadPoolExecutor
 
     import torch
@@ -508,6 +510,16 @@ def _whole_shard(case, label):
             grads[t] = torch.empty(case.numels[t], dtype=gdt, device=dev)
     hp = z.AdamHParams(case.lr, case.beta1, case.beta2, case.eps, case.weight_decay, case.adamw)
     g_scaler = z.LossScaler(case.init_scale, dynamic=case.dynamic, window=case.window)
+    graph = None
+    if step_mode == "graph":
+        z.zero_state_upload(plan, 0, g_scaler)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            z.zero_flatten_grads(plan, -1, grads, flat)
+            z.zero_adam_step_async(plan, hp, flat, master, mom, var, param, begin)
+    else:
+        assert step_mode == "sync", step_mode
 
     o_master = np.zeros(S, np.float32)
     o_m = np.zeros(S, np.float32)
@@ -525,7 +537,11 @@ def _whole_shard(case, label):
     g_t = o_t = skipped = 0
     for it in range(1, case.steps + 1):
         scale = o_scaler.value
-        assert g_scaler.scale == scale, f"{label} it={it}: scale {g_scaler.scale} vs {scale}"
+        if graph is not None:
+            st = z.zero_state_download(plan)
+            assert (st.applied_steps, st.scale) == (o_t, scale), f"{label} it={it}: state"
+        else:
+            assert g_scaler.scale == scale, f"{label} it={it}: scale {g_scaler.scale} vs {scale}"
         key = grad_key(case, it)
         pos = case.injection(it, real)
         for s in range(op.n_segments):
@@ -536,9 +552,14 @@ def _whole_shard(case, label):
             s = int(np.searchsorted(op.seg_shard_off, pos, side="right") - 1)
             t = int(op.seg_tensor[s])
             grads[t][int(op.seg_tensor_off[s] + pos - op.seg_shard_off[s])] = float("inf")
-        z.zero_flatten_grads(plan, -1, grads, flat)
-        g_ovf = z.zero_adam_step(plan, hp, g_t + 1, scale, flat, master, mom, var, param, begin)
-        z.zero_update_loss_scale(g_scaler, g_ovf)
+        if graph is not None:
+            graph.replay()
+            g_ovf = int(z.zero_state_download(plan).last_flag)
+        else:
+            z.zero_flatten_grads(plan, -1, grads, flat)
+            g_ovf = z.zero_adam_step(plan, hp, g_t + 1, scale, flat, master, mom, var, param,
+                                     begin)
+            z.zero_update_loss_scale(g_scaler, g_ovf)
 
         def gen(c):
             lo, hi = c[0], min(c[1], real)
@@ -587,7 +608,10 @@ def _whole_shard(case, label):
         log(f"[whole] {label}: it={it} t={o_t} scale={scale} overflow={o_ovf}: "
             f"every element equal")
     pool.shutdown()
-    del master, mom, var, flat, param, grads
+    if graph is not None:
+        st = z.zero_state_download(plan)
+        assert (st.applied_steps, st.skipped_steps, st.scale) == (o_t, skipped, o_scaler.value)
+    del graph, master, mom, var, flat, param, grads
     gc.collect()
     torch.cuda.empty_cache()
     return skipped
@@ -603,6 +627,14 @@ def test_dna_20b_rank2_whole_shard_every_step():
     case = Case.from_workload(get("dna_20b"), steps=3, inject_p=0.0,
                               inject={2: 2_000_000_017})
     assert _whole_shard(case, "dna_20b") == 1
+
+
+def test_dna_20b_rank2_whole_shard_graph_replayed():
+    # the asynchronous step from a HIP graph: the skip and the halving are
+    # decided on the device
+    case = Case.from_workload(get("dna_20b"), steps=3, inject_p=0.0,
+                              inject={2: 1_000_000_003})
+    assert _whole_shard(case, "dna_20b graph", step_mode="graph") == 1
 
 
 def test_llama2_70b_rank7_whole_shard_every_step():
