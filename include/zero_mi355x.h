@@ -169,7 +169,9 @@ void zero_plan_destroy(zero_plan_t* plan);
  * and flat_grad[real, S) = 0 on every call.  While copying, any element
  * whose exponent field is all ones (+-inf or NaN) raises the plan's device
  * overflow flag ([legal] dynamic loss scaling bullet); the flag stays
- * raised until the next zero_adam_step consumes it.
+ * raised until the next step on this plan consumes it.  The flag belongs to
+ * one buffer: a flatten into another flat_grad (or in another dtype) than
+ * the previous flattens since the last step clears it first.
  * grads: HOST array of n_tensors DEVICE pointers, each to tensor i's first
  * element, aligned to the element size (2 bytes; 4 for ZERO_F32); entries
  * of tensors without a segment in the requested bucket(s) may be NULL.
@@ -185,10 +187,14 @@ int zero_flatten_grads(zero_plan_t* plan, int32_t bucket, const void* const* gra
  * weights, momentum and variance of the partition, updated by their owner;
  * [instr] mixed-precision bullets: the gradient is scaled down and upcast
  * to fp32 for the update, and the weights are cast to fp16/bf16.
- * If the flag is raised -- by zero_flatten_grads since the last step, or by
- * a scan of flat_grad that runs first whenever not every bucket of the
- * shard was flattened into this flat_grad since the last step -- nothing
- * is written and 1 is returned.  Otherwise, per shard element k < S, in
+ * If the flag is raised, nothing is written and 1 is returned.  The flag
+ * is the fused test of the flattens into this flat_grad since the last step
+ * when they covered every bucket of the shard; otherwise the flag is cleared
+ * and a scan of flat_grad's real elements [0, real) decides it (the gate
+ * reads the buffer as it is when the step runs: a write into flat_grad
+ * after a covering flatten is not tested again).  The padding gradients
+ * flat_grad[real, S) are never tested: they update only the padding state,
+ * which is never cast to a parameter.  Otherwise, per shard element k < S, in
  * fp32 with one rounding per operation (scalars formed on the host in
  * double and rounded once):
  *   g = fp32(flat_grad[k]) * fp32(1/loss_scale)  [adamw=0: g += wd * p]
@@ -300,8 +306,8 @@ int zero_adam_step_async(zero_plan_t* plan, const zero_adam_hparams_t* hp, const
  * (ZERO_F16 / ZERO_BF16 2-byte, ZERO_F32 4-byte aligned); master / exp_avg / exp_avg_sq: S floats each (4-byte aligned);
  * param (may be NULL): host buffer holding flat indices [param_base,
  * param_base + param_numel), which must contain the shard's real range.
- * overflow: 1 = skip (nothing written), 0 = apply, -1 = test flat_grad for
- * inf/NaN here first.  n_threads (1..1024): host threads, taken from a pool
+ * overflow: 1 = skip (nothing written), 0 = apply, -1 = test the real
+ * gradients flat_grad[0, real) for inf/NaN here first.  n_threads (1..1024): host threads, taken from a pool
  * the library keeps between calls (a call made while another one holds that
  * pool starts threads of its own; a process made by fork() builds a pool of
  * its own); the result does not depend on it.  Calls on disjoint buffers
@@ -381,10 +387,14 @@ int zero_offload_create(zero_plan_t* plan, const zero_adam_hparams_t* hp, int32_
                         int32_t param_dtype, float* master, float* exp_avg, float* exp_avg_sq,
                         int32_t n_threads, zero_offload_t** out);
 
-/* Submits one step: flat_grad is the device flat gradient shard just
+/* Submits one step: flat_grad is the device flat gradient shard (S
+ * elements of the offload's grad_dtype, 16-byte aligned), normally just
  * flattened on `stream`; param the device parameter buffer holding flat
  * indices [param_base, param_base + param_numel) (may be NULL when
- * param_dtype is 0).  Errors: ZERO_ENULL, ZERO_EINVAL, ZERO_EALIGN,
+ * param_dtype is 0).  The step's overflow flag follows zero_adam_step's
+ * gate: the flattens since the last step when they covered flat_grad,
+ * otherwise a scan of its real elements on `stream`.  Errors: ZERO_ENULL,
+ * ZERO_EINVAL (flat_grad last flattened in another dtype), ZERO_EALIGN,
  * ZERO_EHIP, ZERO_ESTATE, or the worker's error. */
 int zero_offload_submit(zero_offload_t* off, const void* flat_grad, void* param,
                         int64_t param_base, int64_t param_numel, void* stream);
@@ -406,6 +416,21 @@ int zero_offload_stats(zero_offload_t* off, zero_offload_stats_t* out);
 /* Completes the submitted steps, then releases the thread, stream and
  * buffers (NULL is a no-op). */
 void zero_offload_destroy(zero_offload_t* off);
+
+/* The fp32 scalars of the update for bias-correction steps t_first ..
+ * t_first + count - 1 at loss scale loss_scale, ten floats per step in this
+ * order: 1/scale, b1, 1-b1, b2, 1-b2, lr/(1-b1^t), 1/sqrt(1-b2^t), eps,
+ * 1-lr*wd (AdamW; 1 for Adam-L2), wd -- each formed in double and rounded
+ * once ([instr] ZeRO-1 paragraph, momentum and variance; the update of
+ * zero_adam_step).  on_device = 0: out is host memory and the scalars are
+ * those zero_adam_step and zero_cpu_adam_step form on the host; on_device =
+ * 1: out is device memory and a kernel on `stream` forms them as
+ * zero_adam_step_async's prologue does, with the device's pow and sqrt
+ * (async; the caller waits for `stream`).  out: 10 * count floats, 4-byte
+ * aligned.  Errors: ZERO_ENULL, ZERO_EINVAL (t_first < 1, count < 0,
+ * loss_scale, hyperparameters), ZERO_EALIGN, ZERO_EHIP. */
+int zero_adam_scalars(const zero_adam_hparams_t* hp, int64_t t_first, int64_t count,
+                      double loss_scale, float* out, int32_t on_device, void* stream);
 
 /* Message of the calling thread's last error ("" if none). */
 const char* zero_last_error(void);

@@ -24,6 +24,10 @@ hipError_t launch_step_prologue(const int*, const DeviceStep*, AdamScalars*,
     return hipErrorNoDevice;
 }
 hipError_t launch_step_epilogue(int*, DeviceStep*, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_adam_scalars(const zero_adam_hparams_t&, int64_t, int64_t, double, AdamScalars*,
+                               hipStream_t) {
+    return hipErrorNoDevice;
+}
 hipError_t launch_offload_snapshot(int*, DeviceStep*, OffloadSlot*, hipStream_t) {
     return hipErrorNoDevice;
 }

@@ -232,3 +232,38 @@ def test_offload_argument_errors_before_device_work():
     assert lib.zero_offload_wait_params(None, 1, None) == _abi.ZERO_ENULL
     assert lib.zero_offload_drain(None, None) == _abi.ZERO_ENULL
     lib.zero_offload_destroy(None)
+
+
+def test_adam_scalars_on_the_host():
+    """zero_adam_scalars(on_device=0) gives the scalars zero_adam_step forms:
+    each definition evaluated in float64 (Python's math library) and rounded
+    once to fp32; argument errors are reported."""
+    import math
+    for hp, scale in ((z.AdamHParams(), 1024.0),
+                      (z.AdamHParams(lr=0.5, beta1=0.99, beta2=0.95, eps=1e-3, weight_decay=0.2,
+                                     adamw=False), 0.25)):
+        got = z.zero_adam_scalars(hp, 1, 20000, scale)
+        assert got.shape == (20000, len(z.SCALAR_FIELDS))
+        for t in range(1, 20001):
+            want = np.array([1.0 / scale, hp.beta1, 1.0 - hp.beta1, hp.beta2, 1.0 - hp.beta2,
+                             hp.lr / (1.0 - math.pow(hp.beta1, t)),
+                             1.0 / math.sqrt(1.0 - math.pow(hp.beta2, t)), hp.eps,
+                             1.0 - hp.lr * hp.weight_decay if hp.adamw else 1.0,
+                             hp.weight_decay], np.float64).astype(np.float32)
+            assert np.array_equal(got[t - 1].view(np.uint32), want.view(np.uint32)), t
+        # a window starting later is the same rows
+        assert np.array_equal(z.zero_adam_scalars(hp, 777, 5, scale), got[776:781])
+    lib = _abi.lib
+    hp = z.AdamHParams().to_c()
+    buf = np.zeros(40, np.float32)
+    ptr = buf.ctypes.data
+    assert lib.zero_adam_scalars(None, 1, 1, 1.0, ptr, 0, None) == _abi.ZERO_ENULL
+    assert lib.zero_adam_scalars(ctypes.byref(hp), 0, 1, 1.0, ptr, 0, None) == _abi.ZERO_EINVAL
+    assert lib.zero_adam_scalars(ctypes.byref(hp), 1, -1, 1.0, ptr, 0, None) == _abi.ZERO_EINVAL
+    assert lib.zero_adam_scalars(ctypes.byref(hp), 1, 1, 0.0, ptr, 0, None) == _abi.ZERO_EINVAL
+    assert lib.zero_adam_scalars(ctypes.byref(hp), 1, 1, 1.0, ptr, 2, None) == _abi.ZERO_EINVAL
+    assert lib.zero_adam_scalars(ctypes.byref(hp), 1, 1, 1.0, None, 0, None) == _abi.ZERO_ENULL
+    assert lib.zero_adam_scalars(ctypes.byref(hp), 1, 1, 1.0, ptr + 2, 0, None) == _abi.ZERO_EALIGN
+    assert lib.zero_adam_scalars(ctypes.byref(hp), 1, 0, 1.0, None, 0, None) == _abi.ZERO_OK
+    bad = z.AdamHParams(beta2=1.0).to_c()
+    assert lib.zero_adam_scalars(ctypes.byref(bad), 1, 1, 1.0, ptr, 0, None) == _abi.ZERO_EINVAL

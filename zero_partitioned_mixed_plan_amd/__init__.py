@@ -28,6 +28,9 @@ and ZeRO-Offload's host-side update (host buffers: numpy arrays or CPU tensors):
                        exp_avg_sq, param=None, param_base=0, grad_dtype=None,
                        param_dtype=None, overflow=-1, n_threads=None) -> 0 | 1
     zero_cpu_isa() -> "avx512" | "avx2" | "scalar"
+    zero_adam_scalars(hparams, t_first, count, loss_scale, out=None) -> [count, 10]
+                                (the update's fp32 scalars, formed on the host or
+                                 on the device as the asynchronous step does)
     Offload(plan, hparams, grad_dtype, param_dtype, master, exp_avg, exp_avg_sq,
             n_threads=None)     .submit / .wait_params / .drain / .stats / .close
                                 (zero_offload_* : the pipelined offloaded step with the
@@ -46,7 +49,8 @@ __all__ = ["Plan", "AdamHParams", "LossScaler", "DeviceStepState", "ZeroError",
            "zero_partition_plan", "GradList", "zero_flatten_grads", "zero_adam_step",
            "zero_update_loss_scale", "zero_write_param_shard", "zero_state_upload",
            "zero_adam_step_async", "zero_state_download", "zero_state_device_scale",
-           "zero_cpu_adam_step", "zero_cpu_isa", "Offload", "zero_last_error", "ZERO_F16",
+           "zero_cpu_adam_step", "zero_cpu_isa", "zero_adam_scalars", "SCALAR_FIELDS",
+           "Offload", "zero_last_error", "ZERO_F16",
            "ZERO_BF16", "ZERO_F32"]
 
 
@@ -426,6 +430,31 @@ def zero_cpu_isa() -> str:
     return lib.zero_cpu_isa().decode()
 
 
+SCALAR_FIELDS = ("inv_scale", "b1", "omb1", "b2", "omb2", "step", "rsbc2", "eps", "decay", "wd")
+
+
+def zero_adam_scalars(hparams: AdamHParams, t_first: int, count: int, loss_scale: float,
+                      out=None, stream=None):
+    """The update's fp32 scalars for steps t_first .. t_first + count - 1,
+    shape [count, 10] (columns SCALAR_FIELDS).  out=None: formed on the host
+    (a numpy array is returned); out a float32 device tensor of >= 10*count
+    elements: formed on the device as the asynchronous step forms them
+    (enqueued on `stream`)."""
+    hp = hparams.to_c()
+    if out is None:
+        import numpy as np
+        arr = np.zeros((max(count, 0), len(SCALAR_FIELDS)), np.float32)
+        check(lib.zero_adam_scalars(ctypes.byref(hp), int(t_first), int(count), float(loss_scale),
+                                    arr.ctypes.data, 0, None), "zero_adam_scalars")
+        return arr
+    torch = _torch()
+    _require(out, "out", 10 * count, (torch.float32,))
+    check(lib.zero_adam_scalars(ctypes.byref(hp), int(t_first), int(count), float(loss_scale),
+                                out.data_ptr(), 1, _stream_handle(stream, out.device)),
+          "zero_adam_scalars")
+    return out
+
+
 class Offload:
     """ZeRO-Offload pipeline of one rank (zero_offload_*): host-resident fp32
     master / moments, host update on a library thread, parameters copied
@@ -449,6 +478,7 @@ class Offload:
                                       *ptrs, int(n_threads), ctypes.byref(h)),
               "zero_offload_create")
         self._h = h
+        self._gcode = _GRAD_CODES[grad_dtype]
 
     def _stream(self, stream):
         torch = _torch()
@@ -457,6 +487,9 @@ class Offload:
     def submit(self, flat_grad, param=None, param_base: int = 0, stream=None) -> None:
         torch = _torch()
         _require(flat_grad, "flat_grad", self.plan.S, _grad_dtypes())
+        if _dtype_code(flat_grad) != self._gcode:
+            raise TypeError(f"flat_grad has dtype {flat_grad.dtype}; this offload copies "
+                            f"gradients of code {self._gcode}")
         pptr, pnum = None, 0
         if param is not None:
             _require(param, "param", 0, (torch.float16, torch.bfloat16))

@@ -102,6 +102,8 @@ SIGNATURES = {
     "zero_offload_drain": (ctypes.c_int, [_VP, _VP]),
     "zero_offload_stats": (ctypes.c_int, [_VP, ctypes.POINTER(zero_offload_stats_t)]),
     "zero_offload_destroy": (None, [_VP]),
+    "zero_adam_scalars": (ctypes.c_int, [ctypes.POINTER(zero_adam_hparams_t), _I64, _I64,
+                                         ctypes.c_double, _VP, _I32, _VP]),
     "zero_last_error": (ctypes.c_char_p, []),
     "zero_plan_set_timing": (ctypes.c_int, [_VP, _I32]),
     "zero_plan_kernel_ms": (ctypes.c_int, [_VP, _I32, ctypes.POINTER(ctypes.c_float)]),

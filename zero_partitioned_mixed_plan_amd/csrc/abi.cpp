@@ -2,6 +2,7 @@
 // device state of a plan, and kernel launches on the caller's stream.
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -14,18 +15,27 @@
 namespace zmi {
 
 namespace {
-thread_local std::string g_last_error;
+// The calling thread's last error message, in a fixed buffer: setting it
+// never allocates (the allocation-free step reports errors through it too).
+thread_local char g_last_error[512];
 }
 
-void set_error(const std::string& msg) { g_last_error = msg; }
+void set_error(const char* msg) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+}
 
-int fail(int code, const std::string& msg) {
+void set_error(const std::string& msg) { set_error(msg.c_str()); }
+
+int fail(int code, const char* msg) {
     set_error(msg);
     return code;
 }
 
+int fail(int code, const std::string& msg) { return fail(code, msg.c_str()); }
+
 int hip_fail(hipError_t e, const char* what) {
-    set_error(std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")");
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%s)", what, hipGetErrorName(e),
+                  hipGetErrorString(e));
     return ZERO_EHIP;
 }
 
@@ -39,7 +49,42 @@ int check_hparams(const zero_adam_hparams_t* hp) {
     return ZERO_OK;
 }
 
-namespace {
+// Whether every real gradient of flat_grad went through the flatten (and so
+// through its overflow test) since the last step; if not, the step scans.
+bool flatten_covered(const zero_plan* p, const void* flat_grad, int32_t grad_dtype) {
+    bool covered = p->flattened_into == flat_grad && p->flattened_dtype == grad_dtype;
+    if (covered && !p->flatten_all_done) {
+        for (int32_t b = 0; b < p->n_buckets && covered; ++b) {
+            if (p->bucket_seg_last[b] > p->bucket_seg_first[b] && !p->bucket_flattened[b]) {
+                covered = false;
+            }
+        }
+    }
+    return covered;
+}
+
+// The overflow decision for a step on flat_grad.  When the flattens since
+// the last step covered flat_grad, their fused test already raised the flag.
+// Otherwise the flag is cleared (it may hold what a flatten into another
+// buffer found) and the real elements [0, real) are scanned; the padding
+// [real, S) only feeds padding state, which never reaches a parameter.
+int gate_flag(zero_plan* p, const void* flat_grad, int32_t grad_dtype, hipStream_t s,
+              bool* scanned) {
+    *scanned = false;
+    if (flatten_covered(p, flat_grad, grad_dtype)) return ZERO_OK;
+    hipError_t e = launch_flag_clear(p->dev.d_flag, s);
+    if (e != hipSuccess) return hip_fail(e, "flag clear");
+    e = launch_scan(flat_grad, p->real, p->dev.d_flag, grad_dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+    *scanned = true;
+    return ZERO_OK;
+}
+
+void reset_flatten_bookkeeping(zero_plan* p) {
+    std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
+    p->flatten_all_done = false;
+    p->flattened_into = nullptr;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -52,6 +97,43 @@ bool valid_grad_dtype(int32_t d) { return valid_dtype(d) || d == ZERO_F32; }
 int bad_grad_dtype() {
     return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16, ZERO_BF16 or ZERO_F32");
 }
+
+// Parameter destination of shard element 0, after checking that the
+// caller's window [base, base + numel) covers the shard's real elements.
+int param_target(const zero_plan* p, void* param, int64_t base, int64_t numel, int32_t dtype,
+                 uint16_t** out) {
+    *out = nullptr;
+    if (param == nullptr) return ZERO_OK;
+    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "param_dtype must be ZERO_F16 or ZERO_BF16");
+    if ((reinterpret_cast<uintptr_t>(param) & 1u) != 0) {
+        return fail(ZERO_EALIGN, "param must be 2-byte aligned");
+    }
+    if (p->real <= 0) return ZERO_OK;  // a shard of padding writes no parameter
+    if (base < 0 || numel < 0 || p->begin < base || p->begin + p->real - base > numel) {
+        return fail(ZERO_EINVAL, "param window [param_base, param_base + param_numel) must "
+                                 "contain the shard's flat range [shard_begin, shard_begin + "
+                                 "real)");
+    }
+    *out = static_cast<uint16_t*>(param) + (p->begin - base);
+    return ZERO_OK;
+}
+
+// Checks shared by the synchronous and asynchronous steps.
+int check_step_buffers(const zero_plan* p, const void* flat_grad, int32_t grad_dtype,
+                       const float* master, const float* exp_avg, const float* exp_avg_sq) {
+    if (!valid_grad_dtype(grad_dtype)) return bad_grad_dtype();
+    if (p->S > 0 && (flat_grad == nullptr || master == nullptr || exp_avg == nullptr ||
+                     exp_avg_sq == nullptr)) {
+        return fail(ZERO_ENULL, "flat_grad, master, exp_avg and exp_avg_sq must be non-NULL");
+    }
+    if (!aligned16(flat_grad)) return fail(ZERO_EALIGN, "flat_grad must be 16-byte aligned");
+    if (!aligned4(master) || !aligned4(exp_avg) || !aligned4(exp_avg_sq)) {
+        return fail(ZERO_EALIGN, "master, exp_avg and exp_avg_sq must be 4-byte aligned");
+    }
+    return ZERO_OK;
+}
+
+namespace {
 
 // Binds the plan to the current device on first use and creates its device
 // block.  The overflow flag is cleared by a one-thread kernel on the first
@@ -134,24 +216,14 @@ int timer_stop(zero_plan* p, Timer t, hipStream_t s) {
     return ZERO_OK;
 }
 
-// Parameter destination of shard element 0, after checking that the
-// caller's window [base, base + numel) covers the shard's real elements.
-int param_target(const zero_plan* p, void* param, int64_t base, int64_t numel, int32_t dtype,
-                 uint16_t** out) {
-    *out = nullptr;
-    if (param == nullptr) return ZERO_OK;
-    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "param_dtype must be ZERO_F16 or ZERO_BF16");
-    if ((reinterpret_cast<uintptr_t>(param) & 1u) != 0) {
-        return fail(ZERO_EALIGN, "param must be 2-byte aligned");
-    }
-    if (p->real <= 0) return ZERO_OK;  // a shard of padding writes no parameter
-    if (base < 0 || numel < 0 || p->begin < base || p->begin + p->real - base > numel) {
-        return fail(ZERO_EINVAL, "param window [param_base, param_base + param_numel) must "
-                                 "contain the shard's flat range [shard_begin, shard_begin + "
-                                 "real)");
-    }
-    *out = static_cast<uint16_t*>(param) + (p->begin - base);
-    return ZERO_OK;
+// gate_flag with the scan, when it runs, timed like the other kernels.
+int timed_gate(zero_plan* p, const void* flat_grad, int32_t grad_dtype, hipStream_t s) {
+    if (flatten_covered(p, flat_grad, grad_dtype)) return ZERO_OK;
+    int rc = timer_start(p, kTimerScan, s);
+    if (rc != ZERO_OK) return rc;
+    bool scanned = false;
+    if ((rc = gate_flag(p, flat_grad, grad_dtype, s, &scanned)) != ZERO_OK) return rc;
+    return timer_stop(p, kTimerScan, s);
 }
 
 DeviceStep* device_step(zero_plan* p) {
@@ -171,35 +243,6 @@ int check_scaler(const zero_scaler_t* sc) {
         return fail(ZERO_EINVAL, "scaler fields out of range");
     }
     return ZERO_OK;
-}
-
-// Checks shared by the synchronous and asynchronous steps.
-int check_step_buffers(const zero_plan* p, const void* flat_grad, int32_t grad_dtype,
-                       const float* master, const float* exp_avg, const float* exp_avg_sq) {
-    if (!valid_grad_dtype(grad_dtype)) return bad_grad_dtype();
-    if (p->S > 0 && (flat_grad == nullptr || master == nullptr || exp_avg == nullptr ||
-                     exp_avg_sq == nullptr)) {
-        return fail(ZERO_ENULL, "flat_grad, master, exp_avg and exp_avg_sq must be non-NULL");
-    }
-    if (!aligned16(flat_grad)) return fail(ZERO_EALIGN, "flat_grad must be 16-byte aligned");
-    if (!aligned4(master) || !aligned4(exp_avg) || !aligned4(exp_avg_sq)) {
-        return fail(ZERO_EALIGN, "master, exp_avg and exp_avg_sq must be 4-byte aligned");
-    }
-    return ZERO_OK;
-}
-
-// Whether every real gradient of flat_grad went through the flatten (and so
-// through its overflow test) since the last step; if not, the step scans.
-bool flatten_covered(const zero_plan* p, const void* flat_grad, int32_t grad_dtype) {
-    bool covered = p->flattened_into == flat_grad && p->flattened_dtype == grad_dtype;
-    if (covered && !p->flatten_all_done) {
-        for (int32_t b = 0; b < p->n_buckets && covered; ++b) {
-            if (p->bucket_seg_last[b] > p->bucket_seg_first[b] && !p->bucket_flattened[b]) {
-                covered = false;
-            }
-        }
-    }
-    return covered;
 }
 
 // Host threads kept for zero_cpu_adam_step across calls (starting threads
@@ -230,17 +273,12 @@ int run_host_step(const CpuAdamArgs& a, int32_t overflow, int n_threads) {
         }
         pool = g_host_pool;
     }
+    // like the device gate, the test covers the real elements only
     const bool skip =
-        overflow < 0 ? cpu_nonfinite(a.g, a.n, a.gdt, n_threads, pool) : overflow != 0;
+        overflow < 0 ? cpu_nonfinite(a.g, a.real, a.gdt, n_threads, pool) : overflow != 0;
     if (skip) return 1;
     cpu_adam(a, n_threads, pool);
     return 0;
-}
-
-void reset_flatten_bookkeeping(zero_plan* p) {
-    std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
-    p->flatten_all_done = false;
-    p->flattened_into = nullptr;
 }
 
 }  // namespace
@@ -377,6 +415,14 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
     int rc = ensure_device(p, static_cast<hipStream_t>(stream));
     if (rc != ZERO_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // a flatten into another buffer (or dtype) than the one the pending
+    // flag belongs to starts the flag over: a step gates on what was found
+    // in the buffer it consumes
+    const bool retarget = p->flattened_into != flat_grad || p->flattened_dtype != grad_dtype;
+    if (retarget && p->flattened_into != nullptr) {
+        hipError_t e = launch_flag_clear(p->dev.d_flag, s);
+        if (e != hipSuccess) return hip_fail(e, "flag clear");
+    }
     if ((rc = timer_start(p, kTimerFlatten, s)) != ZERO_OK) return rc;
     // launches of up to kMaxPiecesPerLaunch contiguous pieces each
     size_t i = 0;
@@ -393,7 +439,7 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
     }
     if ((rc = timer_stop(p, kTimerFlatten, s)) != ZERO_OK) return rc;
     // bookkeeping for the gate: which buckets reached this flat buffer
-    if (p->flattened_into != flat_grad || p->flattened_dtype != grad_dtype) {
+    if (retarget) {
         std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
         p->flatten_all_done = false;
         p->flattened_into = flat_grad;
@@ -433,13 +479,7 @@ int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, 
                                         hp->adamw, static_cast<double>(step), loss_scale);
 
     // the gate needs every real gradient of this flat buffer tested
-    if (!flatten_covered(p, flat_grad, grad_dtype)) {
-        if ((rc = timer_start(p, kTimerScan, s)) != ZERO_OK) return rc;
-        hipError_t e = launch_scan(flat_grad, p->S, p->dev.d_flag,
-                                   grad_dtype, s);
-        if (e != hipSuccess) return hip_fail(e, "scan launch");
-        if ((rc = timer_stop(p, kTimerScan, s)) != ZERO_OK) return rc;
-    }
+    if ((rc = timed_gate(p, flat_grad, grad_dtype, s)) != ZERO_OK) return rc;
     if ((rc = timer_start(p, kTimerAdam, s)) != ZERO_OK) return rc;
     hipError_t e = launch_adam(flat_grad, master, exp_avg,
                                exp_avg_sq, param0, p->S, p->real, p->dev.d_flag, sc, nullptr,
@@ -551,13 +591,7 @@ int zero_adam_step_async(zero_plan_t* p, const zero_adam_hparams_t* hp, const vo
     rc = ensure_device(p, static_cast<hipStream_t>(stream));
     if (rc != ZERO_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!flatten_covered(p, flat_grad, grad_dtype)) {
-        if ((rc = timer_start(p, kTimerScan, s)) != ZERO_OK) return rc;
-        hipError_t e = launch_scan(flat_grad, p->S, p->dev.d_flag,
-                                   grad_dtype, s);
-        if (e != hipSuccess) return hip_fail(e, "scan launch");
-        if ((rc = timer_stop(p, kTimerScan, s)) != ZERO_OK) return rc;
-    }
+    if ((rc = timed_gate(p, flat_grad, grad_dtype, s)) != ZERO_OK) return rc;
     hipError_t e = launch_step_prologue(p->dev.d_flag, device_step(p), device_scalars(p), *hp, s);
     if (e != hipSuccess) return hip_fail(e, "step prologue launch");
     if ((rc = timer_start(p, kTimerAdam, s)) != ZERO_OK) return rc;
@@ -655,9 +689,37 @@ int zero_cpu_adam_step(const zero_plan_t* p, const zero_adam_hparams_t* hp, int6
     }
 }
 
+int zero_adam_scalars(const zero_adam_hparams_t* hp, int64_t t_first, int64_t count,
+                      double loss_scale, float* out, int32_t on_device, void* stream) {
+    if (hp == nullptr) return fail(ZERO_ENULL, "hparams is NULL");
+    int rc = check_hparams(hp);
+    if (rc != ZERO_OK) return rc;
+    if (t_first < 1 || count < 0 || count > (int64_t(1) << 40) - t_first) {
+        return fail(ZERO_EINVAL, "need t_first >= 1 and 0 <= count < 2^40 - t_first");
+    }
+    if (!(std::isfinite(loss_scale) && loss_scale > 0)) {
+        return fail(ZERO_EINVAL, "loss_scale must be finite and > 0");
+    }
+    if (on_device != 0 && on_device != 1) return fail(ZERO_EINVAL, "on_device must be 0 or 1");
+    if (count == 0) return ZERO_OK;
+    if (out == nullptr) return fail(ZERO_ENULL, "out is NULL");
+    if (!aligned4(out)) return fail(ZERO_EALIGN, "out must be 4-byte aligned");
+    auto* dst = reinterpret_cast<AdamScalars*>(out);
+    if (on_device) {
+        hipError_t e = launch_adam_scalars(*hp, t_first, count, loss_scale, dst,
+                                           static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? ZERO_OK : hip_fail(e, "scalars launch");
+    }
+    for (int64_t i = 0; i < count; ++i) {
+        dst[i] = make_scalars(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->adamw,
+                              static_cast<double>(t_first + i), loss_scale);
+    }
+    return ZERO_OK;
+}
+
 const char* zero_cpu_isa(void) { return cpu_isa_name(cpu_isa()); }
 
-const char* zero_last_error(void) { return g_last_error.c_str(); }
+const char* zero_last_error(void) { return g_last_error; }
 
 int zero_plan_set_timing(zero_plan_t* p, int32_t on) {
     if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");

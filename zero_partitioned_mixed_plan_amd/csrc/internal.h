@@ -20,7 +20,10 @@
 namespace zmi {
 
 // ---------------------------------------------------------------- errors
+// The message goes to a fixed per-thread buffer (setting it never allocates).
+void set_error(const char* msg);
 void set_error(const std::string& msg);
+int fail(int code, const char* msg);
 int fail(int code, const std::string& msg);
 int hip_fail(hipError_t e, const char* what);
 // ZERO_OK, or ZERO_EINVAL (with the message set) for hyperparameters out of
@@ -56,6 +59,7 @@ struct DeviceStep {
 struct AdamScalars {
     float inv_scale, b1, omb1, b2, omb2, step, rsbc2, eps, decay, wd;
 };
+static_assert(sizeof(AdamScalars) == 10 * sizeof(float), "scalars are ten packed floats");
 
 // What an offloaded step needs from the device: its overflow flag, its
 // bias-correction step and the loss scale its gradients carry.
@@ -155,6 +159,29 @@ namespace zmi {
 int build_plan(const int64_t* numels, int32_t n, int32_t R, int32_t r, int64_t A, int64_t B,
                zero_plan* p);
 
+// The gate of a step (or an offloaded step) on flat_grad: whether the
+// flattens since the last step covered every bucket of that buffer in that
+// dtype; if not, gate_flag clears the flag and scans the real elements on
+// `s` (*scanned = true).  reset_flatten_bookkeeping marks the flag consumed.
+bool flatten_covered(const zero_plan* p, const void* flat_grad, int32_t grad_dtype);
+int gate_flag(zero_plan* p, const void* flat_grad, int32_t grad_dtype, hipStream_t s,
+              bool* scanned);
+void reset_flatten_bookkeeping(zero_plan* p);
+
+// Argument checks shared by the entry points (ZERO_OK, or the error code
+// with the message set).
+bool aligned16(const void* p);
+bool aligned4(const void* p);
+bool valid_dtype(int32_t d);
+bool valid_grad_dtype(int32_t d);
+int bad_grad_dtype();
+// *out = the parameter destination of shard element 0 (nullptr when param
+// is NULL or the shard holds only padding), after checking the window.
+int param_target(const zero_plan* p, void* param, int64_t base, int64_t numel, int32_t dtype,
+                 uint16_t** out);
+int check_step_buffers(const zero_plan* p, const void* flat_grad, int32_t grad_dtype,
+                       const float* master, const float* exp_avg, const float* exp_avg_sq);
+
 // ---------------------------------------------------------------- kernels
 // One contiguous piece of the flat destination and where its source is:
 // element d of the flat shard (begin <= d < end) comes from
@@ -186,6 +213,10 @@ hipError_t launch_flag_clear(int* flag, hipStream_t s);
 hipError_t launch_step_prologue(const int* flag, const DeviceStep* st, AdamScalars* out,
                                 const zero_adam_hparams_t& hp, hipStream_t s);
 hipError_t launch_step_epilogue(int* flag, DeviceStep* st, hipStream_t s);
+// The scalars the prologue would form for steps t_first .. t_first + count
+// - 1 at loss scale `scale`, into out[0 .. count) (device memory).
+hipError_t launch_adam_scalars(const zero_adam_hparams_t& hp, int64_t t_first, int64_t count,
+                               double scale, AdamScalars* out, hipStream_t s);
 // Offloaded step: snapshot (flag, t + 1, scale) into *slot, apply the
 // loss-scale policy to the device state, clear the flag.
 hipError_t launch_offload_snapshot(int* flag, DeviceStep* st, OffloadSlot* slot, hipStream_t s);

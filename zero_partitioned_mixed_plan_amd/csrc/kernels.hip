@@ -377,15 +377,30 @@ write_param_kernel(const float* __restrict__ master, uint16_t* __restrict__ para
 
 __global__ void flag_clear_kernel(int* flag) { *flag = 0; }
 
+// The update scalars of bias-correction step t at loss scale `scale`, as the
+// device forms them (make_scalars with the device's pow and sqrt).
+__device__ __noinline__ AdamScalars device_scalars(const zero_adam_hparams_t& hp, int64_t t,
+                                                   double scale) {
+    return make_scalars(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.adamw,
+                        static_cast<double>(t), scale);
+}
+
 // One thread: the fp32 scalars of step t + 1 at the current loss scale, in
-// double and rounded once each (make_scalars), unless the flag says this
-// step is skipped.
+// double and rounded once each, unless the flag says this step is skipped.
 __global__ void step_prologue_kernel(const int* __restrict__ flag,
                                      const DeviceStep* __restrict__ st,
                                      AdamScalars* __restrict__ out, const zero_adam_hparams_t hp) {
     if (*flag != 0) return;
-    *out = make_scalars(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.adamw,
-                        static_cast<double>(st->t + 1), st->scale);
+    *out = device_scalars(hp, st->t + 1, st->scale);
+}
+
+// The scalars of steps t_first .. t_first + count - 1, one thread each,
+// formed exactly as the prologue forms them.
+__global__ void __launch_bounds__(kThreads)
+scalars_kernel(const zero_adam_hparams_t hp, int64_t t_first, int64_t count, double scale,
+               AdamScalars* __restrict__ out) {
+    const int64_t i = block_id() * kThreads + threadIdx.x;
+    if (i < count) out[i] = device_scalars(hp, t_first + i, scale);
 }
 
 // One thread: the loss-scale policy of zero_update_loss_scale on the device
@@ -547,6 +562,14 @@ hipError_t launch_flag_clear(int* flag, hipStream_t s) {
 hipError_t launch_step_prologue(const int* flag, const DeviceStep* st, AdamScalars* out,
                                 const zero_adam_hparams_t& hp, hipStream_t s) {
     hipLaunchKernelGGL(step_prologue_kernel, dim3(1), dim3(1), 0, s, flag, st, out, hp);
+    return hipGetLastError();
+}
+
+hipError_t launch_adam_scalars(const zero_adam_hparams_t& hp, int64_t t_first, int64_t count,
+                               double scale, AdamScalars* out, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    const dim3 grid = grid_2d((count + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(scalars_kernel, grid, dim3(kThreads), 0, s, hp, t_first, count, scale, out);
     return hipGetLastError();
 }
 

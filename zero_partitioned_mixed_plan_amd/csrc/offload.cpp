@@ -434,6 +434,13 @@ int zero_offload_submit(zero_offload_t* o, const void* flat_grad, void* param, i
     if (o == nullptr) return fail(ZERO_ENULL, "offload is NULL");
     zero_plan* p = o->plan;
     if (p->S > 0 && flat_grad == nullptr) return fail(ZERO_ENULL, "flat_grad is NULL");
+    if ((reinterpret_cast<uintptr_t>(flat_grad) & 15u) != 0) {
+        return fail(ZERO_EALIGN, "flat_grad must be 16-byte aligned");
+    }
+    if (p->flattened_into == flat_grad && p->flattened_dtype != o->gdt) {
+        return fail(ZERO_EINVAL, "flat_grad was flattened in another dtype than the offload's "
+                                 "grad_dtype");
+    }
     if (o->pdt != 0 && p->real > 0 && param == nullptr) {
         return fail(ZERO_ENULL, "param is NULL but the offload writes parameters");
     }
@@ -461,6 +468,10 @@ int zero_offload_submit(zero_offload_t* o, const void* flat_grad, void* param, i
     if (i >= 2 && (rc = wait_processed(o, i - 2)) != ZERO_OK) return rc;
     DeviceStep* st = reinterpret_cast<DeviceStep*>(reinterpret_cast<char*>(p->dev.d_flag) +
                                                    kStateOffset);
+    // the flag must cover every real gradient of this buffer, as in a device
+    // step: scanned here unless the flattens since the last step covered it
+    bool scanned = false;
+    if ((rc = gate_flag(p, flat_grad, o->gdt, s, &scanned)) != ZERO_OK) return rc;
     hipError_t e = launch_offload_snapshot(p->dev.d_flag, st, o->dslot + b, s);
     if (e != hipSuccess) return hip_fail(e, "snapshot launch");
     e = hipMemcpyAsync(o->hslot + b, o->dslot + b, sizeof(OffloadSlot), hipMemcpyDeviceToHost, s);
@@ -488,9 +499,7 @@ int zero_offload_submit(zero_offload_t* o, const void* flat_grad, void* param, i
     }
     o->cv.notify_all();
     // the flatten bookkeeping of this flat buffer is consumed
-    std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
-    p->flatten_all_done = false;
-    p->flattened_into = nullptr;
+    reset_flatten_bookkeeping(p);
     return ZERO_OK;
 }
 
