@@ -293,6 +293,34 @@ int zero_adam_step_async(zero_plan_t* plan, const zero_adam_hparams_t* hp, const
                          int32_t param_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * For callers that cannot allocate: code under HIP graph capture, serving
+ * loops and harnesses that forbid hipMalloc.
+ * ---------------------------------------------------------------------- */
+
+/* zero_adam_step with nothing allocated, created or waited for, by the call
+ * or by the plan.  Its overflow accumulator is a 256-byte device array of
+ * the library (one copy per device, held until the process ends); the call
+ * uses 4 bytes of it whatever the shard size, so no shard is rejected for
+ * its size.  Enqueued on `stream`: a kernel clears the accumulator, a scan
+ * of flat_grad's real elements [0, real) raises it on any inf/NaN, the
+ * update and cast of zero_adam_step run gated on it (same host scalars,
+ * same order, same rounding), and a one-thread kernel writes 1 (skipped) or
+ * 0 (applied) to *overflow_out.  It always scans: what zero_flatten_grads
+ * found since the last step is consumed unused, as a step would consume it
+ * (the plan's flag, if the plan has its device block, is cleared).
+ * overflow_out: DEVICE memory, 4-byte aligned, valid once `stream` reaches
+ * the end of the call.  Other arguments as in zero_adam_step.  Returns 0
+ * once the work is enqueued.  All calls on one device share the array: two
+ * calls that overlap in time on one device (other streams, other threads)
+ * race.  Errors: ZERO_ENULL, ZERO_EINVAL, ZERO_EALIGN, ZERO_EHIP,
+ * ZERO_ESTATE (the plan is bound to another device). */
+int zero_adam_step_noalloc(zero_plan_t* plan, const zero_adam_hparams_t* hp, int64_t step,
+                           double loss_scale, const void* flat_grad, int32_t grad_dtype,
+                           float* master, float* exp_avg, float* exp_avg_sq, void* param,
+                           int64_t param_base, int64_t param_numel, int32_t param_dtype,
+                           int32_t* overflow_out, void* stream);
+
+/* ------------------------------------------------------------------------
  * ZeRO-Offload: the rank's optimizer state in host memory, the update on
  * the host cores ([legal] offload list, CPU-offload bullet: optimizer states
  * in CPU DRAM, Adam on the CPU while the GPU runs forward and backward;

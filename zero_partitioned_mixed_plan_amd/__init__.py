@@ -22,6 +22,11 @@ and the step without host round trips (graph-capturable):
     zero_state_download(plan, stream=None) -> DeviceStepState
     zero_state_device_scale(plan) -> device address of the loss scale (double)
 
+and, for callers that cannot allocate, the step with nothing allocated or waited for:
+
+    zero_adam_step_noalloc(plan, hparams, step, loss_scale, flat_grad, master, exp_avg,
+                           exp_avg_sq, overflow_out, param=None, param_base=0, stream=None)
+
 and ZeRO-Offload's host-side update (host buffers: numpy arrays or CPU tensors):
 
     zero_cpu_adam_step(plan, hparams, step, loss_scale, flat_grad, master, exp_avg,
@@ -49,6 +54,7 @@ __all__ = ["Plan", "AdamHParams", "LossScaler", "DeviceStepState", "ZeroError",
            "zero_partition_plan", "GradList", "zero_flatten_grads", "zero_adam_step",
            "zero_update_loss_scale", "zero_write_param_shard", "zero_state_upload",
            "zero_adam_step_async", "zero_state_download", "zero_state_device_scale",
+           "zero_adam_step_noalloc",
            "zero_cpu_adam_step", "zero_cpu_isa", "zero_adam_scalars", "SCALAR_FIELDS",
            "Offload", "zero_last_error", "ZERO_F16",
            "ZERO_BF16", "ZERO_F32"]
@@ -354,6 +360,31 @@ def zero_adam_step_async(plan: Plan, hparams: AdamHParams, flat_grad, master, ex
                                    int(param_base), pnum, pdt,
                                    _stream_handle(stream, master.device)),
           "zero_adam_step_async")
+
+
+def zero_adam_step_noalloc(plan: Plan, hparams: AdamHParams, step: int, loss_scale: float,
+                           flat_grad, master, exp_avg, exp_avg_sq, overflow_out, param=None,
+                           param_base: int = 0, stream=None) -> None:
+    """zero_adam_step with nothing allocated and nothing waited for: the
+    flag (1 skipped, 0 applied) lands in overflow_out, an int32 device
+    tensor, when the stream reaches it."""
+    torch = _torch()
+    _require(flat_grad, "flat_grad", plan.S, _grad_dtypes())
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _require(t, name, plan.S, (torch.float32,))
+    _require(overflow_out, "overflow_out", 1, (torch.int32,))
+    pptr, pnum, pdt = None, 0, 0
+    if param is not None:
+        _require(param, "param", 0, (torch.float16, torch.bfloat16))
+        pptr, pnum, pdt = param.data_ptr(), param.numel(), _dtype_code(param)
+    hp = hparams.to_c()
+    check(lib.zero_adam_step_noalloc(plan.handle, ctypes.byref(hp), int(step), float(loss_scale),
+                                     flat_grad.data_ptr(), _dtype_code(flat_grad),
+                                     master.data_ptr(), exp_avg.data_ptr(),
+                                     exp_avg_sq.data_ptr(), pptr, int(param_base), pnum, pdt,
+                                     overflow_out.data_ptr(),
+                                     _stream_handle(stream, master.device)),
+          "zero_adam_step_noalloc")
 
 
 _HALF_CODES = {"f16": ZERO_F16, "bf16": ZERO_BF16, ZERO_F16: ZERO_F16, ZERO_BF16: ZERO_BF16}

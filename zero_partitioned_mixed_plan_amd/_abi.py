@@ -91,6 +91,9 @@ SIGNATURES = {
     "zero_state_device_scale": (ctypes.c_int, [_VP, ctypes.POINTER(_VP)]),
     "zero_adam_step_async": (ctypes.c_int, [_VP, ctypes.POINTER(zero_adam_hparams_t), _VP, _I32,
                                             _VP, _VP, _VP, _VP, _I64, _I64, _I32, _VP]),
+    "zero_adam_step_noalloc": (ctypes.c_int, [_VP, ctypes.POINTER(zero_adam_hparams_t), _I64,
+                                              ctypes.c_double, _VP, _I32, _VP, _VP, _VP, _VP,
+                                              _I64, _I64, _I32, _VP, _VP]),
     "zero_cpu_adam_step": (ctypes.c_int, [_VP, ctypes.POINTER(zero_adam_hparams_t), _I64,
                                           ctypes.c_double, _VP, _I32, _VP, _VP, _VP, _VP, _I64,
                                           _I64, _I32, _I32, _I32]),
