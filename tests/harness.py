@@ -11,7 +11,9 @@ computes is fed to the oracle.
 """
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence
 
@@ -181,6 +183,80 @@ REL_TOL = 1e-6   # fp32 master / moments
 ULP_TOL = 1      # half parameters
 
 
+def host_threads() -> int:
+    """Host threads for the oracle's chunked work (at most 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:   # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+_POOL = None
+
+
+def pool() -> ThreadPoolExecutor:
+    """Threads for elementwise oracle work over chunks (the oracle's C calls
+    release the interpreter lock; each chunk is the plain scalar loop)."""
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(host_threads())
+    return _POOL
+
+
+def chunk_ranges(n: int, size: int = 1 << 22):
+    return [(lo, min(n, lo + size)) for lo in range(0, n, size)]
+
+
+def float_to_half_chunked(x: np.ndarray, dtype: str) -> np.ndarray:
+    """oracle.float_to_half over chunks on the host threads."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.size, np.uint16)
+
+    def one(c):
+        out[c[0]:c[1]] = oracle.float_to_half(x[c[0]:c[1]], dtype)
+    list(pool().map(one, chunk_ranges(x.size)))
+    return out
+
+
+def cast_library(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 -> fp16 / bf16 bits by torch's CPU round-to-nearest-even
+    conversion, over chunks on the host threads.  The oracle's own cast
+    (oracle.float_to_half, written from IEEE 754) equals this conversion on
+    all 2^32 fp32 bit patterns except NaN payloads (tests/test_oracle_cast.py),
+    so for the multi-billion-element shards the expected parameters come
+    from the oracle's fp32 master through this faster, identical conversion."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.size, np.uint16)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+
+    def one(c):
+        lo, hi = c
+        out[lo:hi] = torch.from_numpy(x[lo:hi]).to(tdt).view(torch.int16).numpy().view(
+            np.uint16)
+    list(pool().map(one, chunk_ranges(x.size)))
+    return out
+
+
+def write_param_chunked(master: np.ndarray, real: int, begin: int, base: int,
+                        param: np.ndarray, pdt: str) -> None:
+    """oracle.write_param over chunks of the shard on the host threads: chunk
+    [lo, hi) of the shard writes param[begin + lo - base, begin + hi - base)."""
+    def one(c):
+        lo, hi = c
+        oracle.write_param(master[lo:hi], hi - lo, begin + lo, base, param, pdt)
+    list(pool().map(one, chunk_ranges(max(real, 0))))
+
+
+def same_bits(a: np.ndarray, b: np.ndarray) -> bool:
+    """Bit-for-bit equality of two equally typed arrays, over chunks."""
+    if a.shape != b.shape:
+        return False
+    return all(pool().map(lambda c: np.array_equal(a[c[0]:c[1]], b[c[0]:c[1]]),
+                          chunk_ranges(a.size)))
+
+
 class OracleRun:
     """The oracle's side of a case over the whole shard."""
 
@@ -216,7 +292,8 @@ class OracleRun:
         write-back is done once, when the buffer is looked at."""
         if getattr(self, "_param_stale", False):
             p = self.plan
-            oracle.write_param(self.master, p.real, p.begin, 0, self.param, self.case.param_dtype)
+            write_param_chunked(self.master, p.real, p.begin, 0, self.param,
+                                self.case.param_dtype)
             self._param_stale = False
         return self.param
 
@@ -339,17 +416,19 @@ def compare_state(gpu: "DeviceRun", orc: OracleRun, worst: dict, where: str) -> 
     case = orc.case
     gm, gmo, gv, gp, gf = gpu.state_host()
     S = orc.plan.S
-    assert np.array_equal(gf[:S], orc.flat), f"{where}: flat gradient shard differs"
+    assert same_bits(gf[:S], orc.flat), f"{where}: flat gradient shard differs"
     for name, a, b in (("master", gm[:S], orc.master), ("m", gmo[:S], orc.m),
                        ("v", gv[:S], orc.v)):
+        if same_bits(a.view(np.uint32), b.view(np.uint32)):
+            continue                      # identical bits: zero error
+        worst["bit_exact"] = False
         err = max_rel(a, b)
         worst[name] = max(worst[name], err)
-        if not np.array_equal(a.view(np.uint32), b.view(np.uint32)):
-            worst["bit_exact"] = False
         assert err <= REL_TOL, f"{where}: {name} max rel err {err}"
     if case.param_mode != "none":
-        du = ulp_diff(gp, orc.params())
-        worst["param_ulp"] = max(worst["param_ulp"], du)
-        if du:
+        want = orc.params()
+        if not same_bits(gp, want):
             worst["bit_exact"] = False
-        assert du <= ULP_TOL, f"{where}: params differ by {du} ulp"
+            du = ulp_diff(gp, want)
+            worst["param_ulp"] = max(worst["param_ulp"], du)
+            assert du <= ULP_TOL, f"{where}: params differ by {du} ulp"

@@ -55,7 +55,7 @@ def test_async_adam_variants_and_param_targets(adamw, param_mode):
 
 def test_async_gpt2_small_thirty_steps():
     case = Case.from_workload(get("gpt2_small"), steps=30)
-    assert _run(case, "gpt2_small", check_every=10)["bit_exact"]
+    assert _run(case, "gpt2_small", check_every=1)["bit_exact"]
 
 
 def _hip():
@@ -152,7 +152,7 @@ def test_async_fp32_gradients():
 
 def test_graph_replay_gpt2_small():
     case = Case.from_workload(get("gpt2_small"), steps=12)
-    worst = _graph_run(case, "gpt2_small", check_every=4)
+    worst = _graph_run(case, "gpt2_small", check_every=1)
     assert worst["bit_exact"]
 
 

@@ -104,7 +104,7 @@ def test_fp32_gradients_every_rank(align, pdt):
 
 def test_fp32_gradients_gpt2_small():
     case = Case.from_workload(get("gpt2_small"), grad_dtype="f32", steps=6)
-    worst = _run(case, "gpt2_small fp32 grads", check_every=3)
+    worst = _run(case, "gpt2_small fp32 grads", check_every=1)
     assert worst["bit_exact"]
 
 
@@ -159,5 +159,5 @@ def test_degenerate_hyperparameters(label, hp):
 def test_gpt2_small_full_shard_all_steps():
     w = get("gpt2_small")
     case = Case.from_workload(w)
-    worst = _run(case, "gpt2_small", check_every=10)
+    worst = _run(case, "gpt2_small", check_every=1)
     assert worst["bit_exact"]
