@@ -506,6 +506,18 @@ def copy_probe(nbytes, reps, device):
 
 
 def main(argv=None):
+    try:
+        return _main(argv)
+    finally:
+        # plans and pipelines are released here, while the HIP runtime and
+        # any profiler attached to it are fully alive, not by destructors
+        # during interpreter shutdown
+        z = sys.modules.get("zero_partitioned_mixed_plan_amd")
+        if z is not None:
+            z.release_all()
+
+
+def _main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)

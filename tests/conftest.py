@@ -34,3 +34,10 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # release the library's plans and pipelines before interpreter shutdown
+    z = sys.modules.get("zero_partitioned_mixed_plan_amd")
+    if z is not None:
+        z.release_all()

@@ -267,3 +267,61 @@ def test_adam_scalars_on_the_host():
     assert lib.zero_adam_scalars(ctypes.byref(hp), 1, 0, 1.0, None, 0, None) == _abi.ZERO_OK
     bad = z.AdamHParams(beta2=1.0).to_c()
     assert lib.zero_adam_scalars(ctypes.byref(bad), 1, 1, 1.0, ptr, 0, None) == _abi.ZERO_EINVAL
+
+
+def test_plans_are_released_explicitly_and_at_exit():
+    """close() releases a plan once (later calls fail with ZERO_ENULL);
+    release_all() releases every live plan; the binding registers it with
+    atexit, so nothing is left for a destructor during interpreter
+    finalization."""
+    import atexit
+    a = z.zero_partition_plan([1000, 24], 2, 0, 8)
+    b = z.zero_partition_plan([77], 1, 0, 1)
+    a.close()
+    a.close()                                    # idempotent
+    with pytest.raises(z.ZeroError):
+        a.segments()
+    assert b in z._LIVE_PLANS
+    z.release_all()
+    with pytest.raises(z.ZeroError):
+        b.tensor_buckets()
+    # the hook is registered: unregister returns quietly only for a known one
+    atexit.unregister(z.release_all)
+    atexit.register(z.release_all)
+
+
+_EXIT_SCRIPT = r"""
+import atexit, sys
+sys.path.insert(0, {root!r})
+import zero_partitioned_mixed_plan_amd as z
+calls = []
+real = z.Plan._destroy
+def spy(h):
+    print("destroy finalizing=%d" % sys.is_finalizing(), flush=True)
+    real(h)
+z.Plan._destroy = staticmethod(spy)
+if {unhook}:
+    atexit.unregister(z.release_all)
+KEEP = [z.zero_partition_plan([1000, 24], 2, 0, 8) for _ in range(3)]
+print("exiting", flush=True)
+"""
+
+
+@pytest.mark.parametrize("unhook", [False, True])
+def test_no_library_call_during_interpreter_finalization(unhook):
+    """Plans still referenced at exit: with the atexit hook they are released
+    before finalization (three destroys, none while finalizing); without it
+    their destructors make no library call at all while finalizing."""
+    import subprocess
+    import sys
+    code = _EXIT_SCRIPT.format(root=ROOT, unhook=unhook)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = r.stdout.split()
+    assert "exiting" in lines
+    out = r.stdout.splitlines()
+    destroys = [x for x in out if x.startswith("destroy")]
+    if unhook:
+        assert destroys == []
+    else:
+        assert destroys == ["destroy finalizing=0"] * 3

@@ -43,14 +43,17 @@ and ZeRO-Offload's host-side update (host buffers: numpy arrays or CPU tensors):
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
+import sys
+import weakref
 from dataclasses import dataclass
 from typing import List, Optional, Sequence
 
 from . import _abi
 from ._abi import ZERO_BF16, ZERO_F16, ZERO_F32, ZeroError, check, lib  # noqa: F401
 
-__all__ = ["Plan", "AdamHParams", "LossScaler", "DeviceStepState", "ZeroError",
+__all__ = ["Plan", "release_all", "AdamHParams", "LossScaler", "DeviceStepState", "ZeroError",
            "zero_partition_plan", "GradList", "zero_flatten_grads", "zero_adam_step",
            "zero_update_loss_scale", "zero_write_param_shard", "zero_state_upload",
            "zero_adam_step_async", "zero_state_download", "zero_state_device_scale",
@@ -133,24 +136,61 @@ class LossScaler:
         return int(self.c.good_steps)
 
 
+# Library handles not yet released.  release_all() runs from atexit, before
+# the interpreter finalizes anything, so no handle is left for a destructor
+# to free while the interpreter -- or the HIP runtime after it -- is being
+# torn down: pipeline threads are joined and device memory is freed while
+# everything is still alive.
+_LIVE_PLANS: "weakref.WeakSet[Plan]" = weakref.WeakSet()
+_LIVE_OFFLOADS: "weakref.WeakSet[Offload]" = weakref.WeakSet()
+
+
+def release_all() -> None:
+    """Release every live offload pipeline (its worker thread is joined),
+    then every live plan (its device block and pinned mirror are freed).
+    Registered with atexit; callers may also call it at the end of a run."""
+    for o in list(_LIVE_OFFLOADS):
+        o.close()
+    for p in list(_LIVE_PLANS):
+        p.close()
+
+
+atexit.register(release_all)
+
+
 class Plan:
-    """A partition plan handle (owned; released on garbage collection)."""
+    """A partition plan handle (owned): released by close(), by release_all()
+    at exit, or when collected before the interpreter finalizes."""
 
     def __init__(self, handle: int):
         self._h = ctypes.c_void_p(handle)
         info = _abi.zero_plan_info_t()
         check(lib.zero_plan_info(self._h, ctypes.byref(info)), "zero_plan_info")
         self.info = info
+        _LIVE_PLANS.add(self)
 
     # bound at class creation: module globals may already be gone when a
     # plan is collected at interpreter exit
     _destroy = staticmethod(lib.zero_plan_destroy)
+    _finalizing = staticmethod(sys.is_finalizing)
 
-    def __del__(self):
+    def close(self) -> None:
+        """Release the plan (and first any offload pipeline built on it).
+        Later calls that need the plan fail with ZERO_ENULL."""
         h = getattr(self, "_h", None)
         if h is not None and h.value:
+            for o in list(_LIVE_OFFLOADS):
+                if o.plan is self:
+                    o.close()
             self._destroy(h)
-            self._h = None
+        self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        # no HIP call once the interpreter is finalizing: release_all() ran
+        # at exit; what is left is reclaimed with the process
+        if self._finalizing():
+            return
+        self.close()
 
     @property
     def handle(self) -> ctypes.c_void_p:
@@ -510,6 +550,7 @@ class Offload:
               "zero_offload_create")
         self._h = h
         self._gcode = _GRAD_CODES[grad_dtype]
+        _LIVE_OFFLOADS.add(self)
 
     def _stream(self, stream):
         torch = _torch()
@@ -541,14 +582,18 @@ class Offload:
         return {k: getattr(st, k) for k, _ in st._fields_ if k != "_pad"}
 
     _destroy = staticmethod(lib.zero_offload_destroy)
+    _finalizing = staticmethod(sys.is_finalizing)
 
     def close(self) -> None:
+        """Complete the submitted steps, join the worker, free the buffers."""
         h = getattr(self, "_h", None)
         if h is not None and h.value:
             self._destroy(h)
-            self._h = None
+        self._h = ctypes.c_void_p()
 
     def __del__(self):
+        if self._finalizing():
+            return
         self.close()
 
 
