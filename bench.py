@@ -457,8 +457,12 @@ def cpu_baseline(w, plan_S, plan_begin, target_s=12.0, window=1 << 24):
             "gbps_equiv": rate * (adam_bytes(w.grad_dtype) + flatten_bytes(w.grad_dtype)) / 1e9}
 
 
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "adam_fused_llama2_70b_rank7_hbm_counters.md")
+PROFILES_DIR = os.path.join(ROOT, "profiles")
 KERNELS_SRC = os.path.join(ROOT, "zero_partitioned_mixed_plan_amd", "csrc", "kernels.hip")
+# Bytes per L2-to-memory request on MI355X, shown by a copy of known size
+# (profiles/*_hbm_requests.md): a read that is not a 32-byte request moves a
+# 128-byte line, a write request moves 64 bytes (or 32).
+READ_LINE_BYTES = 128
 
 
 def kernels_digest(path=KERNELS_SRC):
@@ -474,23 +478,29 @@ def kernels_digest(path=KERNELS_SRC):
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
-def counted_traffic(workload_name, grad_dtype="bf16"):
-    """HBM bytes per launch of the update kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary (copy-calibrated), or None when that
-    summary is for another workload or gradient dtype, or the kernels have
-    changed since."""
+def request_bytes(rdreq, rdreq_32b, wrreq, wrreq_64b):
+    """HBM bytes of TCC/EA request counts: reads at 128 (32) bytes, writes at
+    64 (32) bytes per request."""
+    reads = READ_LINE_BYTES * (rdreq - rdreq_32b) + 32 * rdreq_32b
+    writes = 64 * wrreq_64b + 32 * (wrreq - wrreq_64b)
+    return reads + writes
+
+
+def counted_traffic(workload_name, grad_dtype="bf16", kernel="adam"):
+    """HBM bytes per launch of the update (kernel="adam") or per call of the
+    flatten (kernel="flatten"), from the raw request counts in the committed
+    rocprofv3 summary for this workload and gradient dtype; None when there is
+    none, or the kernels have changed since it was taken."""
+    import glob
     import re
-    try:
-        text = open(COUNTERS_FILE).read()
-        digest = kernels_digest()
-    except OSError:
-        return None
-    vals = dict(re.findall(r"^(\w+) = (\S+)$", text, flags=re.M))
-    if vals.get("workload") != workload_name or vals.get("grad_dtype", "bf16") != grad_dtype:
-        return None
-    if vals.get("kernels_sha256") != digest:
-        return None
-    return int(vals["traffic_bytes_per_launch"])
+    digest = kernels_digest()
+    for path in sorted(glob.glob(os.path.join(PROFILES_DIR, "*_hbm_requests.md"))):
+        vals = dict(re.findall(r"^(\w+) = (\S+)$", open(path).read(), flags=re.M))
+        if (vals.get("workload") == workload_name and vals.get("grad_dtype") == grad_dtype
+                and vals.get("kernels_sha256") == digest):
+            return request_bytes(*(int(vals[f"{kernel}_{c}"])
+                                   for c in ("rdreq", "rdreq_32b", "wrreq", "wrreq_64b")))
+    return None
 
 
 def copy_probe(nbytes, reps, device):
@@ -624,7 +634,8 @@ def _main(argv=None):
                            "params_per_s": S / (adam_ms * 1e-3)},
             "flatten": {"avg_ms": flat_ms, "median_ms": statistics.median(times["flatten"]),
                         "min_ms": min(times["flatten"]),
-                        "bytes_per_elem": fb, "gbps": flat_gbs},
+                        "bytes_per_elem": fb, "gbps": flat_gbs,
+                        "traffic": counted_traffic(w.name, w.grad_dtype, "flatten")},
             "write_param": {"ms": write_ms, "bytes_per_elem": 6,
                             "gbps": 6 * real / (write_ms * 1e-3) / 1e9},
             "scan": {"ms": scan_ms, "bytes_per_elem": GRAD_BYTES[w.grad_dtype],

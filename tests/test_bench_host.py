@@ -1,8 +1,8 @@
 """bench.py's host-side bookkeeping, on the CPU: the algorithmic byte counts
 it prices the kernels at, the kernel-source digest that gates the counted
-HBM traffic, and that the committed counter summaries were taken with the
-kernel source as it stands (so a GPU run reports `traffic` rather than
-null)."""
+HBM traffic, the pricing of raw memory-request counts, and that the
+committed counter summaries were taken with the kernel source as it stands
+(so a GPU run reports `traffic` rather than null)."""
 import os
 import re
 import subprocess
@@ -32,22 +32,33 @@ def test_digest_ignores_comments_and_blank_lines(tmp_path):
     commented.write_text("// a new comment\n\n" + src.replace("\n", "  // trailing note\n", 3))
     assert bench.kernels_digest(str(commented)) == base
     changed = tmp_path / "b.hip"
-    changed.write_text(src.replace("kAdamThreads = 128", "kAdamThreads = 256", 1))
-    assert "kAdamThreads = 128" in src
+    changed.write_text(src.replace("kAdamSpan = 256", "kAdamSpan = 512", 1))
+    assert "kAdamSpan = 256" in src
     assert bench.kernels_digest(str(changed)) != base
 
 
-def test_counter_summary_matches_the_kernel_source():
-    # the committed FETCH_SIZE / WRITE_SIZE summary is for this kernel source
-    # and the default workload, and its bytes are the update's 28 B x S
-    traffic = bench.counted_traffic("llama2_70b", "bf16")
-    assert traffic is not None, "kernels.hip changed since profiles/ counters were taken"
-    w = get("llama2_70b")
-    plan = z.zero_partition_plan(w.numels, w.world_size, w.rank, w.align, w.bucket_elems)
-    alg = bench.adam_bytes("bf16") * plan.S
-    assert abs(traffic / alg - 1) < 1e-3
-    assert bench.counted_traffic("llama3_8b", "bf16") is None
+def test_counter_summaries_match_the_kernel_source():
+    # the committed raw request counts are for this kernel source; priced at
+    # the request sizes (128-byte read lines, 64-byte writes) they give the
+    # update's 28 B x S on every large workload and the flatten's 4 B x S
+    # (the 20B shard's misaligned pieces re-read ~2.3% of their lines)
+    for name, flat_tol in (("llama2_70b", 1e-4), ("llama3_8b", 1e-4), ("dna_20b", 0.03)):
+        w = get(name)
+        plan = z.zero_partition_plan(w.numels, w.world_size, w.rank, w.align, w.bucket_elems)
+        adam = bench.counted_traffic(name, w.grad_dtype)
+        assert adam is not None, f"{name}: kernels.hip changed since profiles/ counters were taken"
+        assert abs(adam / (bench.adam_bytes(w.grad_dtype) * plan.S) - 1) < 1e-5, name
+        flat = bench.counted_traffic(name, w.grad_dtype, "flatten")
+        assert 0 <= flat / (bench.flatten_bytes(w.grad_dtype) * plan.S) - 1 < flat_tol, name
     assert bench.counted_traffic("llama2_70b", "f32") is None
+    assert bench.counted_traffic("gpt2_small", "bf16") is None
+
+
+def test_request_bytes():
+    # reads priced at a 128-byte line (32 for 32-byte requests), writes at 64
+    # (32 for the rest): a 4 GiB copy's counts give its 4 GiB each way
+    assert bench.request_bytes(1 << 25, 0, 1 << 26, 1 << 26) == 2 * (4 << 30)
+    assert bench.request_bytes(10, 4, 10, 6) == 6 * 128 + 4 * 32 + 6 * 64 + 4 * 32
 
 
 def test_every_profile_names_the_current_kernel_source():

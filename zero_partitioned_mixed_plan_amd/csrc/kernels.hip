@@ -13,11 +13,12 @@
 //     chunks) was 1-10% slower than plain address order.
 //   * the update uses 2- and 4-byte accesses (128-256 contiguous bytes per
 //     wave instruction), not 8- or 16-byte vectors: with four read and four
-//     write streams, vector accesses were 5-15% slower.  On a 70B-class
-//     shard (8.6e9 elements) the best shape was 128-thread workgroups with
-//     two elements per thread, t and t + 128, both loaded before the math:
-//     37.1 ms vs 38.2 ms for 256 threads x 1 element, 37.6 ms for 256 x 4
-//     and 38.1 ms for 64 x 2 (same box, same run).
+//     write streams, vector accesses were 5-15% slower.  A workgroup updates
+//     256 consecutive elements.  On a 70B-class shard (8.6e9 elements) the
+//     best shape was 128 threads with two elements each, t and t + 128,
+//     both loaded before the math: 37.1 ms vs 38.2 ms for 256 threads x 1
+//     element, 37.6 ms for 256 x 4 and 38.1 ms for 64 x 2 (same box, same
+//     run).  Below 7.5e9 elements 256 x 1 is faster (see adam_dispatch_d).
 //   * non-temporal loads and stores (the streaming cache policy) on the
 //     three fp32 state arrays, plain accesses for the gradient (half, or
 //     fp32 when gradients are kept in fp32) and the half parameter: +3-6%
@@ -59,9 +60,11 @@ constexpr int64_t kTile = kThreads * kVec;  // 2048 words per workgroup and vect
 constexpr int kFlatV = 2;                   // 16-byte vectors per thread in flatten
 constexpr int64_t kFlatTile = kTile * kFlatV;  // flatten tile: 4096 16-bit words
 constexpr int64_t kGridX = 65536;           // x extent of the 2-D grids
-constexpr int kAdamThreads = 128;           // update: two waves per workgroup,
-constexpr int kAdamPer = 2;                 // two elements per thread,
-constexpr int64_t kAdamSpan = kAdamThreads * kAdamPer;  // 256 elements per workgroup
+// update: 256 consecutive elements per workgroup, in one of two shapes (the
+// launcher picks by shard size): 256 threads x 1 element, or 128 threads x
+// 2 elements (t and t + 128)
+constexpr int64_t kAdamSpan = 256;
+constexpr int64_t kAdamBigShard = 7500000000LL;  // from here on: 128 x 2
 constexpr int kWritePer = 8;                // parameter cast: elements per thread,
 constexpr int64_t kWriteSpan = kThreads * kWritePer;  // 2048 per workgroup
 
@@ -173,18 +176,33 @@ __device__ __forceinline__ const __attribute__((address_space(1))) T* global_ptr
 // element 0 is read from byte address src0 (uniform over the workgroup);
 // vector j of lane t starts at src0 + 16 (t + j * kThreads).  An aligned
 // source is read with the streaming (non-temporal) policy.  A misaligned
-// one is read as two aligned blocks per vector, each block also read by the
-// neighbouring lane: plain loads keep that second read a cache hit
-// (non-temporal loads cost ~9% there).  Both blocks hold wanted elements of
-// the tile, so no read leaves the source allocation.
+// one straddles two aligned blocks: the lane's own block (lo) and the next
+// lane's (hi).  Each lane loads its lo block (non-temporal) and takes hi
+// from its neighbour with a cross-lane permute (ds_bpermute, no LDS
+// memory); only the last lane of each wave loads its hi block itself.
+// That halves the loads of a misaligned tile (1.5% faster on a shard of 300
+// mostly misaligned pieces than a second load per lane).  Every block read
+// holds wanted elements of the tile, so no read leaves the source allocation.
 template <int MIS>
 __device__ __forceinline__ void load_tile_mis(const __attribute__((address_space(1))) u32x4* blk,
                                               u32x4 (&q)[kFlatV]) {
     u32x4 lo[kFlatV], hi[kFlatV];
+    const int lane = static_cast<int>(threadIdx.x & 63);
+    const bool last = lane == 63;
 #pragma unroll
     for (int j = 0; j < kFlatV; ++j) {
-        lo[j] = blk[j * kThreads];
-        hi[j] = blk[j * kThreads + 1];
+        lo[j] = __builtin_nontemporal_load(blk + j * kThreads);
+        if (last) hi[j] = blk[j * kThreads + 1];
+    }
+    const int from = (lane + 1) << 2;  // byte address of the next lane (wraps at 64)
+#pragma unroll
+    for (int j = 0; j < kFlatV; ++j) {
+        u32x4 nb;
+        nb.x = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(from, static_cast<int>(lo[j].x)));
+        nb.y = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(from, static_cast<int>(lo[j].y)));
+        nb.z = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(from, static_cast<int>(lo[j].z)));
+        nb.w = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(from, static_cast<int>(lo[j].w)));
+        if (!last) hi[j] = nb;
     }
 #pragma unroll
     for (int j = 0; j < kFlatV; ++j) q[j] = realign<MIS>(lo[j], hi[j]);
@@ -317,23 +335,25 @@ __device__ __forceinline__ void adam_elem(float g, float& p, float& m, float& v,
 
 // GDT: gradient dtype.  PDT: parameter dtype, 0 = no parameter write.
 // DEVSC: the scalars come from device memory (asynchronous step) instead of
-// the kernel arguments.  A 128-thread workgroup (two waves) updates
-// kAdamSpan = 256 consecutive elements; thread t takes elements t and
-// t + 128 and issues the loads of both before any arithmetic.
-template <int GDT, int PDT, bool ADAMW, bool DEVSC>
-__global__ void __launch_bounds__(kAdamThreads)
+// the kernel arguments.  A workgroup of THREADS threads updates kAdamSpan =
+// 256 consecutive elements; thread t takes elements t + j * THREADS for
+// j < 256 / THREADS and issues the loads of all of them before any
+// arithmetic.
+template <int GDT, int PDT, bool ADAMW, bool DEVSC, int THREADS>
+__global__ void __launch_bounds__(THREADS)
 adam_kernel(const void* __restrict__ g, float* __restrict__ master, float* __restrict__ mom,
             float* __restrict__ var, uint16_t* __restrict__ param, int64_t S, int64_t real,
             const int* __restrict__ flag, const AdamScalars c_arg,
             const AdamScalars* __restrict__ c_dev) {
+    constexpr int PER = static_cast<int>(kAdamSpan / THREADS);
     if (*flag != 0) return;  // overflow: the step is skipped, nothing is written
     const AdamScalars c = DEVSC ? *c_dev : c_arg;
     const int64_t k0 = block_id() * kAdamSpan + threadIdx.x;
-    float p[kAdamPer], m[kAdamPer], v[kAdamPer];
-    uint32_t h[kAdamPer];
+    float p[PER], m[PER], v[PER];
+    uint32_t h[PER];
 #pragma unroll
-    for (int j = 0; j < kAdamPer; ++j) {
-        const int64_t k = k0 + j * kAdamThreads;
+    for (int j = 0; j < PER; ++j) {
+        const int64_t k = k0 + j * THREADS;
         if (k < S) {
             p[j] = __builtin_nontemporal_load(master + k);
             m[j] = __builtin_nontemporal_load(mom + k);
@@ -343,8 +363,8 @@ adam_kernel(const void* __restrict__ g, float* __restrict__ master, float* __res
         }
     }
 #pragma unroll
-    for (int j = 0; j < kAdamPer; ++j) {
-        const int64_t k = k0 + j * kAdamThreads;
+    for (int j = 0; j < PER; ++j) {
+        const int64_t k = k0 + j * THREADS;
         if (k < S) {
             adam_elem<ADAMW>(grad_to_f32<GDT>(h[j]), p[j], m[j], v[j], c);
             __builtin_nontemporal_store(p[j], master + k);
@@ -429,16 +449,33 @@ __global__ void offload_snapshot_kernel(int* __restrict__ flag, DeviceStep* __re
     *flag = 0;
 }
 
+template <int GDT, int PDT, bool ADAMW, int THREADS>
+void adam_launch(const AdamScalars* dsc, dim3 grid, hipStream_t s, const void* g, float* master,
+                 float* m, float* v, uint16_t* param, int64_t S, int64_t real, const int* flag,
+                 const AdamScalars& sc) {
+    if (dsc != nullptr) {
+        hipLaunchKernelGGL((adam_kernel<GDT, PDT, ADAMW, true, THREADS>), grid, dim3(THREADS), 0,
+                           s, g, master, m, v, param, S, real, flag, sc, dsc);
+    } else {
+        hipLaunchKernelGGL((adam_kernel<GDT, PDT, ADAMW, false, THREADS>), grid, dim3(THREADS), 0,
+                           s, g, master, m, v, param, S, real, flag, sc, dsc);
+    }
+}
+
+// Shape by shard size (same box, same buffers, HIP events; bf16 update,
+// fp32 state): 256 x 1 ran 2-5% faster than 128 x 2 from 1e9 to 4e9
+// elements and matched it at 7e9, but 1.3-1.5% slower at 8.6e9.  The
+// 128 x 2 shape was also 3-4% slower at 1e9 and 2.5e9 when the arrays were
+// the process's first allocations than after 100 GB of other buffers, which
+// did not move 256 x 1.
 template <int GDT, int PDT, bool ADAMW>
 hipError_t adam_dispatch_d(const AdamScalars* dsc, dim3 grid, hipStream_t s, const void* g,
                            float* master, float* m, float* v, uint16_t* param, int64_t S,
                            int64_t real, const int* flag, const AdamScalars& sc) {
-    if (dsc != nullptr) {
-        hipLaunchKernelGGL((adam_kernel<GDT, PDT, ADAMW, true>), grid, dim3(kAdamThreads), 0, s, g,
-                           master, m, v, param, S, real, flag, sc, dsc);
+    if (S >= kAdamBigShard) {
+        adam_launch<GDT, PDT, ADAMW, 128>(dsc, grid, s, g, master, m, v, param, S, real, flag, sc);
     } else {
-        hipLaunchKernelGGL((adam_kernel<GDT, PDT, ADAMW, false>), grid, dim3(kAdamThreads), 0, s,
-                           g, master, m, v, param, S, real, flag, sc, dsc);
+        adam_launch<GDT, PDT, ADAMW, 256>(dsc, grid, s, g, master, m, v, param, S, real, flag, sc);
     }
     return hipGetLastError();
 }
