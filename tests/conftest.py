@@ -20,6 +20,11 @@ def pytest_configure(config):
     if not all(os.path.exists(p) for p in _LIBS):
         import __graft_entry__
         __graft_entry__.build()
+    tests_dir = os.path.dirname(os.path.abspath(__file__))
+    if tests_dir not in sys.path:
+        sys.path.insert(0, tests_dir)
+    import harness
+    harness.CAPTURE_MANAGER = config.pluginmanager.getplugin("capturemanager")
 
 
 def pytest_collection_modifyitems(config, items):

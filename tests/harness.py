@@ -27,7 +27,17 @@ INF_BITS = {"f16": 0x7C00, "bf16": 0x7F80, "f32": 0x7F800000}
 GRAD_WORD = {"f16": np.uint16, "bf16": np.uint16, "f32": np.uint32}
 
 
+# pytest's capture manager, set by conftest.py: progress lines of the long
+# GPU tests go around the output capture, so a run under `pytest -q` prints
+# them as they happen (a multi-minute test is never silent).
+CAPTURE_MANAGER = None
+
+
 def log(msg: str) -> None:
+    if CAPTURE_MANAGER is not None:
+        with CAPTURE_MANAGER.global_and_fixture_disabled():
+            print(msg, flush=True)
+        return
     print(msg, flush=True)
     sys.stdout.flush()
 
