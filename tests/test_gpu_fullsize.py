@@ -700,7 +700,9 @@ def _whole_shard(case, label, step_mode="sync"):
 
 
 def test_llama3_8b_rank3_whole_shard_every_step():
-    case = Case.from_workload(get("llama3_8b"), steps=4)
+    # all 20 steps of the workload, with its 1% x100 outliers
+    case = Case.from_workload(get("llama3_8b"))
+    assert case.steps == 20
     assert _whole_shard(case, "llama3_8b") == 0
 
 
