@@ -11,6 +11,11 @@
 // (synth/synth_host.c); the fp32 -> half rounding of the inputs uses the
 // compiler's _Float16 / __bf16 conversions (IEEE round to nearest even).
 //
+// The fp16 and fp32-gradient cases run a second time with the gated update
+// through zero_adam_step_noalloc (the flag read from the caller's device
+// int), and the update scalars that zero_adam_scalars forms on the device
+// are compared with the host's for t = 1..4096.
+//
 // Prints "c-abi ok" and exits 0 on success; prints the first mismatch and
 // exits 1 otherwise.
 #include <hip/hip_runtime_api.h>
@@ -89,7 +94,9 @@ uint32_t grad_word(float x, int dt) {
     return to_half(x, dt);
 }
 
-int run_case(int gdt, int pdt, int adamw) {
+// noalloc = 1: the step goes through zero_adam_step_noalloc instead of
+// zero_adam_step.
+int run_case(int gdt, int pdt, int adamw, int noalloc) {
     const size_t esize = gdt == ZERO_F32 ? 4 : 2;
     const std::vector<int64_t> numels = {3000, 1, 7, 100003, 65, 2048, 511, 30000, 13};
     const int R = 3, r = 1, A = 8, steps = 8, inject_step = 3;
@@ -124,6 +131,8 @@ int run_case(int gdt, int pdt, int adamw) {
     for (int i = 0; i < n; ++i) HIP_OK(hipMalloc(&d_grads[i], esize * numels[i]));
     void *d_flat, *d_param;
     float *d_master, *d_m, *d_v;
+    int32_t* d_flag = nullptr;
+    HIP_OK(hipMalloc(reinterpret_cast<void**>(&d_flag), sizeof(int32_t)));
     HIP_OK(hipMalloc(&d_flat, esize * S));
     HIP_OK(hipMalloc(&d_param, 2 * P));
     HIP_OK(hipMalloc(reinterpret_cast<void**>(&d_master), 4 * S));
@@ -186,8 +195,19 @@ int run_case(int gdt, int pdt, int adamw) {
         std::vector<const void*> dg(d_grads.begin(), d_grads.end());
         ZERO_OK_OR_FAIL(zero_flatten_grads(plan, -1, dg.data(), gdt, d_flat, s));
         const double scale_used = scaler.scale;
-        const int flag = zero_adam_step(plan, &hp, t + 1, scale_used, d_flat, gdt, d_master, d_m,
-                                        d_v, d_param, 0, P, pdt, s);
+        int flag = 0;
+        if (noalloc) {
+            ZERO_OK_OR_FAIL(zero_adam_step_noalloc(plan, &hp, t + 1, scale_used, d_flat, gdt,
+                                                   d_master, d_m, d_v, d_param, 0, P, pdt,
+                                                   d_flag, s));
+            int32_t h_flag = -1;
+            HIP_OK(hipStreamSynchronize(s));
+            HIP_OK(hipMemcpy(&h_flag, d_flag, sizeof(h_flag), hipMemcpyDeviceToHost));
+            flag = h_flag;
+        } else {
+            flag = zero_adam_step(plan, &hp, t + 1, scale_used, d_flat, gdt, d_master, d_m, d_v,
+                                  d_param, 0, P, pdt, s);
+        }
         ZERO_OK_OR_FAIL(flag);
         ZERO_OK_OR_FAIL(zero_update_loss_scale(&scaler, flag));
         if (!flag) ++t;
@@ -237,6 +257,7 @@ int run_case(int gdt, int pdt, int adamw) {
         return 1;
     }
     for (void* p : d_grads) HIP_OK(hipFree(p));
+    HIP_OK(hipFree(d_flag));
     HIP_OK(hipFree(d_flat));
     HIP_OK(hipFree(d_param));
     HIP_OK(hipFree(d_master));
@@ -244,18 +265,41 @@ int run_case(int gdt, int pdt, int adamw) {
     HIP_OK(hipFree(d_v));
     HIP_OK(hipStreamDestroy(s));
     zero_plan_destroy(plan);
-    std::printf("case gdt=%d pdt=%d adamw=%d: %d steps, %lld applied, scale %g\n", gdt, pdt,
-                adamw, steps,
+    std::printf("case gdt=%d pdt=%d adamw=%d%s: %d steps, %lld applied, scale %g\n", gdt, pdt,
+                adamw, noalloc ? " (allocation-free step)" : "", steps,
                 static_cast<long long>(t), scaler.scale);
+    return 0;
+}
+
+// zero_adam_scalars: the device's scalars equal the host's, bit for bit.
+int scalars_case() {
+    const int64_t n = 4096;
+    const zero_adam_hparams_t hp = {3e-4, 0.95, 0.98, 1e-6, 0.1, 1, 0};
+    std::vector<float> host(10 * n), dev(10 * n);
+    ZERO_OK_OR_FAIL(zero_adam_scalars(&hp, 1, n, 65536.0, host.data(), 0, nullptr));
+    float* d_out = nullptr;
+    HIP_OK(hipMalloc(reinterpret_cast<void**>(&d_out), sizeof(float) * 10 * n));
+    ZERO_OK_OR_FAIL(zero_adam_scalars(&hp, 1, n, 65536.0, d_out, 1, nullptr));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(dev.data(), d_out, sizeof(float) * 10 * n, hipMemcpyDeviceToHost));
+    HIP_OK(hipFree(d_out));
+    if (std::memcmp(host.data(), dev.data(), sizeof(float) * 10 * n) != 0) {
+        std::printf("device and host update scalars differ\n");
+        return 1;
+    }
+    std::printf("update scalars: device = host for t = 1..%lld\n", static_cast<long long>(n));
     return 0;
 }
 
 }  // namespace
 
 int main() {
-    if (run_case(ZERO_F16, ZERO_F16, 1) != 0) return 1;
-    if (run_case(ZERO_BF16, ZERO_BF16, 0) != 0) return 1;
-    if (run_case(ZERO_F32, ZERO_F16, 1) != 0) return 1;
+    if (run_case(ZERO_F16, ZERO_F16, 1, 0) != 0) return 1;
+    if (run_case(ZERO_BF16, ZERO_BF16, 0, 0) != 0) return 1;
+    if (run_case(ZERO_F32, ZERO_F16, 1, 0) != 0) return 1;
+    if (run_case(ZERO_F16, ZERO_F16, 1, 1) != 0) return 1;
+    if (run_case(ZERO_F32, ZERO_F16, 1, 1) != 0) return 1;
+    if (scalars_case() != 0) return 1;
     std::printf("c-abi ok\n");
     return 0;
 }

@@ -1,6 +1,9 @@
 """The C ABI without Python: tests/c_abi_check (C++, hipMalloc'ed buffers,
-built by __graft_entry__.build()) runs three cases through include/zero_mi355x.h
-and compares every step with the C oracle bit for bit (see its header)."""
+built by __graft_entry__.build()) runs five cases through include/zero_mi355x.h
+-- three through zero_adam_step, two through zero_adam_step_noalloc -- and
+compares every step with the C oracle bit for bit, then compares the update
+scalars zero_adam_scalars forms on the device with the host's (see its
+header)."""
 import os
 import subprocess
 
@@ -16,3 +19,4 @@ def test_c_abi_program_matches_the_oracle():
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
     print(r.stdout)
     assert r.returncode == 0 and "c-abi ok" in r.stdout, r.stdout + r.stderr
+    assert r.stdout.count("(allocation-free step)") == 2 and "device = host" in r.stdout
