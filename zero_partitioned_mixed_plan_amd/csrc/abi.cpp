@@ -418,10 +418,18 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
     // a flatten into another buffer (or dtype) than the one the pending
     // flag belongs to starts the flag over: a step gates on what was found
     // in the buffer it consumes
-    const bool retarget = p->flattened_into != flat_grad || p->flattened_dtype != grad_dtype;
-    if (retarget && p->flattened_into != nullptr) {
-        hipError_t e = launch_flag_clear(p->dev.d_flag, s);
-        if (e != hipSuccess) return hip_fail(e, "flag clear");
+    if (p->flattened_into != flat_grad || p->flattened_dtype != grad_dtype) {
+        if (p->flattened_into != nullptr) {
+            hipError_t e = launch_flag_clear(p->dev.d_flag, s);
+            if (e != hipSuccess) return hip_fail(e, "flag clear");
+        }
+        // the bookkeeping follows the new buffer before anything is launched
+        // into it, so a launch that fails below leaves it uncovered (a step
+        // on it scans), never the previous buffer covered by a cleared flag
+        std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
+        p->flatten_all_done = false;
+        p->flattened_into = flat_grad;
+        p->flattened_dtype = grad_dtype;
     }
     if ((rc = timer_start(p, kTimerFlatten, s)) != ZERO_OK) return rc;
     // launches of up to kMaxPiecesPerLaunch contiguous pieces each
@@ -439,12 +447,6 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
     }
     if ((rc = timer_stop(p, kTimerFlatten, s)) != ZERO_OK) return rc;
     // bookkeeping for the gate: which buckets reached this flat buffer
-    if (retarget) {
-        std::fill(p->bucket_flattened.begin(), p->bucket_flattened.end(), 0);
-        p->flatten_all_done = false;
-        p->flattened_into = flat_grad;
-        p->flattened_dtype = grad_dtype;
-    }
     if (bucket < 0) {
         p->flatten_all_done = true;
     } else {
