@@ -229,7 +229,7 @@ def float_to_half_chunked(x: np.ndarray, dtype: str) -> np.ndarray:
     return out
 
 
-def cast_library(x: np.ndarray, dtype: str) -> np.ndarray:
+def cast_library(x: np.ndarray, dtype: str, parallel: bool = True) -> np.ndarray:
     """fp32 -> fp16 / bf16 bits by torch's CPU round-to-nearest-even
     conversion, over chunks on the host threads.  The oracle's own cast
     (oracle.float_to_half, written from IEEE 754) equals this conversion on
@@ -245,7 +245,10 @@ def cast_library(x: np.ndarray, dtype: str) -> np.ndarray:
         lo, hi = c
         out[lo:hi] = torch.from_numpy(x[lo:hi]).to(tdt).view(torch.int16).numpy().view(
             np.uint16)
-    list(pool().map(one, chunk_ranges(x.size)))
+    if parallel:
+        list(pool().map(one, chunk_ranges(x.size)))
+    else:                      # the caller already runs on one of several threads
+        one((0, x.size))
     return out
 
 

@@ -1,27 +1,39 @@
 """GPU vs oracle parity at the workloads' full sizes (and one tensor past 2^31
 elements).
 
-Whole shard (the _whole_shard tests): every element of the flat gradients,
-master, moments and parameters after every step, on the Llama-3-8B, 20B
-DNA-LM and Llama-2-70B shards (the last when the host has the ~125 GB the
-oracle's state takes).
+Whole shards (the _whole_shard runs): every element of the flat gradients,
+master, moments and parameters after every step, and the flag and loss
+scale, for the full-length runs of the large workloads in bench.py's launch
+configuration: Llama-3-8B rank 3 (20 steps; all buckets at once, bucket by
+bucket, graph-replayed; and 6 steps with fp32 gradients), the 20B DNA-LM
+rank 2 (50 steps with the workload's injected infs, 25 of them graph-
+replayed with the device-side scaler, and 3 steps with a +inf past 2^31),
+Llama-2-70B rank 7 (5 steps, synchronous and graph-replayed) when the host
+holds the oracle's ~121 GB, and a 5e9-element tensor whose shard starts past
+2^31, 10 bytes off a 16-byte boundary.  The device state comes back through
+pinned buffers, chunk by chunk, and the oracle runs over the same chunks on
+host threads (the step is elementwise once the overflow decision, taken over
+the whole shard first, is known).
 
-Sampled windows (the _run_sampled tests): the GPU runs the whole shard
-exactly as bench.py does (same library calls, same launch shapes); the
-oracle recomputes fixed windows of the shard -- its head and tail, +-4096
-elements around every segment edge, +-64 around every injected +inf, and 16
-seeded random windows of 2^24 elements -- from the host generator, over
-chunks of the windows on host threads.  The update is elementwise, so a
-window evolves exactly as it does inside the whole shard.  The overflow
-decision is global: the windows contain every injected position, and the
-generator's support (|z| <= 2*sqrt(3)) keeps every other gradient finite,
-which the test asserts from the workload's constants, so the window's
-overflow test equals the whole shard's.
+Sampled windows (the _run_sampled runs): the Llama-2-70B step on any box with
+its device memory (and its graph-replayed step where the host cannot hold the
+whole oracle state), the standalone cast and scan at that size, and the
+offload pipeline on Llama-3-8B.  The oracle recomputes fixed windows of the
+shard -- its head and tail, +-4096 elements around every segment edge, +-64
+around every injected +inf, and 16 seeded random windows of 2^24 elements --
+from the host generator; the update is elementwise, so a window evolves
+exactly as it does inside the whole shard.  The overflow decision is global:
+the windows contain every injected position, and the generator's support
+(|z| <= 2*sqrt(3)) keeps every other gradient finite, which the test asserts
+from the workload's constants, so the window's overflow test equals the
+whole shard's.
 
 Bar, after every step: flags, loss scale and applied-step counter equal;
-the flat gradient shard, master, moments and parameters bit-identical on
-the windows (within 1e-6 relative error and 1 ulp is the acceptance bound;
-identical bits are expected and required).
+flat gradients, master, moments and parameters bit-identical (within 1e-6
+relative error and 1 ulp is the acceptance bound; identical bits are
+expected and required).  Expected parameters come from the oracle's fp32
+master through torch's round-to-nearest-even conversion, which equals the
+oracle's own cast on all 2^32 fp32 inputs (tests/test_oracle_cast.py).
 
 step_mode="graph" runs the step as bench.py's graph line does: flatten +
 zero_adam_step_async captured once into a HIP graph and replayed every
@@ -30,6 +42,7 @@ each replay only to compare with the oracle).
 """
 import gc
 import os
+import threading
 import time
 from concurrent.futures import ThreadPoolExecutor
 
@@ -316,39 +329,48 @@ def _run_sampled(case, flatten_mode="all", label="", step_mode="sync"):
     return skipped
 
 
+def _whole_70b_fits():
+    """Whether this box holds the oracle's whole 70B-class shard (~121 GB of
+    host memory) beside the device state (~160 GB)."""
+    import torch
+    free, _ = torch.cuda.mem_get_info()
+    return _mem_available() >= 140e9 and free >= 170e9
+
+
 def test_llama3_8b_rank3_bucketed_flatten():
+    # one flatten call per bucket (19 buckets touch this shard), all 20 steps
     case = Case.from_workload(get("llama3_8b"))
-    _run_sampled(case, flatten_mode="buckets", label="llama3_8b")
+    assert _whole_shard(case, "llama3_8b buckets", flatten_mode="buckets") == 0
 
 
 def test_llama3_8b_rank3_fp32_gradients():
     # gradients kept in fp32 at full size: 4-byte flatten and update path
     case = Case.from_workload(get("llama3_8b"), grad_dtype="f32", steps=6)
-    _run_sampled(case, label="llama3_8b fp32 grads")
+    assert _whole_shard(case, "llama3_8b fp32 grads") == 0
 
 
 def test_dna_20b_rank2_dynamic_scale_with_injected_overflows():
+    # all 50 steps: fp16 at the dynamic scale, the workload's injected infs
     case = Case.from_workload(get("dna_20b"))
-    skipped = _run_sampled(case, label="dna_20b")
     expect = sum(case.injection(it, 2_498_481_408) is not None for it in range(1, case.steps + 1))
-    assert skipped == expect and skipped >= 1
+    assert _whole_shard(case, "dna_20b") == expect and expect >= 1
 
 
 def test_llama3_8b_rank3_graph_replayed_step():
     case = Case.from_workload(get("llama3_8b"))
-    _run_sampled(case, label="llama3_8b graph", step_mode="graph")
+    assert _whole_shard(case, "llama3_8b graph", step_mode="graph") == 0
 
 
 def test_dna_20b_rank2_graph_replayed_step_with_device_scaler():
     # the loss-scale policy runs on the device: skips and halvings at full
     # size; 25 of the workload's 50 steps hold all three of its injections
     case = Case.from_workload(get("dna_20b"), steps=25)
-    skipped = _run_sampled(case, label="dna_20b graph", step_mode="graph")
     expect = sum(case.injection(it, 2_498_481_408) is not None for it in range(1, case.steps + 1))
-    assert skipped == expect and skipped >= 1
+    assert _whole_shard(case, "dna_20b graph", step_mode="graph") == expect and expect >= 1
 
 
 def test_llama2_70b_rank7_full_shard():
+    # sampled windows: runs on any box with the device memory
     import torch
     free, _ = torch.cuda.mem_get_info()
     if free < 170e9:
@@ -358,12 +380,16 @@ def test_llama2_70b_rank7_full_shard():
 
 
 def test_llama2_70b_rank7_graph_replayed_step():
+    # every element when the host holds the oracle's whole shard, else windows
     import torch
     free, _ = torch.cuda.mem_get_info()
     if free < 170e9:
         pytest.skip(f"needs ~160 GB of free device memory, {free / 1e9:.0f} GB free")
     case = Case.from_workload(get("llama2_70b"))
-    _run_sampled(case, label="llama2_70b graph", step_mode="graph")
+    if _whole_70b_fits():
+        assert _whole_shard(case, "llama2_70b graph", step_mode="graph") == 0
+    else:
+        _run_sampled(case, label="llama2_70b graph", step_mode="graph")
 
 
 def test_llama2_70b_rank7_standalone_cast_and_scan():
@@ -454,8 +480,7 @@ def test_tensor_beyond_2_31_elements():
         pytest.skip(f"needs ~50 GB of free device memory, {free / 1e9:.0f} GB free")
     case = Case(numels=[3, 4_999_999_990, 7], world_size=2, rank=1, grad_dtype="bf16",
                 param_dtype="bf16", steps=3, inject={2: 2_300_000_000})
-    skipped = _run_sampled(case, label="5e9-element tensor")
-    assert skipped == 1
+    assert _whole_shard(case, "5e9-element tensor") == 1
 
 
 def _offload_sampled(case, lag, label, n_threads=8):
@@ -555,15 +580,18 @@ def test_llama3_8b_rank3_offload(lag):
     assert _offload_sampled(case, lag, f"llama3_8b offload lag={lag}") == 1
 
 
-def _whole_shard(case, label, step_mode="sync"):
+def _whole_shard(case, label, step_mode="sync", flatten_mode="all"):
     """Every element of the shard after every step: the flat gradients,
     master, moments and parameters bit for bit, and the overflow flag and
     loss scale.  The oracle runs over contiguous chunks of the shard on host
     threads (the step is elementwise once the overflow decision, taken over
     the whole shard first, is known); its gradients come from the host
     generator at the same flat indices as the device's, with the same +inf.
+    The device's state comes back through pinned buffers, chunk by chunk.
     step_mode="graph": flatten + zero_adam_step_async replayed from a HIP
-    graph, t and the scale on the device."""
+    graph, t and the scale on the device.  flatten_mode="buckets": one
+    zero_flatten_grads call per bucket, each given only that bucket's
+    gradient tensors, as backward hooks would call it."""
     import torch
     dev = torch.device("cuda:0")
     gdt, pdt = torch_dtype(case.grad_dtype), torch_dtype(case.param_dtype)
@@ -592,13 +620,24 @@ def _whole_shard(case, label, step_mode="sync"):
             grads[t] = torch.empty(case.numels[t], dtype=gdt, device=dev)
     hp = z.AdamHParams(case.lr, case.beta1, case.beta2, case.eps, case.weight_decay, case.adamw)
     g_scaler = z.LossScaler(case.init_scale, dynamic=case.dynamic, window=case.window)
+    tb = plan.tensor_buckets()
+
+    def flatten():
+        if flatten_mode == "buckets":
+            for b in range(plan.n_buckets):
+                z.zero_flatten_grads(plan, b, [g if (g is not None and tb[i] == b) else None
+                                               for i, g in enumerate(grads)], flat)
+        else:
+            assert flatten_mode == "all", flatten_mode
+            z.zero_flatten_grads(plan, -1, grads, flat)
+
     graph = None
     if step_mode == "graph":
         z.zero_state_upload(plan, 0, g_scaler)
         torch.cuda.synchronize(dev)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            z.zero_flatten_grads(plan, -1, grads, flat)
+            flatten()
             z.zero_adam_step_async(plan, hp, flat, master, mom, var, param, begin)
     else:
         assert step_mode == "sync", step_mode
@@ -606,7 +645,9 @@ def _whole_shard(case, label, step_mode="sync"):
     o_master = np.zeros(S, np.float32)
     o_m = np.zeros(S, np.float32)
     o_v = np.zeros(S, np.float32)
-    bits = np.zeros(S, np.uint16)
+    word = GRAD_WORD[case.grad_dtype]           # uint16, or uint32 for fp32 gradients
+    flat_bits = torch.int32 if case.grad_dtype == "f32" else torch.int16
+    bits = np.zeros(S, word)
 
     def init(c):
         lo, hi = c[0], min(c[1], real)
@@ -616,6 +657,21 @@ def _whole_shard(case, label, step_mode="sync"):
 
     list(pool.map(init, chunks))
     o_scaler = oracle.Scaler(case.init_scale, dynamic=case.dynamic, window=case.window)
+    staging = threading.local()
+
+    def fetch(t, name):
+        """A device slice's contents on the host, through a pinned buffer of
+        the calling thread (synchronous copy)."""
+        bufs = getattr(staging, "bufs", None)
+        if bufs is None:
+            bufs = staging.bufs = {}
+        buf = bufs.get(name)
+        if buf is None:
+            buf = bufs[name] = torch.empty(chunk, dtype=t.dtype, pin_memory=True)
+        dst = buf[:t.numel()]
+        dst.copy_(t)
+        return dst.numpy()
+
     g_t = o_t = skipped = 0
     for it in range(1, case.steps + 1):
         t_step = time.perf_counter()
@@ -639,7 +695,7 @@ def _whole_shard(case, label, step_mode="sync"):
             graph.replay()
             g_ovf = int(z.zero_state_download(plan).last_flag)
         else:
-            z.zero_flatten_grads(plan, -1, grads, flat)
+            flatten()
             g_ovf = z.zero_adam_step(plan, hp, g_t + 1, scale, flat, master, mom, var, param,
                                      begin)
             z.zero_update_loss_scale(g_scaler, g_ovf)
@@ -671,17 +727,18 @@ def _whole_shard(case, label, step_mode="sync"):
         def check(c):
             lo, hi = c
             bad = []
-            got = flat[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16)
+            got = fetch(flat[lo:hi].view(flat_bits), "flat").view(word)
             if not np.array_equal(got, bits[lo:hi]):
                 bad.append("flat")
             for name, d, o in (("master", master, o_master), ("m", mom, o_m), ("v", var, o_v)):
-                got = d[lo:hi].cpu().numpy()
+                got = fetch(d[lo:hi], name)
                 if not np.array_equal(got.view(np.uint32), o[lo:hi].view(np.uint32)):
                     bad.append(f"{name} (max rel err {max_rel(got, o[lo:hi])})")
             hi = min(hi, real)
             if o_t > 0 and hi > lo:
-                got = param[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16)
-                if not np.array_equal(got, cast_library(o_master[lo:hi], case.param_dtype)):
+                got = fetch(param[lo:hi].view(torch.int16), "param").view(np.uint16)
+                if not np.array_equal(got, cast_library(o_master[lo:hi], case.param_dtype,
+                                                        parallel=False)):
                     bad.append("param")
             return (lo, bad) if bad else None
 
@@ -690,6 +747,7 @@ def _whole_shard(case, label, step_mode="sync"):
         log(f"[whole] {label}: it={it} t={o_t} scale={scale} overflow={o_ovf}: "
             f"every element equal ({time.perf_counter() - t_step:.1f} s)")
     pool.shutdown()
+    del staging
     if graph is not None:
         st = z.zero_state_download(plan)
         assert (st.applied_steps, st.skipped_steps, st.scale) == (o_t, skipped, o_scaler.value)
@@ -713,26 +771,14 @@ def test_dna_20b_rank2_whole_shard_every_step():
     assert _whole_shard(case, "dna_20b") == 1
 
 
-def test_dna_20b_rank2_whole_shard_graph_replayed():
-    # the asynchronous step from a HIP graph: the skip and the halving are
-    # decided on the device
-    case = Case.from_workload(get("dna_20b"), steps=3, inject_p=0.0,
-                              inject={2: 1_000_000_003})
-    assert _whole_shard(case, "dna_20b graph", step_mode="graph") == 1
-
-
 @pytest.mark.timeout(1200)
 def test_llama2_70b_rank7_whole_shard_every_step():
     """Every element of the 8.6e9-element shard after each of the workload's
     5 steps.  The oracle's state (fp32 master, moments, gradient bits) takes
     ~121 GB of host memory and the device ~155 GB."""
-    import torch
-    avail = _mem_available()
-    if avail < 140e9:
-        pytest.skip(f"needs ~140 GB of available host memory, {avail / 1e9:.0f} GB available")
-    free, _ = torch.cuda.mem_get_info()
-    if free < 170e9:
-        pytest.skip(f"needs ~160 GB of free device memory, {free / 1e9:.0f} GB free")
+    if not _whole_70b_fits():
+        pytest.skip(f"needs ~140 GB of available host memory and ~170 GB of free device "
+                    f"memory ({_mem_available() / 1e9:.0f} GB available on the host)")
     case = Case.from_workload(get("llama2_70b"))
     assert case.steps == 5
     assert _whole_shard(case, "llama2_70b") == 0
