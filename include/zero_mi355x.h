@@ -182,6 +182,13 @@ void zero_plan_destroy(zero_plan_t* plan);
 int zero_flatten_grads(zero_plan_t* plan, int32_t bucket, const void* const* grads,
                        int32_t grad_dtype, void* flat_grad, void* stream);
 
+/* Declares that the flat gradient buffer was written after the flattens
+ * since the last step (for example averaged in place): the next step (or
+ * offloaded step) on this plan then clears the flag and scans the buffer's
+ * real elements instead of trusting the flattens' fused test.  Host only;
+ * no device work.  Errors: ZERO_ENULL. */
+int zero_flatten_invalidate(zero_plan_t* plan);
+
 /* One gated Adam/AdamW step on the shard, with the half cast fused in.
  * [genomic] memory breakdown / [instr] ZeRO-1 mechanism: fp32 master
  * weights, momentum and variance of the partition, updated by their owner;
@@ -192,7 +199,8 @@ int zero_flatten_grads(zero_plan_t* plan, int32_t bucket, const void* const* gra
  * when they covered every bucket of the shard; otherwise the flag is cleared
  * and a scan of flat_grad's real elements [0, real) decides it (the gate
  * reads the buffer as it is when the step runs: a write into flat_grad
- * after a covering flatten is not tested again).  The padding gradients
+ * after a covering flatten is not tested again unless the caller declares
+ * it with zero_flatten_invalidate).  The padding gradients
  * flat_grad[real, S) are never tested: they update only the padding state,
  * which is never cast to a parameter.  Otherwise, per shard element k < S, in
  * fp32 with one rounding per operation (scalars formed on the host in

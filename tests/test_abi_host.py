@@ -156,6 +156,8 @@ def test_argument_errors_before_device_work():
     bad = _abi.zero_scaler_t(0.0, 1.0, 0.5, 2.0, 10, 0, 1, 0)
     assert lib.zero_update_loss_scale(ctypes.byref(bad), 0) == _abi.ZERO_EINVAL
     assert lib.zero_update_loss_scale(None, 0) == _abi.ZERO_ENULL
+    assert lib.zero_flatten_invalidate(None) == _abi.ZERO_ENULL
+    assert lib.zero_flatten_invalidate(plan.handle) == _abi.ZERO_OK
 
 
 def test_async_step_argument_errors_before_device_work():

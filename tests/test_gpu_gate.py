@@ -2,7 +2,8 @@
 
 * A step trusts the fused test of the flattens that covered its buffer: a
   value written into that buffer afterwards is not tested again (the
-  documented rule), and is consumed as a gradient.
+  documented rule), and is consumed as a gradient -- unless the caller
+  declares the write with zero_flatten_invalidate, which makes the step scan.
 * A flatten into another buffer starts the flag over, so a step on the
   second buffer does not inherit what was found in the first.
 * A scan decides a step whose buffer was not (fully) flattened, and it tests
@@ -77,6 +78,31 @@ def test_write_after_covering_flatten_is_not_retested(dt):
     keep = np.arange(op.S) != pos
     assert np.array_equal(got.view(np.uint32)[keep], om.view(np.uint32)[keep])
     assert np.array_equal(_bits(va)[keep], ov.view(np.uint32)[keep])
+
+
+@pytest.mark.parametrize("mode", ["sync", "async"])
+def test_invalidate_makes_the_step_scan(mode):
+    """The same write after a covering flatten, declared with
+    zero_flatten_invalidate: the step scans the buffer, finds the inf and is
+    skipped, leaving the state unchanged."""
+    import torch
+    plan = z.zero_partition_plan(NUMELS, 2, 1, 8, 20000)
+    op = oracle.plan(NUMELS, 2, 1, 8, 20000)
+    host = _grads("bf16", 7)
+    flat = torch.empty(op.S, dtype=torch.bfloat16, device=DEV)
+    z.zero_flatten_grads(plan, -1, [to_device_grad(h, "bf16", DEV) for h in host], flat)
+    pos = op.real // 5
+    flat[pos] = float("inf")
+    z.zero_flatten_invalidate(plan)
+    m0, master, mo, va = _state(op.S, 8)
+    if mode == "sync":
+        assert z.zero_adam_step(plan, z.AdamHParams(), 1, 1.0, flat, master, mo, va) == 1
+    else:
+        z.zero_state_upload(plan, 0, z.LossScaler(1.0, dynamic=False))
+        z.zero_adam_step_async(plan, z.AdamHParams(), flat, master, mo, va)
+        assert z.zero_state_download(plan).last_flag == 1
+    assert np.array_equal(_bits(master), m0.view(np.uint32))
+    assert not _bits(va).any()
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])

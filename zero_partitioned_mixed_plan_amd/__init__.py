@@ -9,6 +9,7 @@ and the stream.  The functions keep the names of the C ABI
     zero_partition_plan(numels, world_size, rank, align_elems, bucket_elems) -> Plan
     zero_flatten_grads(plan, bucket, grads, flat_grad, stream=None)
                                 (grads: a list of tensors, or a GradList bound once)
+    zero_flatten_invalidate(plan)  (the flat buffer was written after the flattens)
     zero_adam_step(plan, hparams, step, loss_scale, flat_grad, master, exp_avg,
                    exp_avg_sq, param=None, param_base=0, stream=None) -> 0 | 1
     zero_update_loss_scale(scaler, overflow)
@@ -54,7 +55,8 @@ from . import _abi
 from ._abi import ZERO_BF16, ZERO_F16, ZERO_F32, ZeroError, check, lib  # noqa: F401
 
 __all__ = ["Plan", "release_all", "AdamHParams", "LossScaler", "DeviceStepState", "ZeroError",
-           "zero_partition_plan", "GradList", "zero_flatten_grads", "zero_adam_step",
+           "zero_partition_plan", "GradList", "zero_flatten_grads", "zero_flatten_invalidate",
+           "zero_adam_step",
            "zero_update_loss_scale", "zero_write_param_shard", "zero_state_upload",
            "zero_adam_step_async", "zero_state_download", "zero_state_device_scale",
            "zero_adam_step_noalloc",
@@ -294,6 +296,12 @@ def zero_flatten_grads(plan: Plan, bucket: int, grads, flat_grad, stream=None) -
     check(lib.zero_flatten_grads(plan.handle, bucket, ptrs, _dtype_code(flat_grad),
                                  flat_grad.data_ptr(), _stream_handle(stream, flat_grad.device)),
           "zero_flatten_grads")
+
+
+def zero_flatten_invalidate(plan: Plan) -> None:
+    """The flat gradient buffer was written after the flattens: the next
+    step scans it instead of trusting their fused inf/NaN test."""
+    check(lib.zero_flatten_invalidate(plan.handle), "zero_flatten_invalidate")
 
 
 def _plan_numels(plan: Plan) -> List[int]:

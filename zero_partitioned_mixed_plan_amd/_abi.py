@@ -80,6 +80,7 @@ SIGNATURES = {
     "zero_plan_tensor_buckets": (ctypes.c_int, [_VP, ctypes.POINTER(_I32), _I64]),
     "zero_plan_destroy": (None, [_VP]),
     "zero_flatten_grads": (ctypes.c_int, [_VP, _I32, ctypes.POINTER(_VP), _I32, _VP, _VP]),
+    "zero_flatten_invalidate": (ctypes.c_int, [_VP]),
     "zero_adam_step": (ctypes.c_int, [_VP, ctypes.POINTER(zero_adam_hparams_t), _I64,
                                       ctypes.c_double, _VP, _I32, _VP, _VP, _VP, _VP, _I64, _I64,
                                       _I32, _VP]),

@@ -455,6 +455,12 @@ int zero_flatten_grads(zero_plan_t* p, int32_t bucket, const void* const* grads,
     return ZERO_OK;
 }
 
+int zero_flatten_invalidate(zero_plan_t* p) {
+    if (p == nullptr) return fail(ZERO_ENULL, "plan is NULL");
+    reset_flatten_bookkeeping(p);
+    return ZERO_OK;
+}
+
 int zero_adam_step(zero_plan_t* p, const zero_adam_hparams_t* hp, int64_t step, double loss_scale,
                    const void* flat_grad, int32_t grad_dtype, float* master, float* exp_avg,
                    float* exp_avg_sq, void* param, int64_t param_base, int64_t param_numel,
