@@ -29,9 +29,12 @@
 //     non-temporal loads where the source is 16-byte aligned (copy 6.19 ->
 //     6.44 TB/s, read 6.81 -> 7.07).  A flatten workgroup first searches
 //     the launch's piece table for its tile (a short chain of dependent
-//     scalar loads); two vectors per thread (4096-element tiles) amortise
-//     that better than one or four (-3% flatten time on a 70B-class shard,
-//     -5% on a shard of 300 mostly misaligned pieces).
+//     scalar loads) and ends with a ballot and a barrier; between those
+//     phases it has no load in flight.  128 threads with two vectors each
+//     (2048-element tiles), at most 13 workgroups per CU, was the fastest
+//     of 256 x 1/2/4, 128 x 1/2/4 and 64 x 2/4/8 threads x vectors, each
+//     with and without such a cap (5.29 ms against 5.65 ms for 256 x 2 on
+//     a 70B-class shard).
 //   * a workgroup must move enough bytes: the dispatcher starts roughly two
 //     billion workgroups a second, so the 6 B/element parameter cast with
 //     one element per thread (256 per workgroup) ran at 3.1 TB/s; eight
@@ -41,7 +44,8 @@
 //     to 2^32 work-items and a 70B-class shard has more elements than that;
 //     workgroup id = blockIdx.y * gridDim.x + blockIdx.x keeps address order.
 //   * the overflow flag is reduced per workgroup with a wave ballot and a
-//     tiny LDS table, then at most one global atomic OR per workgroup.
+//     tiny LDS table (none in a one-wave workgroup), then at most one
+//     global atomic OR per workgroup.
 // Device code is built without FMA contraction: every fp32 operation of
 // the update rounds once, in the order documented in zero_mi355x.h.
 #include "internal.h"
@@ -56,9 +60,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kVec = 8;                     // 16-bit words per 16-byte access
-constexpr int64_t kTile = kThreads * kVec;  // 2048 words per workgroup and vector
-constexpr int kFlatV = 2;                   // 16-byte vectors per thread in flatten
-constexpr int64_t kFlatTile = kTile * kFlatV;  // flatten tile: 4096 16-bit words
+// flatten: 128 threads x 2 vectors of 16 bytes, a tile of 2048 16-bit words
+// (4 KiB read, 4 KiB written) per workgroup
+constexpr int kFlatThreads = 128;
+constexpr int kFlatV = 2;
+constexpr int64_t kFlatTile = int64_t(kFlatThreads) * kVec * kFlatV;
+// The flatten reserves LDS it never touches so that at most 13 of its
+// workgroups share a CU (160 KiB of LDS per CU; the pad fits 13 and not 14
+// whether LDS is granted in 256- or 512-byte units).  A pure copy stream
+// moves the most bytes with a bounded number of requests in flight per CU;
+// 13 workgroups (about 52 KiB of loads in flight) ran the flatten 2-6%
+// faster than the 16 that fit otherwise, and 11 or fewer slower.
+constexpr int kLdsPerCu = 160 * 1024;
+constexpr int kFlatPerCu = 13;
+constexpr unsigned kFlatLdsPad = (kLdsPerCu / kFlatPerCu - 512) / 512 * 512;
+static_assert(kFlatLdsPad + 512 <= kLdsPerCu / kFlatPerCu &&
+                  kFlatLdsPad + 8 > kLdsPerCu / (kFlatPerCu + 1),
+              "flatten LDS pad admits exactly kFlatPerCu workgroups per CU");
 constexpr int64_t kGridX = 65536;           // x extent of the 2-D grids
 // update: 256 consecutive elements per workgroup, in one of two shapes (the
 // launcher picks by shard size): 256 threads x 1 element, or 128 threads x
@@ -119,15 +137,20 @@ __device__ __forceinline__ uint16_t f32_to_half(float x) {
 // ------------------------------------------------------------ flag reduce
 // Wave ballot -> one LDS word per wave -> one atomic per workgroup.  Every
 // thread of the workgroup must reach this call.
+template <int WAVES = kWaves>
 __device__ __forceinline__ void raise_flag_if_any(bool bad, int* flag) {
-    __shared__ int wave_bad[kWaves];
     const unsigned long long mask = __ballot(bad);
+    if (WAVES == 1) {  // a one-wave workgroup needs no LDS and no barrier
+        if ((threadIdx.x & 63) == 0 && mask != 0ull) atomicOr(flag, 1);
+        return;
+    }
+    __shared__ int wave_bad[WAVES];
     if ((threadIdx.x & 63) == 0) wave_bad[threadIdx.x >> 6] = mask != 0ull;
     __syncthreads();
     if (threadIdx.x == 0) {
         int any = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) any |= wave_bad[w];
+        for (int w = 0; w < WAVES; ++w) any |= wave_bad[w];
         if (any) atomicOr(flag, 1);
     }
 }
@@ -174,7 +197,7 @@ __device__ __forceinline__ const __attribute__((address_space(1))) T* global_ptr
 
 // The kFlatV 16-byte source vectors of this lane in a full tile whose
 // element 0 is read from byte address src0 (uniform over the workgroup);
-// vector j of lane t starts at src0 + 16 (t + j * kThreads).  An aligned
+// vector j of lane t starts at src0 + 16 (t + j * kFlatThreads).  An aligned
 // source is read with the streaming (non-temporal) policy.  A misaligned
 // one straddles two aligned blocks: the lane's own block (lo) and the next
 // lane's (hi).  Each lane loads its lo block (non-temporal) and takes hi
@@ -191,8 +214,8 @@ __device__ __forceinline__ void load_tile_mis(const __attribute__((address_space
     const bool last = lane == 63;
 #pragma unroll
     for (int j = 0; j < kFlatV; ++j) {
-        lo[j] = __builtin_nontemporal_load(blk + j * kThreads);
-        if (last) hi[j] = blk[j * kThreads + 1];
+        lo[j] = __builtin_nontemporal_load(blk + j * kFlatThreads);
+        if (last) hi[j] = blk[j * kFlatThreads + 1];
     }
     const int from = (lane + 1) << 2;  // byte address of the next lane (wraps at 64)
 #pragma unroll
@@ -214,7 +237,7 @@ __device__ __forceinline__ void load_tile(uint64_t src0, u32x4 (&q)[kFlatV]) {
     switch (mis) {
         case 0:
 #pragma unroll
-            for (int j = 0; j < kFlatV; ++j) q[j] = __builtin_nontemporal_load(blk + j * kThreads);
+            for (int j = 0; j < kFlatV; ++j) q[j] = __builtin_nontemporal_load(blk + j * kFlatThreads);
             return;
         case 2: return load_tile_mis<2>(blk, q);
         case 4: return load_tile_mis<4>(blk, q);
@@ -228,7 +251,7 @@ __device__ __forceinline__ void load_tile(uint64_t src0, u32x4 (&q)[kFlatV]) {
 
 // One workgroup per tile of kFlatTile 16-bit words of the flat shard.
 template <int DT>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kFlatThreads)
 flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict__ flag) {
     const int64_t blk = block_id();
     if (blk >= a.n_tiles) return;  // the whole workgroup leaves together
@@ -256,7 +279,7 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
         }
         auto* dst = reinterpret_cast<u32x4*>(flat + lo) + threadIdx.x;
 #pragma unroll
-        for (int j = 0; j < kFlatV; ++j) __builtin_nontemporal_store(q[j], dst + j * kThreads);
+        for (int j = 0; j < kFlatV; ++j) __builtin_nontemporal_store(q[j], dst + j * kFlatThreads);
     } else {
         // tile crosses piece edges: element-wise, coalesced per piece
         for (; p < a.n && a.begin[p] < hi; ++p) {
@@ -266,7 +289,7 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
             if (DT == ZERO_F32) {
                 // piece edges are even words (element edges): 4-byte elements
                 auto* flat32 = reinterpret_cast<uint32_t*>(flat);
-                for (int64_t d = (s0 >> 1) + threadIdx.x; d < (s1 >> 1); d += kThreads) {
+                for (int64_t d = (s0 >> 1) + threadIdx.x; d < (s1 >> 1); d += kFlatThreads) {
                     uint32_t w = 0;
                     if (!zero) {
                         w = *global_ptr<uint32_t>(a.src[p] + 4ull * static_cast<uint64_t>(d));
@@ -276,7 +299,7 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
                 }
                 continue;
             }
-            for (int64_t d = s0 + threadIdx.x; d < s1; d += kThreads) {
+            for (int64_t d = s0 + threadIdx.x; d < s1; d += kFlatThreads) {
                 uint32_t h = 0;
                 if (!zero) {
                     h = *global_ptr<uint16_t>(a.src[p] + 2ull * static_cast<uint64_t>(d));
@@ -286,19 +309,23 @@ flatten_kernel(const FlattenArgs a, uint16_t* __restrict__ flat, int* __restrict
             }
         }
     }
-    raise_flag_if_any(bad, flag);
+    raise_flag_if_any<kFlatThreads / 64>(bad, flag);
 }
 
 // ------------------------------------------------------------ scan
+// 128 threads per workgroup, one 16-byte vector each (16 workgroups per CU):
+// 1-3% faster than 256 or 512 threads x 1; capping the workgroups per CU
+// below what fits slows this read-only stream.
+constexpr int kScanThreads = 128;
 // Elements per 16-byte vector, and per workgroup (one vector per thread).
 template <int DT>
 constexpr int64_t scan_per() { return DT == ZERO_F32 ? 4 : kVec; }
 template <int DT>
-constexpr int64_t scan_span() { return kThreads * scan_per<DT>(); }
+constexpr int64_t scan_span() { return kScanThreads * scan_per<DT>(); }
 
 // One 16-byte non-temporal load per thread, element-wise at the tail.
 template <int DT>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kScanThreads)
 scan_kernel(const void* __restrict__ flat, int64_t n, int* __restrict__ flag) {
     constexpr int64_t per = scan_per<DT>();
     const int64_t blk = block_id();
@@ -314,7 +341,7 @@ scan_kernel(const void* __restrict__ flat, int64_t n, int* __restrict__ flag) {
                                                      : static_cast<const uint16_t*>(flat)[k]);
         }
     }
-    raise_flag_if_any(bad, flag);
+    raise_flag_if_any<kScanThreads / 64>(bad, flag);
 }
 
 // ------------------------------------------------------------ fused Adam
@@ -532,11 +559,14 @@ hipError_t launch_flatten(const FlatPiece* pieces, int n, void* flat, int* flag,
     const dim3 grid = grid_2d(a.n_tiles);
     auto* words16 = static_cast<uint16_t*>(flat);
     if (grad_dtype == ZERO_F16) {
-        hipLaunchKernelGGL(flatten_kernel<ZERO_F16>, grid, dim3(kThreads), 0, s, a, words16, flag);
+        hipLaunchKernelGGL(flatten_kernel<ZERO_F16>, grid, dim3(kFlatThreads), kFlatLdsPad, s, a, words16,
+                           flag);
     } else if (grad_dtype == ZERO_BF16) {
-        hipLaunchKernelGGL(flatten_kernel<ZERO_BF16>, grid, dim3(kThreads), 0, s, a, words16, flag);
+        hipLaunchKernelGGL(flatten_kernel<ZERO_BF16>, grid, dim3(kFlatThreads), kFlatLdsPad, s, a, words16,
+                           flag);
     } else {
-        hipLaunchKernelGGL(flatten_kernel<ZERO_F32>, grid, dim3(kThreads), 0, s, a, words16, flag);
+        hipLaunchKernelGGL(flatten_kernel<ZERO_F32>, grid, dim3(kFlatThreads), kFlatLdsPad, s, a, words16,
+                           flag);
     }
     return hipGetLastError();
 }
@@ -544,7 +574,7 @@ hipError_t launch_flatten(const FlatPiece* pieces, int n, void* flat, int* flag,
 template <int DT>
 void scan_launch(const void* flat, int64_t n, int* flag, hipStream_t s) {
     const dim3 grid = grid_2d((n + scan_span<DT>() - 1) / scan_span<DT>());
-    hipLaunchKernelGGL(scan_kernel<DT>, grid, dim3(kThreads), 0, s, flat, n, flag);
+    hipLaunchKernelGGL(scan_kernel<DT>, grid, dim3(kScanThreads), 0, s, flat, n, flag);
 }
 
 hipError_t launch_scan(const void* flat, int64_t n, int* flag, int grad_dtype, hipStream_t s) {
