@@ -515,6 +515,61 @@ def copy_probe(nbytes, reps, device):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def placement_probe(S, ballasts_gb, device, reps=10):
+    """The fused update on one S-element shard placed anew for every trial:
+    before each trial a ballast allocation of the given size moves where the
+    arrays land, and the arrays are either five allocations ("separate") or
+    carved back to back from one ("one").  The caching allocator is emptied
+    between trials, so even a repeated virtual address gets its physical
+    pages afresh.  Prints one line per trial and a JSON summary."""
+    import ctypes
+    import statistics
+
+    import torch
+
+    import zero_partitioned_mixed_plan_amd as z
+    plan = z.zero_partition_plan([S], 1, 0, 64, 1 << 25)
+    plan.set_timing(True)
+    hp = z.AdamHParams()
+    out = {}
+    for gb in ballasts_gb:
+        for layout in ("separate", "one"):
+            ballast = (torch.empty(int(gb * 1e9), dtype=torch.uint8, device=device)
+                       if gb > 0 else None)
+            if layout == "separate":
+                master, m, v = (torch.empty(S, device=device) for _ in range(3))
+                g = torch.empty(S, dtype=torch.bfloat16, device=device)
+                param = torch.empty(S, dtype=torch.bfloat16, device=device)
+                buf = None
+            else:
+                buf = torch.empty(16 * S, dtype=torch.uint8, device=device)
+                master, m, v = (buf[4 * S * i:4 * S * (i + 1)].view(torch.float32)
+                                for i in range(3))
+                g = buf[12 * S:14 * S].view(torch.bfloat16)
+                param = buf[14 * S:16 * S].view(torch.bfloat16)
+            g.normal_(0, 1e-3)
+            master.normal_(0, 0.02)
+            m.zero_()
+            v.zero_()
+            t = []
+            for i in range(reps + 2):
+                assert z.zero_adam_step(plan, hp, 1, 1.0, g, master, m, v, param, 0) == 0
+                if i >= 2:
+                    t.append(plan.kernel_ms(2))
+            med = statistics.median(t)
+            out.setdefault(layout, []).append(med)
+            print(f"[placement] ballast {gb:g} GB, {layout}: update {med:.3f} ms "
+                  f"(min {min(t):.3f}, max {max(t):.3f}) = {28 * S / med / 8e9 * 100:.2f}% of "
+                  f"8 TB/s; master at {master.data_ptr():#x}", flush=True)
+            del master, m, v, g, param, buf, ballast
+            torch.cuda.empty_cache()
+    summary = {k: {"min_ms": min(v), "max_ms": max(v), "median_ms": statistics.median(v),
+                   "spread_pct": (max(v) / min(v) - 1) * 100} for k, v in out.items()}
+    print(json.dumps({"placement_probe_elems": S, "ballasts_gb": ballasts_gb,
+                      "reps": reps, "layouts": summary}), flush=True)
+    plan.close()
+
+
 def main(argv=None):
     try:
         return _main(argv)
@@ -556,6 +611,9 @@ def _main(argv=None):
                          "that the one-step delayed update overlaps")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run only a plain copy of this many bytes (counter calibration)")
+    ap.add_argument("--placement-probe", default=None, metavar="GB,GB,...",
+                    help="run only the update on the workload's shard size, placed anew "
+                         "after ballast allocations of these sizes (GB)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -578,6 +636,13 @@ def _main(argv=None):
     w = get(args.workload)
     if args.grad_dtype:
         w = dataclasses.replace(w, grad_dtype=args.grad_dtype)
+    if args.placement_probe:
+        import zero_partitioned_mixed_plan_amd as z
+        wplan = z.zero_partition_plan(w.numels, w.world_size, w.rank, w.align, w.bucket_elems)
+        S = wplan.S
+        wplan.close()
+        placement_probe(S, [float(x) for x in args.placement_probe.split(",")], device)
+        return 0
     if args.mode == "offload":
         threads = args.host_threads or max(1, host_info()["usable_cpus"] - 1)
         plan, res = run_offload(w, args.steps, args.warmup, device, threads, args.forward_ms)
