@@ -356,7 +356,9 @@ int zero_cpu_adam_step(const zero_plan_t* plan, const zero_adam_hparams_t* hp, i
                        int32_t overflow, int32_t n_threads);
 
 /* Name of the host instruction set the update uses: "avx512", "avx2" or
- * "scalar" (environment variable ZERO_CPU_ISA may force a narrower one). */
+ * "scalar".  The default is the widest the CPU has, except that AMD cores
+ * use "avx2" (faster there); the environment variable ZERO_CPU_ISA forces
+ * any of the three that the CPU has.  Every path gives the same bits. */
 const char* zero_cpu_isa(void);
 
 /* The offloaded step as a pipeline, with the one-step delayed parameter

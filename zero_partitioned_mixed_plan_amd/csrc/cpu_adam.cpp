@@ -370,6 +370,12 @@ ZMI_AVX512 bool nonfinite_avx512(const void* g, int64_t lo, int64_t hi, uint32_t
 }
 
 // ------------------------------------------------------------ dispatch
+// The default is the widest path, except on AMD cores, where the 8-wide
+// path is the faster one: on the EPYC host of an MI355X node the AVX2 update
+// of a 1e9-element shard took 74-77 ms on 15 threads against 92-93 ms for
+// the AVX-512 one (which also stayed behind with unmasked full blocks or
+// software prefetch).  Every path gives the same bits, so the choice only
+// changes speed.  ZERO_CPU_ISA forces any path the CPU has.
 CpuIsa detect_isa() {
     const char* force = std::getenv("ZERO_CPU_ISA");
     const bool has512 = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
@@ -381,7 +387,7 @@ CpuIsa detect_isa() {
         if (f == "avx2" && has2) return CpuIsa::kAvx2;
         if (f == "avx512" && has512) return CpuIsa::kAvx512;
     }
-    if (has512) return CpuIsa::kAvx512;
+    if (has512 && !(has2 && __builtin_cpu_is("amd"))) return CpuIsa::kAvx512;
     if (has2) return CpuIsa::kAvx2;
     return CpuIsa::kScalar;
 }
