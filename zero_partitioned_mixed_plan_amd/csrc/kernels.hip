@@ -83,7 +83,7 @@ static_assert(kFlatLdsPad + 512 <= kLdsPerCu / kFlatPerCu &&
 // tiles (1 MiB of flat shard) instead, so that the 128-byte line a
 // misaligned tile shares with the next one is fetched once, by one L2: the
 // 20B shard's 300 mostly misaligned pieces then read 1.0009 x 2 B x S
-// rather than 1.032 x, and the flatten ran 0.7-1.9% faster on the 8B, 20B
+// rather than 1.032 x, and the flatten ran 0.5-1.9% faster on the 8B, 20B
 // and 70B shards (runs of 4-32 tiles were slower, 64-1024 about equal).
 constexpr int64_t kXcds = 8;
 constexpr int64_t kFlatRun = 256;
