@@ -90,6 +90,64 @@ def test_flatten_every_source_misalignment(dt):
             assert np.array_equal(got, expect), (r, mode)
 
 
+# The flatten copies tiles of 2048 16-bit words and, within each launch,
+# hands every XCD runs of 256 consecutive tiles over the largest whole
+# multiple of 2048 tiles; the remaining tiles keep dispatch order.  These
+# sizes put a launch just below, at and past such multiples, with ragged
+# last tiles and misaligned sources.
+_TILE_WORDS = 2048
+_RUN_TILES = 2048
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_flatten_tile_runs_at_launch_size_edges(dt):
+    import torch
+    wpe = 2 if dt == "f32" else 1  # 16-bit words per element
+    rng = np.random.default_rng(17)
+    for n_tiles, last in [(2047, 2048), (2048, 1000), (2048, 2048), (2049, 3), (5001, 77)]:
+        words = (n_tiles - 1) * _TILE_WORDS + last
+        E = words // wpe
+        cuts = np.sort(rng.choice(np.arange(1, E), 6, replace=False))
+        numels = np.diff(np.concatenate([[0], cuts, [E]])).tolist()
+        op = oracle.plan(numels, 1, 0, 8, bucket_elems=E // 3)
+        plan = z.zero_partition_plan(numels, 1, 0, 8, E // 3)
+        assert -(-(op.real * wpe) // _TILE_WORDS) == n_tiles
+        big = torch.empty(E + 16 * len(numels) + 64, dtype=torch_dtype(dt), device=DEV)
+        host, views, off = [], [], 0
+        for i, n in enumerate(numels):
+            off += (2 * i + 1) % 8  # every source misaligned
+            bits = synth.grad_bits(rng.normal(0, 1e-2, n).astype(np.float32), dt)
+            big[off:off + n].copy_(_to_dev_half(bits, dt))
+            host.append(bits)
+            views.append(big[off:off + n])
+            off += n
+        expect = oracle.flatten(op, host)
+        for mode in ("all", "buckets"):
+            flat = torch.full((op.S,), float("nan"), dtype=torch_dtype(dt), device=DEV)
+            if mode == "all":
+                z.zero_flatten_grads(plan, -1, views, flat)
+            else:
+                for b in range(plan.n_buckets):
+                    z.zero_flatten_grads(plan, b, views, flat)
+            assert np.array_equal(_bits(flat), expect), (n_tiles, last, mode)
+        log(f"[kernels] tile runs {dt}: {n_tiles} tiles, last {last} words: flat bit-equal")
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+def test_overflow_inside_and_after_the_tile_runs(dt):
+    # one tensor of 2048 + 3 tiles: an inf in the remapped region (first,
+    # middle and last tile of the runs) and in the tail tile is each found
+    wpe = 2 if dt == "f32" else 1
+    n = (_RUN_TILES * _TILE_WORDS + 3 * _TILE_WORDS - 100) // wpe
+    bad = 0x7F800000 if dt == "f32" else 0x7C00
+    run_end = _RUN_TILES * _TILE_WORDS // wpe
+    for pos in (0, run_end // 2 + 12345, run_end - 1, run_end, n - 1):
+        flag, same, expect, _ = _gate_case(dt, [pos], bad, numels=(n,), R=1, r=0)
+        assert expect and flag == 1 and same, pos
+    flag, same, expect, _ = _gate_case(dt, [], bad, numels=(n,), R=1, r=0)
+    assert not expect and flag == 0
+
+
 def _gate_case(dt, bad_pos, bad_bits, numels=(3000, 4099, 65, 70001, 2048), R=2, r=1):
     """One step whose flat shard carries bad_bits at shard positions bad_pos;
     returns (flag, state unchanged?)."""
