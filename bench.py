@@ -254,7 +254,66 @@ def forward_stand_in(forward_ms, device):
     return (lambda: gemms(k)), k, timed(k)
 
 
-def run_offload(w, steps, warmup, device, n_threads, forward_ms=0.0):
+def _merged(iv):
+    """Union of [start, end) intervals as sorted disjoint ones."""
+    out = []
+    for a, b in sorted(iv):
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return out
+
+
+def _length(iv):
+    return sum(b - a for a, b in _merged(iv))
+
+
+def _overlap(x, y):
+    """Length of the intersection of two interval sets."""
+    x, y = _merged(x), _merged(y)
+    i = j = 0
+    tot = 0.0
+    while i < len(x) and j < len(y):
+        a, b = max(x[i][0], y[j][0]), min(x[i][1], y[j][1])
+        tot += max(0.0, b - a)
+        if x[i][1] < y[j][1]:
+            i += 1
+        else:
+            j += 1
+    return tot
+
+
+def timeline_summary(tl):
+    """Per submitted step, from the pipeline's own timeline: time spent
+    copying (gradients to the host, parameters back), updating on the host,
+    and how much of the copying ran while the host update of the same step
+    ran; medians over the steps after the first."""
+    import statistics
+    steps = sorted({r["step"] for r in tl})
+    rows = []
+    for j in steps:
+        g = [(r["start_ms"], r["end_ms"]) for r in tl
+             if r["step"] == j and r["kind"] == "gradient copy"]
+        u = [(r["start_ms"], r["end_ms"]) for r in tl
+             if r["step"] == j and r["kind"] == "host update"]
+        h = [(r["start_ms"], r["end_ms"]) for r in tl
+             if r["step"] == j and r["kind"] == "parameter copy"]
+        if not u:
+            continue
+        allv = g + u + h
+        rows.append({"gradient_copy_ms": _length(g), "host_update_ms": _length(u),
+                     "parameter_copy_ms": _length(h),
+                     "copies_during_update_ms": _overlap(g + h, u),
+                     "span_ms": max(b for _, b in allv) - min(a for a, _ in allv),
+                     "pieces": len(u)})
+    rows = rows[1:] if len(rows) > 1 else rows
+    if not rows:
+        return None
+    return {k: statistics.median(r[k] for r in rows) for k in rows[0]} | {"steps": len(rows)}
+
+
+def run_offload(w, steps, warmup, device, n_threads, forward_ms=0.0, timeline_file=None):
     """ZeRO-Offload: fp32 master / moments in host memory, the update on the
     host cores, gradients and parameters crossing PCIe; timed with the
     one-step delayed update (lag 1) and serialised (lag 0).  forward_ms > 0
@@ -280,6 +339,7 @@ def run_offload(w, steps, warmup, device, n_threads, forward_ms=0.0):
         out["forward"] = {"what": "8192^3 bf16 torch.mm chain before each step, standing in "
                                   "for the forward and backward passes",
                           "gemms_per_step": k, "ms_alone": measured}
+    timelines = {}
     for lag in (1, 0):
         m = np.zeros(S, np.float32)
         v = np.zeros(S, np.float32)
@@ -301,6 +361,8 @@ def run_offload(w, steps, warmup, device, n_threads, forward_ms=0.0):
         # pipeline after the drain does not weigh on the average
         n = steps
         while True:
+            if timeline_file:
+                off.timeline_start()
             s0 = off.stats()
             t0 = time.perf_counter()
             for _ in range(n):
@@ -312,6 +374,7 @@ def run_offload(w, steps, warmup, device, n_threads, forward_ms=0.0):
             n = min(5000, max(n + 1, int(n * 0.6 / max(wall, 1e-6))))
         st = off.stats()
         host_ms = (st["host_ms_total"] - s0["host_ms_total"]) / n
+        tl = off.timeline() if timeline_file else None
         off.close()
         out[f"lag{lag}"] = {"timed_steps": n,
                             "ms_per_step": wall * 1000.0 / n, "host_update_ms": host_ms,
@@ -324,7 +387,13 @@ def run_offload(w, steps, warmup, device, n_threads, forward_ms=0.0):
                                                    "wait_grad_ms_total", "wait_h2d_ms_total",
                                                    "wait_release_ms_total",
                                                    "caller_wait_ms_total")}}
+        if tl is not None:
+            out[f"lag{lag}"]["timeline"] = timeline_summary(tl)
+            timelines[f"lag{lag}"] = tl
         log(f"[bench] offload lag={lag}: {out[f'lag{lag}']}")
+    if timeline_file:
+        with open(timeline_file, "w") as f:
+            json.dump({"workload": w.name, "forward_ms": forward_ms, **timelines}, f)
     return plan, out
 
 
@@ -609,6 +678,10 @@ def _main(argv=None):
                     help="offload mode: run about this many ms of bf16 products on the GPU "
                          "before each step, a stand-in for the forward and backward passes "
                          "that the one-step delayed update overlaps")
+    ap.add_argument("--timeline", default=None, metavar="FILE",
+                    help="offload mode: record the pipeline's timeline of the timed steps "
+                         "(every piece's copies and host update), summarise it in the JSON "
+                         "line and write the intervals to FILE")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run only a plain copy of this many bytes (counter calibration)")
     ap.add_argument("--placement-probe", default=None, metavar="GB,GB,...",
@@ -645,7 +718,8 @@ def _main(argv=None):
         return 0
     if args.mode == "offload":
         threads = args.host_threads or max(1, host_info()["usable_cpus"] - 1)
-        plan, res = run_offload(w, args.steps, args.warmup, device, threads, args.forward_ms)
+        plan, res = run_offload(w, args.steps, args.warmup, device, threads, args.forward_ms,
+                                args.timeline)
         print(json.dumps({
             "metric": METRIC, "value": res["lag1"]["value"], "unit": "params/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["lag1"]["ms_per_step"],

@@ -451,6 +451,40 @@ int zero_offload_drain(zero_offload_t* off, void* stream);
 /* Counters of the pipeline; returns the worker's error, if any. */
 int zero_offload_stats(zero_offload_t* off, zero_offload_stats_t* out);
 
+/* One interval of the pipeline's timeline: piece `piece` of submitted step
+ * `step`; kind 0 = its gradient copy (device -> pinned host), 1 = its host
+ * update, 2 = its parameter copy (pinned host -> device).  Times in ms on
+ * one host clock, from the moment zero_offload_timeline_start returned. */
+typedef struct {
+    int64_t step;
+    int32_t piece;
+    int32_t kind;
+    double start_ms;
+    double end_ms;
+} zero_offload_interval_t;
+
+/* Records a timeline of the steps submitted from now on, up to `capacity`
+ * intervals (1 .. 2^24), to show how the copies of a step overlap its host
+ * update ([legal] offload list, DPU bullet: CPU work of one iteration
+ * overlaps GPU work).  The copies are bracketed by timing events on their
+ * own streams, the update by host clock readings; a reference event, polled
+ * by the host until it completes, puts both on the host clock (to within
+ * the polling interval, microseconds).  Costs a few events per piece; off
+ * unless called.  Call with no step in flight (after zero_offload_drain, or
+ * before the first submit); it drops what an earlier start recorded.
+ * Errors: ZERO_ENULL, ZERO_EINVAL (capacity), ZERO_ESTATE (steps in
+ * flight), ZERO_EHIP, ZERO_ENOMEM. */
+int zero_offload_timeline_start(zero_offload_t* off, int64_t capacity);
+
+/* Copies up to `cap` recorded intervals into `out` (host memory; may be
+ * NULL when cap is 0), in the order they were completed, and returns how
+ * many are stored (at most the capacity given to zero_offload_timeline_start;
+ * later intervals are dropped) or a negative error.  Call after
+ * zero_offload_drain so that the last steps' parameter copies are included.
+ * Errors: ZERO_ENULL, ZERO_EINVAL (cap < 0), ZERO_ESTATE (no timeline
+ * started, or another device current). */
+int64_t zero_offload_timeline(zero_offload_t* off, zero_offload_interval_t* out, int64_t cap);
+
 /* Completes the submitted steps, then releases the thread, stream and
  * buffers (NULL is a no-op). */
 void zero_offload_destroy(zero_offload_t* off);

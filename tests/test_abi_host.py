@@ -157,6 +157,8 @@ def test_argument_errors_before_device_work():
     assert lib.zero_update_loss_scale(ctypes.byref(bad), 0) == _abi.ZERO_EINVAL
     assert lib.zero_update_loss_scale(None, 0) == _abi.ZERO_ENULL
     assert lib.zero_flatten_invalidate(None) == _abi.ZERO_ENULL
+    assert lib.zero_offload_timeline_start(None, 16) == _abi.ZERO_ENULL
+    assert lib.zero_offload_timeline(None, None, 0) == _abi.ZERO_ENULL
     assert lib.zero_flatten_invalidate(plan.handle) == _abi.ZERO_OK
 
 

@@ -76,3 +76,22 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_timeline_summary_by_hand():
+    # two steps of two pieces: gradient copies [0,2) [2,4), updates [2,5)
+    # [5,8), parameter copies [5,6) [8,9); the second step 10 ms later.
+    # Copying 4 + 2 ms, updating 6 ms; the second gradient piece (2 ms) and
+    # the first parameter piece (1 ms) run during the update; span 9 ms.
+    tl = []
+    for j, t in ((0, 0.0), (1, 10.0)):
+        for kind, ivs in (("gradient copy", [(0, 2), (2, 4)]), ("host update", [(2, 5), (5, 8)]),
+                          ("parameter copy", [(5, 6), (8, 9)])):
+            for c, (a, b) in enumerate(ivs):
+                tl.append({"step": j, "piece": c, "kind": kind, "start_ms": a + t,
+                           "end_ms": b + t})
+    s = bench.timeline_summary(tl)
+    assert s == {"gradient_copy_ms": 4.0, "host_update_ms": 6.0, "parameter_copy_ms": 2.0,
+                 "copies_during_update_ms": 3.0, "span_ms": 9.0, "pieces": 2, "steps": 1}
+    assert bench._overlap([(0, 3), (5, 9)], [(2, 6), (8, 10)]) == 1 + 1 + 1
+    assert bench._length([(0, 2), (1, 3), (5, 6)]) == 4

@@ -8,7 +8,10 @@ device, zero_flatten_grads, submit.  Checked:
     the serialised step) -- so the parameter copy never lands early or late;
   * the device loss scale before each iteration equals the oracle's;
   * after drain: host master / moments and the device parameters equal the
-    oracle's bit for bit, and the applied / skipped counts match.
+    oracle's bit for bit, and the applied / skipped counts match;
+  * where a timeline is recorded: every piece's copies and update in the
+    order the pipeline must run them (an update after its gradient arrived,
+    a parameter copy after its update).
 """
 import numpy as np
 import pytest
@@ -28,7 +31,49 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def _offload_run(case, lag, label, write_params=True, n_threads=4):
+_EPS_MS = 0.05  # clock mapping of the timeline: the host's polling of one reference event
+
+
+def _check_timeline(tl, steps, skipped_steps, write_params, real, S, label):
+    """The recorded intervals against what the pipeline must do: every step
+    copies every gradient piece in order; every applied step updates every
+    piece after its gradient arrived, in order, and copies back the pieces
+    holding real parameters only after their update."""
+    by = {}
+    for r in tl:
+        assert r["end_ms"] >= r["start_ms"] - _EPS_MS, (label, r)
+        by.setdefault((r["step"], r["kind"]), {})[r["piece"]] = (r["start_ms"], r["end_ms"])
+    grads0 = by.get((0, "gradient copy"), {})
+    n = len(grads0)
+    assert n >= 1 and sorted(grads0) == list(range(n)), (label, sorted(grads0))
+    sent_pieces = None
+    for j in range(steps):
+        g = by.get((j, "gradient copy"), {})
+        assert sorted(g) == list(range(n)), (label, j, "gradient pieces")
+        for c in range(1, n):
+            assert g[c][0] >= g[c - 1][1] - _EPS_MS, (label, j, c, "gradient copies out of order")
+        u = by.get((j, "host update"), {})
+        h = by.get((j, "parameter copy"), {})
+        if j in skipped_steps:
+            assert not u and not h, (label, j, "a skipped step updated or copied")
+            continue
+        assert sorted(u) == list(range(n)), (label, j, "update pieces")
+        for c in range(n):
+            assert u[c][0] >= g[c][1] - _EPS_MS, (label, j, c, "update before its gradient")
+            if c:
+                assert u[c][0] >= u[c - 1][1] - _EPS_MS, (label, j, c, "updates out of order")
+        if not write_params or real == 0:
+            assert not h, (label, j, "parameters copied without param_dtype")
+            continue
+        assert h and sorted(h) == list(range(len(h))), (label, j, sorted(h))
+        assert len(h) == n if real == S else len(h) <= n, (label, j, len(h), n)
+        sent_pieces = len(h) if sent_pieces is None else sent_pieces
+        assert len(h) == sent_pieces, (label, j, "parameter pieces vary between steps")
+        for c in h:
+            assert h[c][0] >= u[c][1] - _EPS_MS, (label, j, c, "parameters sent before the update")
+
+
+def _offload_run(case, lag, label, write_params=True, n_threads=4, timeline=False):
     import torch
     dev = torch.device("cuda:0")
     orc = OracleRun(case)
@@ -48,8 +93,11 @@ def _offload_run(case, lag, label, write_params=True, n_threads=4):
     flat = torch.empty(max(S, 1), dtype=gdt, device=dev)
     off = z.Offload(plan, hp, case.grad_dtype, case.param_dtype if write_params else None,
                     master, mom, var, n_threads=n_threads)
+    if timeline:
+        off.timeline_start()
     hist = [orc.params().copy()]       # oracle parameters after iteration k
     skipped = 0
+    skipped_steps = set()
     log(f"[offload] {label}: S={S} real={real} lag={lag} steps={case.steps}")
     for it in range(1, case.steps + 1):
         off.wait_params(lag)
@@ -62,12 +110,16 @@ def _offload_run(case, lag, label, write_params=True, n_threads=4):
         z.zero_flatten_grads(plan, -1, grads_dev, flat)
         off.submit(flat, param if write_params else None, 0)
         skipped += o_ovf
+        if o_ovf:
+            skipped_steps.add(it - 1)
         hist.append(orc.params().copy())
         if write_params:
             want = hist[max(it - 1 - lag, 0)]
             assert np.array_equal(_bits(seen), want), \
                 f"{label} it={it}: the forward saw other parameters than iteration {it - 1 - lag}'s"
     off.drain()
+    if timeline:
+        _check_timeline(off.timeline(), case.steps, skipped_steps, write_params, real, S, label)
     stats = off.stats()
     assert stats["applied"] == orc.t and stats["skipped"] == skipped, stats
     assert stats["submitted"] == stats["processed"] == case.steps, stats
@@ -128,15 +180,15 @@ def test_offload_in_many_pieces(lag, monkeypatch):
     case = Case(numels=RAGGED, world_size=3, rank=2, grad_dtype="f16", param_dtype="f16",
                 steps=7, dynamic=True, init_scale=1024.0, window=2, grad_sigma=1e-2,
                 inject={4: 99999})
-    assert _offload_run(case, lag, f"pieces lag={lag}") == 1
+    assert _offload_run(case, lag, f"pieces lag={lag}", timeline=True) == 1
     case = Case(numels=RAGGED, world_size=2, rank=1, grad_dtype="f32", param_dtype="bf16",
                 steps=4, grad_sigma=1e-2)
-    assert _offload_run(case, lag, f"pieces fp32 lag={lag}") == 0
+    assert _offload_run(case, lag, f"pieces fp32 lag={lag}", timeline=True) == 0
 
 
 def test_offload_gpt2_small():
     case = Case.from_workload(get("gpt2_small"), steps=6)
-    _offload_run(case, 1, "gpt2_small", n_threads=8)
+    _offload_run(case, 1, "gpt2_small", n_threads=8, timeline=True)
 
 
 @pytest.mark.parametrize("seed", range(60))
@@ -155,8 +207,10 @@ def test_offload_random_configuration(seed, monkeypatch):
     piece = rnd.choice([64, 256, 4096, None])
     if piece is not None:
         monkeypatch.setenv("ZERO_OFFLOAD_MIN_CHUNK", str(piece))
+    timeline = rnd.random() < 0.5
     label = (f"offload random seed={seed} numels={case.numels} R={case.world_size} "
              f"r={case.rank} A={case.align} grads={case.grad_dtype} params={case.param_dtype} "
              f"adamw={case.adamw} inject_p={case.inject_p} lag={lag} write={write_params} "
-             f"threads={threads} piece={piece}")
-    _offload_run(case, lag, label, write_params=write_params, n_threads=threads)
+             f"threads={threads} piece={piece} timeline={timeline}")
+    _offload_run(case, lag, label, write_params=write_params, n_threads=threads,
+                 timeline=timeline)

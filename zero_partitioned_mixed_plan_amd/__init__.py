@@ -589,6 +589,24 @@ class Offload:
         check(lib.zero_offload_stats(self._h, ctypes.byref(st)), "zero_offload_stats")
         return {k: getattr(st, k) for k, _ in st._fields_ if k != "_pad"}
 
+    TIMELINE_KINDS = ("gradient copy", "host update", "parameter copy")
+
+    def timeline_start(self, capacity: int = 1 << 20) -> None:
+        """Record the copies and host update of every piece of the steps
+        submitted from now on (call with no step in flight)."""
+        check(lib.zero_offload_timeline_start(self._h, int(capacity)),
+              "zero_offload_timeline_start")
+
+    def timeline(self) -> List[dict]:
+        """The recorded intervals (call after drain()): step, piece, kind
+        (one of TIMELINE_KINDS), start_ms, end_ms on one host clock."""
+        n = int(check(lib.zero_offload_timeline(self._h, None, 0), "zero_offload_timeline"))
+        buf = (_abi.zero_offload_interval_t * max(n, 1))()
+        kept = min(n, int(check(lib.zero_offload_timeline(self._h, buf, n),
+                                "zero_offload_timeline")))  # stored count; it only grows
+        return [{"step": r.step, "piece": r.piece, "kind": self.TIMELINE_KINDS[r.kind],
+                 "start_ms": r.start_ms, "end_ms": r.end_ms} for r in buf[:kept]]
+
     _destroy = staticmethod(lib.zero_offload_destroy)
     _finalizing = staticmethod(sys.is_finalizing)
 

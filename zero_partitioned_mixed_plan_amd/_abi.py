@@ -60,6 +60,11 @@ class zero_offload_stats_t(ctypes.Structure):
                 ("caller_wait_ms_total", ctypes.c_double)]
 
 
+class zero_offload_interval_t(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int64), ("piece", ctypes.c_int32), ("kind", ctypes.c_int32),
+                ("start_ms", ctypes.c_double), ("end_ms", ctypes.c_double)]
+
+
 class zero_scaler_t(ctypes.Structure):
     _fields_ = [("scale", ctypes.c_double), ("min_scale", ctypes.c_double),
                 ("backoff", ctypes.c_double), ("growth", ctypes.c_double),
@@ -105,6 +110,9 @@ SIGNATURES = {
     "zero_offload_wait_params": (ctypes.c_int, [_VP, _I32, _VP]),
     "zero_offload_drain": (ctypes.c_int, [_VP, _VP]),
     "zero_offload_stats": (ctypes.c_int, [_VP, ctypes.POINTER(zero_offload_stats_t)]),
+    "zero_offload_timeline_start": (ctypes.c_int, [_VP, _I64]),
+    "zero_offload_timeline": (ctypes.c_int64, [_VP, ctypes.POINTER(zero_offload_interval_t),
+                                               _I64]),
     "zero_offload_destroy": (None, [_VP]),
     "zero_adam_scalars": (ctypes.c_int, [ctypes.POINTER(zero_adam_hparams_t), _I64, _I64,
                                          ctypes.c_double, _VP, _I32, _VP]),

@@ -40,6 +40,7 @@
 #include <new>
 #include <string>
 #include <thread>
+#include <vector>
 
 #include "internal.h"
 
@@ -52,6 +53,7 @@ struct Pending {
     bool free_recorded = false;     // ev_free[b] holds the release point
     bool processed = false;         // host part done, H2D enqueued (or step skipped)
     bool applied = false;
+    bool timeline = false;          // the submit recorded timeline events for this step
 };
 
 constexpr int kMaxChunks = 16;                       // gradient / parameter copy pieces
@@ -61,6 +63,8 @@ constexpr int64_t kMinChunkElems = int64_t(1) << 25;  // per piece (64-128 MB of
 }  // namespace zmi
 
 using namespace zmi;
+
+using Clock0 = std::chrono::steady_clock::time_point;
 
 struct zero_offload {
     zero_plan* plan = nullptr;
@@ -100,6 +104,20 @@ struct zero_offload {
     double caller_wait_ms = 0;
     int err = ZERO_OK;
     std::string err_msg;
+    // optional timeline (zero_offload_timeline_start): timing events around
+    // every piece's copies, host times around its update, all on one host
+    // clock; tl_* written by the submitting thread before a step is handed
+    // over, or by the worker while it owns the step, read under mu
+    bool tl_on = false;
+    int64_t tl_cap = 0;
+    Clock0 tl_t0{};                 // host time of the reference event
+    hipEvent_t tl_ref = nullptr;    // reference event, completed at tl_t0
+    hipEvent_t tl_d2h[2][kMaxChunks][2] = {};  // start / end of each gradient piece
+    hipEvent_t tl_h2d[2][kMaxChunks][2] = {};  // start / end of each parameter piece
+    bool tl_d2h_rec[2] = {false, false};       // step in buffer b recorded its gradient events
+    int64_t tl_h2d_step[2] = {-1, -1};         // step whose parameter events buffer b holds
+    bool tl_h2d_sent[2][kMaxChunks] = {};      // pieces of that step with recorded events
+    std::vector<zero_offload_interval_t> tl;
 };
 
 namespace {
@@ -126,6 +144,56 @@ int worker_hip(zero_offload* o, hipError_t e, const char* what) {
     return ZERO_EHIP;
 }
 
+// ---- timeline (caller holds mu for tl_push and tl_read_h2d)
+double tl_host_ms(const zero_offload* o, Clock::time_point t) {
+    return std::chrono::duration<double, std::milli>(t - o->tl_t0).count();
+}
+
+void tl_push(zero_offload* o, int64_t step, int piece, int kind, double t0, double t1) {
+    if (static_cast<int64_t>(o->tl.size()) >= o->tl_cap) return;  // past the capacity: dropped
+    zero_offload_interval_t r{};
+    r.step = step;
+    r.piece = piece;
+    r.kind = kind;
+    r.start_ms = t0;
+    r.end_ms = t1;
+    o->tl.push_back(r);
+}
+
+// Start and end of an event pair on the host clock; false if not complete.
+bool tl_pair_ms(const zero_offload* o, hipEvent_t const (&ev)[2], double* t0, double* t1) {
+    float a = 0.f, b = 0.f;
+    if (hipEventElapsedTime(&a, o->tl_ref, ev[0]) != hipSuccess) return false;
+    if (hipEventElapsedTime(&b, o->tl_ref, ev[1]) != hipSuccess) return false;
+    *t0 = a;
+    *t1 = b;
+    return true;
+}
+
+// The parameter-copy intervals buffer b holds, once its copies are complete
+// (wait = false: only if they already are).  Returns false if they are not.
+bool tl_read_h2d(zero_offload* o, int b, bool wait) {
+    if (o->tl_h2d_step[b] < 0) return true;
+    int last = -1;
+    for (int c = 0; c < o->n_chunks; ++c) {
+        if (o->tl_h2d_sent[b][c]) last = c;
+    }
+    if (last >= 0) {
+        const hipError_t e = wait ? hipEventSynchronize(o->tl_h2d[b][last][1])
+                                  : hipEventQuery(o->tl_h2d[b][last][1]);
+        if (e != hipSuccess) return false;
+        for (int c = 0; c <= last; ++c) {
+            double t0 = 0, t1 = 0;
+            if (o->tl_h2d_sent[b][c] && tl_pair_ms(o, o->tl_h2d[b][c], &t0, &t1)) {
+                tl_push(o, o->tl_h2d_step[b], c, 2, t0, t1);
+            }
+            o->tl_h2d_sent[b][c] = false;
+        }
+    }
+    o->tl_h2d_step[b] = -1;
+    return true;
+}
+
 // Enqueues the parameter copies of chunks [*sent, upto) of step buffer b on
 // the transfer stream, gated once on the caller's release of the device
 // parameters.  block = false: does nothing until that release is recorded.
@@ -138,6 +206,8 @@ int send_params(zero_offload* o, int b, int upto, bool block, int* sent, bool* g
         return ZERO_OK;
     }
     uint16_t* dst = nullptr;
+    bool tl = false;
+    int64_t step = -1;
     {
         std::unique_lock<std::mutex> lk(o->mu);
         if (!o->rec[b].free_recorded) {
@@ -148,6 +218,8 @@ int send_params(zero_offload* o, int b, int upto, bool block, int* sent, bool* g
             *wait_release += ms_since(tw);
         }
         dst = o->rec[b].param_dst;
+        tl = o->rec[b].timeline;
+        step = o->rec[b].idx;
     }
     if (dst == nullptr) {
         *sent = upto;
@@ -163,11 +235,24 @@ int send_params(zero_offload* o, int b, int upto, bool block, int* sent, bool* g
         const int64_t lo = c * o->chunk;
         const int64_t hi = std::min(p->real, lo + o->chunk);
         if (hi <= lo) continue;
+        if (tl && worker_hip(o, hipEventRecord(o->tl_h2d[b][c][0], o->xfer), "hipEventRecord") !=
+                      ZERO_OK) {
+            return ZERO_EHIP;
+        }
         if (worker_hip(o, hipMemcpyAsync(dst + lo, o->hparam[b] + lo,
                                          2 * static_cast<size_t>(hi - lo),
                                          hipMemcpyHostToDevice, o->xfer),
                        "parameter copy") != ZERO_OK) {
             return ZERO_EHIP;
+        }
+        if (tl) {
+            if (worker_hip(o, hipEventRecord(o->tl_h2d[b][c][1], o->xfer), "hipEventRecord") !=
+                ZERO_OK) {
+                return ZERO_EHIP;
+            }
+            std::lock_guard<std::mutex> g(o->mu);
+            o->tl_h2d_step[b] = step;
+            o->tl_h2d_sent[b][c] = true;
         }
     }
     *sent = upto;
@@ -187,6 +272,19 @@ void worker_main(zero_offload* o) {
             if (o->submitted <= j) return;  // stopped with nothing left
         }
         const double wait_submit = ms_since(tw);
+        bool tl = false;
+        {
+            std::lock_guard<std::mutex> g(o->mu);
+            tl = o->rec[b].timeline;
+        }
+        // gradient piece c of this step as an interval (its copies are done)
+        const auto tl_d2h = [&](int c) {
+            double t0 = 0, t1 = 0;
+            if (tl && tl_pair_ms(o, o->tl_d2h[b][c], &t0, &t1)) {
+                std::lock_guard<std::mutex> g(o->mu);
+                tl_push(o, j, c, 0, t0, t1);
+            }
+        };
         tw = Clock::now();
         if (worker_hip(o, hipEventSynchronize(o->ev_slot[b]), "slot copy") != ZERO_OK) return;
         double wait_grad = ms_since(tw), wait_h2d = 0, wait_release = 0, host_ms = 0;
@@ -201,6 +299,10 @@ void worker_main(zero_offload* o) {
                 return;
             }
             wait_h2d = ms_since(tw);
+            if (o->h2d_recorded[b]) {  // step j - 2's parameter copies are complete
+                std::lock_guard<std::mutex> g(o->mu);
+                (void)tl_read_h2d(o, b, false);
+            }
             CpuAdamArgs a;
             a.sc = make_scalars(o->hp.lr, o->hp.beta1, o->hp.beta2, o->hp.eps,
                                 o->hp.weight_decay, o->hp.adamw, static_cast<double>(slot.t),
@@ -218,6 +320,7 @@ void worker_main(zero_offload* o) {
                     return;
                 }
                 wait_grad += ms_since(tw);
+                tl_d2h(c);
                 a.g = static_cast<const char*>(o->hgrad[b]) + esize * static_cast<size_t>(lo);
                 a.p = o->master + lo;
                 a.m = o->m + lo;
@@ -227,7 +330,12 @@ void worker_main(zero_offload* o) {
                 a.real = std::max<int64_t>(0, std::min(p->real, hi) - lo);
                 const auto t0 = Clock::now();
                 cpu_adam(a, o->n_threads, o->pool);
-                host_ms += ms_since(t0);
+                const auto t1 = Clock::now();
+                host_ms += std::chrono::duration<double, std::milli>(t1 - t0).count();
+                if (tl) {
+                    std::lock_guard<std::mutex> g(o->mu);
+                    tl_push(o, j, c, 1, tl_host_ms(o, t0), tl_host_ms(o, t1));
+                }
                 // this chunk's parameters go back now if the caller has released
                 if (send_params(o, b, c + 1, false, &sent, &gated, &wait_release) != ZERO_OK) {
                     return;
@@ -250,6 +358,7 @@ void worker_main(zero_offload* o) {
                 return;
             }
             wait_grad += ms_since(tw);
+            for (int c = 0; c < o->n_chunks; ++c) tl_d2h(c);
         }
         std::lock_guard<std::mutex> g(o->mu);
         if (gated) o->h2d_recorded[b] = true;
@@ -330,6 +439,15 @@ void release_all(zero_offload* o) {
         }
         if (o->ev_free[b]) (void)hipEventDestroy(o->ev_free[b]);
         if (o->ev_h2d[b]) (void)hipEventDestroy(o->ev_h2d[b]);
+    }
+    if (o->tl_ref) (void)hipEventDestroy(o->tl_ref);
+    for (int b = 0; b < 2; ++b) {
+        for (int c = 0; c < kMaxChunks; ++c) {
+            for (int k = 0; k < 2; ++k) {
+                if (o->tl_d2h[b][c][k]) (void)hipEventDestroy(o->tl_d2h[b][c][k]);
+                if (o->tl_h2d[b][c][k]) (void)hipEventDestroy(o->tl_h2d[b][c][k]);
+            }
+        }
     }
     if (o->hslot) (void)hipHostFree(o->hslot);
     if (o->dslot) (void)hipFree(o->dslot);
@@ -479,13 +597,21 @@ int zero_offload_submit(zero_offload_t* o, const void* flat_grad, void* param, i
     e = hipEventRecord(o->ev_slot[b], s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     const size_t esize = static_cast<size_t>(grad_bytes(o->gdt));
+    const bool tl = o->tl_on;
     for (int c = 0; c < o->n_chunks; ++c) {
         const int64_t lo = c * o->chunk;
         const int64_t hi = std::min(p->S, lo + o->chunk);
+        if (tl && (e = hipEventRecord(o->tl_d2h[b][c][0], s)) != hipSuccess) {
+            return hip_fail(e, "hipEventRecord");
+        }
         e = hipMemcpyAsync(static_cast<char*>(o->hgrad[b]) + esize * static_cast<size_t>(lo),
                            static_cast<const char*>(flat_grad) + esize * static_cast<size_t>(lo),
                            esize * static_cast<size_t>(hi - lo), hipMemcpyDeviceToHost, s);
         if (e != hipSuccess) return hip_fail(e, "gradient copy");
+        // the timeline's end event before ev_d2h: complete once the worker sees ev_d2h
+        if (tl && (e = hipEventRecord(o->tl_d2h[b][c][1], s)) != hipSuccess) {
+            return hip_fail(e, "hipEventRecord");
+        }
         e = hipEventRecord(o->ev_d2h[b][c], s);
         if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
@@ -495,6 +621,7 @@ int zero_offload_submit(zero_offload_t* o, const void* flat_grad, void* param, i
         r = Pending{};
         r.idx = i;
         r.param_dst = param0;
+        r.timeline = tl;
         o->submitted = i + 1;
     }
     o->cv.notify_all();
@@ -569,6 +696,72 @@ int zero_offload_stats(zero_offload_t* o, zero_offload_stats_t* out) {
         out->caller_wait_ms_total = o->caller_wait_ms;
     }
     return offload_error(o);
+}
+
+int zero_offload_timeline_start(zero_offload_t* o, int64_t capacity) {
+    if (o == nullptr) return fail(ZERO_ENULL, "offload is NULL");
+    if (capacity < 1 || capacity > (int64_t(1) << 24)) {
+        return fail(ZERO_EINVAL, "capacity must be in [1, 2^24]");
+    }
+    int rc = check_device(o);
+    if (rc != ZERO_OK) return rc;
+    if ((rc = offload_error(o)) != ZERO_OK) return rc;
+    {
+        std::lock_guard<std::mutex> g(o->mu);
+        if (o->processed != o->submitted) {
+            return fail(ZERO_ESTATE, "steps in flight: drain the pipeline first");
+        }
+    }
+    hipError_t e = hipSuccess;
+    if (o->tl_ref == nullptr) {
+        e = hipEventCreate(&o->tl_ref);
+        for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+            for (int c = 0; c < o->n_chunks && e == hipSuccess; ++c) {
+                for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+                    e = hipEventCreate(&o->tl_d2h[b][c][k]);
+                    if (e == hipSuccess) e = hipEventCreate(&o->tl_h2d[b][c][k]);
+                }
+            }
+        }
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    // the transfer stream idle, then a reference event the host sees complete
+    if ((e = hipStreamSynchronize(o->xfer)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    if ((e = hipEventRecord(o->tl_ref, o->xfer)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    while ((e = hipEventQuery(o->tl_ref)) == hipErrorNotReady) {
+    }
+    const auto t0 = Clock::now();
+    if (e != hipSuccess) return hip_fail(e, "hipEventQuery");
+    std::lock_guard<std::mutex> g(o->mu);
+    o->tl.clear();
+    try {
+        o->tl.reserve(static_cast<size_t>(std::min<int64_t>(capacity, int64_t(1) << 16)));
+    } catch (const std::exception&) {
+        return fail(ZERO_ENOMEM, "timeline allocation failed");
+    }
+    for (int b = 0; b < 2; ++b) {
+        o->tl_h2d_step[b] = -1;
+        for (int c = 0; c < kMaxChunks; ++c) o->tl_h2d_sent[b][c] = false;
+    }
+    o->tl_cap = capacity;
+    o->tl_t0 = t0;
+    o->tl_on = true;
+    return ZERO_OK;
+}
+
+int64_t zero_offload_timeline(zero_offload_t* o, zero_offload_interval_t* out, int64_t cap) {
+    if (o == nullptr) return fail(ZERO_ENULL, "offload is NULL");
+    if (cap < 0) return fail(ZERO_EINVAL, "cap must be >= 0");
+    if (cap > 0 && out == nullptr) return fail(ZERO_ENULL, "out is NULL");
+    int rc = check_device(o);
+    if (rc != ZERO_OK) return rc;
+    std::lock_guard<std::mutex> g(o->mu);
+    if (!o->tl_on) return fail(ZERO_ESTATE, "no timeline was started");
+    // parameter copies not read yet: those already complete
+    for (int b = 0; b < 2; ++b) (void)tl_read_h2d(o, b, false);
+    const int64_t n = std::min<int64_t>(cap, static_cast<int64_t>(o->tl.size()));
+    if (n > 0) std::memcpy(out, o->tl.data(), static_cast<size_t>(n) * sizeof(*out));
+    return static_cast<int64_t>(o->tl.size());
 }
 
 void zero_offload_destroy(zero_offload_t* o) {
