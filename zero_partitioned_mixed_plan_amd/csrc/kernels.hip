@@ -19,7 +19,8 @@
 //     best shape was 128 threads with two elements each, t and t + 128,
 //     both loaded before the math: 37.1 ms vs 38.2 ms for 256 threads x 1
 //     element, 37.6 ms for 256 x 4 and 38.1 ms for 64 x 2 (same box, same
-//     run).  Below 7.5e9 elements 256 x 1 is faster (see adam_dispatch_d).
+//     run).  Below 7.5e9 elements, and for fp32 gradients at any size,
+//     256 x 1 is faster (see adam_dispatch_d).
 //   * non-temporal loads and stores (the streaming cache policy) on the
 //     three fp32 state arrays, plain accesses for the gradient (half, or
 //     fp32 when gradients are kept in fp32) and the half parameter: +3-6%
@@ -92,7 +93,7 @@ constexpr int64_t kGridX = 65536;           // x extent of the 2-D grids
 // launcher picks by shard size): 256 threads x 1 element, or 128 threads x
 // 2 elements (t and t + 128)
 constexpr int64_t kAdamSpan = 256;
-constexpr int64_t kAdamBigShard = 7500000000LL;  // from here on: 128 x 2
+constexpr int64_t kAdamBigShard = 7500000000LL;  // from here on: 128 x 2 (half gradients)
 constexpr int kWritePer = 8;                // parameter cast: elements per thread,
 constexpr int64_t kWriteSpan = kThreads * kWritePer;  // 2048 per workgroup
 
@@ -511,12 +512,14 @@ void adam_launch(const AdamScalars* dsc, dim3 grid, hipStream_t s, const void* g
 // elements and matched it at 7e9, but 1.3-1.5% slower at 8.6e9.  The
 // 128 x 2 shape was also 3-4% slower at 1e9 and 2.5e9 when the arrays were
 // the process's first allocations than after 100 GB of other buffers, which
-// did not move 256 x 1.
+// did not move 256 x 1.  With gradients kept in fp32 (30 B per element)
+// 256 x 1 stays ahead at 8.6e9 too: 40.8 against 42.6 ms, alternating the
+// two over six rounds.
 template <int GDT, int PDT, bool ADAMW>
 hipError_t adam_dispatch_d(const AdamScalars* dsc, dim3 grid, hipStream_t s, const void* g,
                            float* master, float* m, float* v, uint16_t* param, int64_t S,
                            int64_t real, const int* flag, const AdamScalars& sc) {
-    if (S >= kAdamBigShard) {
+    if (GDT != ZERO_F32 && S >= kAdamBigShard) {
         adam_launch<GDT, PDT, ADAMW, 128>(dsc, grid, s, g, master, m, v, param, S, real, flag, sc);
     } else {
         adam_launch<GDT, PDT, ADAMW, 256>(dsc, grid, s, g, master, m, v, param, S, real, flag, sc);
