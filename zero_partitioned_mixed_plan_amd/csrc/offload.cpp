@@ -170,18 +170,17 @@ bool tl_pair_ms(const zero_offload* o, hipEvent_t const (&ev)[2], double* t0, do
     return true;
 }
 
-// The parameter-copy intervals buffer b holds, once its copies are complete
-// (wait = false: only if they already are).  Returns false if they are not.
-bool tl_read_h2d(zero_offload* o, int b, bool wait) {
-    if (o->tl_h2d_step[b] < 0) return true;
+// Moves the parameter-copy intervals buffer b holds into the timeline if
+// its copies are complete (one stream: the last piece's end implies the
+// others'); otherwise leaves them for a later call.
+void tl_read_h2d(zero_offload* o, int b) {
+    if (o->tl_h2d_step[b] < 0) return;
     int last = -1;
     for (int c = 0; c < o->n_chunks; ++c) {
         if (o->tl_h2d_sent[b][c]) last = c;
     }
     if (last >= 0) {
-        const hipError_t e = wait ? hipEventSynchronize(o->tl_h2d[b][last][1])
-                                  : hipEventQuery(o->tl_h2d[b][last][1]);
-        if (e != hipSuccess) return false;
+        if (hipEventQuery(o->tl_h2d[b][last][1]) != hipSuccess) return;
         for (int c = 0; c <= last; ++c) {
             double t0 = 0, t1 = 0;
             if (o->tl_h2d_sent[b][c] && tl_pair_ms(o, o->tl_h2d[b][c], &t0, &t1)) {
@@ -191,7 +190,6 @@ bool tl_read_h2d(zero_offload* o, int b, bool wait) {
         }
     }
     o->tl_h2d_step[b] = -1;
-    return true;
 }
 
 // Enqueues the parameter copies of chunks [*sent, upto) of step buffer b on
@@ -301,7 +299,7 @@ void worker_main(zero_offload* o) {
             wait_h2d = ms_since(tw);
             if (o->h2d_recorded[b]) {  // step j - 2's parameter copies are complete
                 std::lock_guard<std::mutex> g(o->mu);
-                (void)tl_read_h2d(o, b, false);
+                tl_read_h2d(o, b);
             }
             CpuAdamArgs a;
             a.sc = make_scalars(o->hp.lr, o->hp.beta1, o->hp.beta2, o->hp.eps,
@@ -758,7 +756,7 @@ int64_t zero_offload_timeline(zero_offload_t* o, zero_offload_interval_t* out, i
     std::lock_guard<std::mutex> g(o->mu);
     if (!o->tl_on) return fail(ZERO_ESTATE, "no timeline was started");
     // parameter copies not read yet: those already complete
-    for (int b = 0; b < 2; ++b) (void)tl_read_h2d(o, b, false);
+    for (int b = 0; b < 2; ++b) tl_read_h2d(o, b);
     const int64_t n = std::min<int64_t>(cap, static_cast<int64_t>(o->tl.size()));
     if (n > 0) std::memcpy(out, o->tl.data(), static_cast<size_t>(n) * sizeof(*out));
     return static_cast<int64_t>(o->tl.size());
