@@ -191,6 +191,8 @@ def run_graph(bufs, steps, warmup, device):
         step()
         dev_ms.append(plan.kernel_ms(2))
     torch.cuda.synchronize(device)
+    # captured without the plan's timing events, as a caller would capture it
+    plan.set_timing(False)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
@@ -206,6 +208,7 @@ def run_graph(bufs, steps, warmup, device):
     done = (after.applied_steps + after.skipped_steps) - (before.applied_steps +
                                                           before.skipped_steps)
     assert done == steps + warmup + max(warmup, 2), (done, steps, warmup)
+    plan.set_timing(True)
     log(f"[bench] graph: {steps} replays in {wall:.3f} s; skipped {after.skipped_steps}")
     return wall, sum(dev_ms[1:]) / len(dev_ms[1:])
 
