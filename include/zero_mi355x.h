@@ -214,10 +214,11 @@ int zero_flatten_invalidate(zero_plan_t* plan);
  * step: the bias-correction step t >= 1 (count applied steps only).
  * loss_scale: finite, > 0.  flat_grad: device, >= S elements of grad_dtype
  * (ZERO_F16, ZERO_BF16 or ZERO_F32), 16-byte aligned.  master/exp_avg/exp_avg_sq: device fp32 arrays of >= S
- * elements, 4-byte aligned (for full bandwidth: 256-byte aligned and in
- * separate allocations, as hipMalloc / torch give them -- on MI355X an array
- * starting 12 bytes past a 128-byte line ran the update at 57% of peak
- * instead of 81%, and the three arrays packed into one allocation at 75-78%).  param: device buffer holding flat
+ * elements, 4-byte aligned (for full bandwidth: all five arrays at the same
+ * offset within a 4 KB page, as separate hipMalloc / torch allocations give
+ * them -- on MI355X an array starting 12 bytes past a 128-byte line ran the
+ * update at 57% of peak instead of 81%, and arrays 256 or 768 bytes apart
+ * within a page 3-5% slower).  param: device buffer holding flat
  * indices [param_base, param_base + param_numel), which must contain
  * [shard_begin, shard_begin + real); 2-byte aligned.
  * Returns 0 applied, 1 skipped, or a negative error (ZERO_ENULL,
