@@ -14,7 +14,8 @@
 // The fp16 and fp32-gradient cases run a second time with the gated update
 // through zero_adam_step_noalloc (the flag read from the caller's device
 // int), and the update scalars that zero_adam_scalars forms on the device
-// are compared with the host's for t = 1..4096.
+// are compared with the host's for t = 1..4096.  Then the ZeRO-Offload
+// pipeline through its calls alone (offload_case).
 //
 // Prints "c-abi ok" and exits 0 on success; prints the first mismatch and
 // exits 1 otherwise.
@@ -271,6 +272,182 @@ int run_case(int gdt, int pdt, int adamw, int noalloc) {
     return 0;
 }
 
+// ZeRO-Offload through the C ABI: host-resident master / moments, the
+// pipeline at lag 1 (one-step delayed update) or lag 0, an overflow at step
+// 3.  Each iteration a stand-in forward copies the device parameters after
+// zero_offload_wait_params; they must be the oracle's after iteration
+// it - 1 - lag.  After the drain the host state and the device parameters
+// must equal the oracle's, and the timeline must hold every piece's copies
+// and host update in the pipeline's order.
+int offload_case(int gdt, int pdt, int lag) {
+    const size_t esize = gdt == ZERO_F32 ? 4 : 2;
+    const std::vector<int64_t> numels = {3000, 1, 7, 100003, 65, 2048, 511, 30000, 13};
+    const int R = 3, r = 1, A = 8, steps = 7, inject_step = 3;
+    const int64_t B = 20000;
+    const int n = static_cast<int>(numels.size());
+    std::vector<int64_t> off(n + 1, 0);
+    for (int i = 0; i < n; ++i) off[i + 1] = off[i] + numels[i];
+    const int64_t P = off[n];
+    zero_plan_t* plan = nullptr;
+    ZERO_OK_OR_FAIL(zero_partition_plan(numels.data(), n, R, r, A, B, &plan));
+    int64_t scal[10];
+    std::vector<int64_t> st(n), sto(n), sso(n), sn(n), tb(n);
+    if (oracle_plan(numels.data(), n, R, r, A, B, scal, st.data(), sto.data(), sso.data(),
+                    sn.data(), tb.data()) != 0) {
+        std::printf("oracle_plan failed\n");
+        return 1;
+    }
+    const int64_t S = scal[2], begin = scal[3], real = scal[4], nseg = scal[5];
+
+    std::vector<void*> d_grads(n, nullptr);
+    for (int i = 0; i < n; ++i) HIP_OK(hipMalloc(&d_grads[i], esize * numels[i]));
+    void *d_flat, *d_param;
+    HIP_OK(hipMalloc(&d_flat, esize * S));
+    HIP_OK(hipMalloc(&d_param, 2 * P));
+    std::vector<float> o_master(S, 0.0f), o_m(S, 0.0f), o_v(S, 0.0f);
+    synth_fill_f32(o_master.data(), real, synth_key(0, 2, 0), begin, 0.02f, 1.0f, 0, 1.0f);
+    std::vector<float> h_master(o_master), h_m(S, 0.0f), h_v(S, 0.0f);  // the pipeline's state
+    std::vector<uint16_t> o_param(P, 0xFFFF);
+    HIP_OK(hipMemcpy(d_param, o_param.data(), 2 * P, hipMemcpyHostToDevice));
+    std::vector<std::vector<uint16_t>> hist = {o_param};  // oracle parameters after iteration k
+
+    const zero_adam_hparams_t hp = {1e-3, 0.9, 0.999, 1e-8, 0.05, 1, 0};
+    const int dynamic = gdt != ZERO_BF16;
+    zero_scaler_t scaler = {dynamic ? 1024.0 : 1.0, 1.0, 0.5, 2.0, 2, 0, dynamic, 0};
+    double o_scale = scaler.scale;
+    int32_t o_good = 0;
+    int64_t o_t = 0;
+    int skipped = 0;
+    hipStream_t s;
+    HIP_OK(hipStreamCreate(&s));
+    ZERO_OK_OR_FAIL(zero_state_upload(plan, 0, &scaler, s));
+    zero_offload_t* offl = nullptr;
+    ZERO_OK_OR_FAIL(zero_offload_create(plan, &hp, gdt, pdt, h_master.data(), h_m.data(),
+                                        h_v.data(), 3, &offl));
+    ZERO_OK_OR_FAIL(zero_offload_timeline_start(offl, 4096));
+
+    std::vector<std::vector<unsigned char>> gbytes(n);
+    std::vector<const void*> gptr(n);
+    std::vector<unsigned char> o_flat(esize * S);
+    std::vector<uint16_t> seen(P);
+    std::vector<float> vals;
+    for (int it = 1; it <= steps; ++it) {
+        ZERO_OK_OR_FAIL(zero_offload_wait_params(offl, lag, s));
+        HIP_OK(hipMemcpyAsync(seen.data(), d_param, 2 * P, hipMemcpyDeviceToHost, s));
+        HIP_OK(hipStreamSynchronize(s));
+        const std::vector<uint16_t>& want = hist[it - 1 - lag > 0 ? it - 1 - lag : 0];
+        if (std::memcmp(seen.data(), want.data(), 2 * P) != 0) {
+            std::printf("offload lag %d it %d: the forward saw other parameters\n", lag, it);
+            return 1;
+        }
+        double dev_scale = 0;
+        zero_scaler_t dsc;
+        ZERO_OK_OR_FAIL(zero_state_download(plan, nullptr, &dsc, nullptr, nullptr, s));
+        dev_scale = dsc.scale;
+        if (dev_scale != o_scale) {
+            std::printf("offload lag %d it %d: device scale %g, oracle %g\n", lag, it, dev_scale,
+                        o_scale);
+            return 1;
+        }
+        for (int i = 0; i < n; ++i) {
+            vals.assign(numels[i], 0.0f);
+            synth_fill_f32(vals.data(), numels[i], synth_key(0, 1, it), off[i], 1e-2f,
+                           static_cast<float>(o_scale), 0, 1.0f);
+            gbytes[i].resize(esize * numels[i]);
+            for (int64_t k = 0; k < numels[i]; ++k) {
+                uint32_t w = grad_word(vals[k], gdt);
+                if (it == inject_step && i == st[0] && k == sto[0] + sn[0] / 2) {
+                    w = gdt == ZERO_F32 ? 0x7F800000u : gdt == ZERO_F16 ? 0x7C00u : 0x7F80u;
+                }
+                std::memcpy(&gbytes[i][esize * k], &w, esize);  // little endian: low half first
+            }
+            gptr[i] = gbytes[i].data();
+            HIP_OK(hipMemcpyAsync(d_grads[i], gbytes[i].data(), esize * numels[i],
+                                  hipMemcpyHostToDevice, s));
+        }
+        std::vector<const void*> dg(d_grads.begin(), d_grads.end());
+        ZERO_OK_OR_FAIL(zero_flatten_grads(plan, -1, dg.data(), gdt, d_flat, s));
+        ZERO_OK_OR_FAIL(zero_offload_submit(offl, d_flat, d_param, 0, P, s));
+        HIP_OK(hipStreamSynchronize(s));  // the host gradient copies are read below
+        // oracle
+        if (esize == 4) {
+            oracle_flatten_f32(reinterpret_cast<const uint32_t* const*>(gptr.data()), st.data(),
+                               sto.data(), sso.data(), sn.data(), nseg, S, real,
+                               reinterpret_cast<uint32_t*>(o_flat.data()));
+        } else {
+            oracle_flatten(reinterpret_cast<const uint16_t* const*>(gptr.data()), st.data(),
+                           sto.data(), sso.data(), sn.data(), nseg, S, real,
+                           reinterpret_cast<uint16_t*>(o_flat.data()));
+        }
+        const int o_flag = oracle_adam_step(S, o_t + 1, o_scale, o_flat.data(), gdt,
+                                            o_master.data(), o_m.data(), o_v.data(), hp.lr,
+                                            hp.beta1, hp.beta2, hp.eps, hp.weight_decay, 1);
+        if (!o_flag) {
+            ++o_t;
+            oracle_write_param(o_master.data(), real, begin, 0, o_param.data(), pdt);
+        } else {
+            ++skipped;
+        }
+        oracle_update_scale(&o_scale, &o_good, o_flag, dynamic, 1.0, 0.5, 2.0, 2);
+        hist.push_back(o_param);
+    }
+    ZERO_OK_OR_FAIL(zero_offload_drain(offl, s));
+    zero_offload_stats_t stats;
+    ZERO_OK_OR_FAIL(zero_offload_stats(offl, &stats));
+    if (stats.applied != o_t || stats.skipped != skipped || stats.processed != steps) {
+        std::printf("offload lag %d: stats applied %lld skipped %lld\n", lag,
+                    static_cast<long long>(stats.applied), static_cast<long long>(stats.skipped));
+        return 1;
+    }
+    if (std::memcmp(h_master.data(), o_master.data(), 4 * S) != 0 ||
+        std::memcmp(h_m.data(), o_m.data(), 4 * S) != 0 ||
+        std::memcmp(h_v.data(), o_v.data(), 4 * S) != 0) {
+        std::printf("offload lag %d: host state differs from the oracle\n", lag);
+        return 1;
+    }
+    HIP_OK(hipMemcpy(seen.data(), d_param, 2 * P, hipMemcpyDeviceToHost));
+    if (std::memcmp(seen.data(), o_param.data(), 2 * P) != 0) {
+        std::printf("offload lag %d: final parameters differ\n", lag);
+        return 1;
+    }
+    // the timeline: per step, every gradient piece; per applied step, each
+    // piece's update after its gradient copy and its parameter copy after it
+    const int64_t n_iv = zero_offload_timeline(offl, nullptr, 0);
+    ZERO_OK_OR_FAIL(static_cast<int>(n_iv < 0 ? n_iv : 0));
+    std::vector<zero_offload_interval_t> iv(n_iv > 0 ? n_iv : 1);
+    const int64_t got = zero_offload_timeline(offl, iv.data(), n_iv);
+    if (got != n_iv || n_iv < 3 * (steps - skipped)) {
+        std::printf("offload lag %d: %lld timeline intervals\n", lag, static_cast<long long>(n_iv));
+        return 1;
+    }
+    for (int64_t a = 0; a < n_iv; ++a) {
+        if (iv[a].end_ms < iv[a].start_ms - 0.05) {
+            std::printf("offload lag %d: an interval ends before it starts\n", lag);
+            return 1;
+        }
+        for (int64_t b = 0; b < n_iv; ++b) {
+            if (iv[b].step != iv[a].step || iv[b].piece != iv[a].piece) continue;
+            if (iv[a].kind == 1 && iv[b].kind == 0 && iv[a].start_ms < iv[b].end_ms - 0.05) {
+                std::printf("offload lag %d: an update started before its gradient arrived\n", lag);
+                return 1;
+            }
+            if (iv[a].kind == 2 && iv[b].kind == 1 && iv[a].start_ms < iv[b].end_ms - 0.05) {
+                std::printf("offload lag %d: parameters went back before their update\n", lag);
+                return 1;
+            }
+        }
+    }
+    zero_offload_destroy(offl);
+    for (void* p : d_grads) HIP_OK(hipFree(p));
+    HIP_OK(hipFree(d_flat));
+    HIP_OK(hipFree(d_param));
+    HIP_OK(hipStreamDestroy(s));
+    zero_plan_destroy(plan);
+    std::printf("offload gdt=%d pdt=%d lag %d: %d steps, %lld applied, %lld timeline intervals\n",
+                gdt, pdt, lag, steps, static_cast<long long>(o_t), static_cast<long long>(n_iv));
+    return 0;
+}
+
 // zero_adam_scalars: the device's scalars equal the host's, bit for bit.
 int scalars_case() {
     const int64_t n = 4096;
@@ -300,6 +477,9 @@ int main() {
     if (run_case(ZERO_F16, ZERO_F16, 1, 1) != 0) return 1;
     if (run_case(ZERO_F32, ZERO_F16, 1, 1) != 0) return 1;
     if (scalars_case() != 0) return 1;
+    if (offload_case(ZERO_F16, ZERO_F16, 1) != 0) return 1;
+    if (offload_case(ZERO_BF16, ZERO_BF16, 0) != 0) return 1;
+    if (offload_case(ZERO_F32, ZERO_F16, 1) != 0) return 1;
     std::printf("c-abi ok\n");
     return 0;
 }

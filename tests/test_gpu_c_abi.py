@@ -2,8 +2,9 @@
 built by __graft_entry__.build()) runs five cases through include/zero_mi355x.h
 -- three through zero_adam_step, two through zero_adam_step_noalloc -- and
 compares every step with the C oracle bit for bit, then compares the update
-scalars zero_adam_scalars forms on the device with the host's (see its
-header)."""
+scalars zero_adam_scalars forms on the device with the host's, then runs the
+ZeRO-Offload pipeline three times (lag 1 and 0; fp16, bf16 and fp32
+gradients) through its calls alone, timeline included (see its header)."""
 import os
 import subprocess
 
