@@ -657,7 +657,7 @@ def main(argv=None):
 def _main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama2_70b")
     ap.add_argument("--grad-dtype", choices=["f16", "bf16", "f32"], default=None,
