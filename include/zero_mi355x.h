@@ -469,8 +469,9 @@ typedef struct {
  * update ([legal] offload list, DPU bullet: CPU work of one iteration
  * overlaps GPU work).  The copies are bracketed by timing events on their
  * own streams, the update by host clock readings; a reference event, polled
- * by the host until it completes, puts both on the host clock (to within
- * the polling interval, microseconds).  Costs four timing events per piece
+ * by the host until it completes, puts both on the host clock: its
+ * completion is bracketed by two polls, taken at the bracket's midpoint,
+ * and a bracket wider than 20 microseconds is retried with a new event.  Costs four timing events per piece
  * and 32 bytes of host memory per interval; off unless called.  Call with no step in flight (after zero_offload_drain, or
  * before the first submit); it drops what an earlier start recorded.
  * Errors: ZERO_ENULL, ZERO_EINVAL (capacity), ZERO_ESTATE (steps in

@@ -723,13 +723,33 @@ int zero_offload_timeline_start(zero_offload_t* o, int64_t capacity) {
         }
         if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
     }
-    // the transfer stream idle, then a reference event the host sees complete
+    // The GPU clock tied to the host's: a reference event on the idle transfer
+    // stream, polled by the host.  It completed after the last poll that
+    // found it pending began (or after it was recorded) and before the first
+    // poll that found it done returned; the midpoint of that window is its
+    // host time.  A window over kRefWindowMs (the thread was descheduled, say)
+    // is retried with a new reference event, up to kRefTries times.
+    constexpr double kRefWindowMs = 0.02;
+    constexpr int kRefTries = 64;
     if ((e = hipStreamSynchronize(o->xfer)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    if ((e = hipEventRecord(o->tl_ref, o->xfer)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    while ((e = hipEventQuery(o->tl_ref)) == hipErrorNotReady) {
+    Clock::time_point t0{};
+    for (int attempt = 0; attempt < kRefTries; ++attempt) {
+        auto lo = Clock::now();
+        if ((e = hipEventRecord(o->tl_ref, o->xfer)) != hipSuccess) {
+            return hip_fail(e, "hipEventRecord");
+        }
+        Clock::time_point hi{};
+        for (;;) {
+            const auto a = Clock::now();
+            e = hipEventQuery(o->tl_ref);
+            hi = Clock::now();
+            if (e != hipErrorNotReady) break;
+            lo = a;
+        }
+        if (e != hipSuccess) return hip_fail(e, "hipEventQuery");
+        t0 = lo + (hi - lo) / 2;
+        if (std::chrono::duration<double, std::milli>(hi - lo).count() <= kRefWindowMs) break;
     }
-    const auto t0 = Clock::now();
-    if (e != hipSuccess) return hip_fail(e, "hipEventQuery");
     std::lock_guard<std::mutex> g(o->mu);
     o->tl.clear();
     try {
