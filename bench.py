@@ -213,6 +213,35 @@ def run_graph(bufs, steps, warmup, device):
     return wall, sum(dev_ms[1:]) / len(dev_ms[1:])
 
 
+def time_bucketed_flatten(bufs, reps=5):
+    """The flatten as a training loop overlapping backward would call it:
+    one call per bucket of the shard, in bucket order (the reverse of
+    registration order), bracketed as a whole by HIP events on the stream
+    the calls are enqueued on.  Returns the call count and the median time
+    of the whole sequence."""
+    import statistics
+
+    import torch
+
+    import zero_partitioned_mixed_plan_amd as z
+
+    plan, master, m, v, flat, param, grads, hp, scaler = bufs
+    buckets = sorted({s.bucket for s in plan.segments()})
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for r in range(reps + 1):
+        e0.record()
+        for b in buckets:
+            z.zero_flatten_grads(plan, b, grads, flat)
+        e1.record()
+        e1.synchronize()
+        if r:
+            times.append(e0.elapsed_time(e1))
+    # the bookkeeping now says every bucket was flattened into `flat`, as the
+    # one-call flatten leaves it
+    return len(buckets), statistics.median(times)
+
+
 def time_standalone_kernels(bufs):
     """One launch each of the kernels the default step does not run: the
     standalone parameter cast (6 B/element) and the overflow scan of a flat
@@ -738,6 +767,7 @@ def _main(argv=None):
     if step_log is not None:
         step_log.close()
     write_ms, scan_ms = time_standalone_kernels(bufs)
+    n_buckets, bflat_ms = time_bucketed_flatten(bufs)
     graph_wall, devsc_ms = (None, None) if args.no_graph else run_graph(bufs, args.steps,
                                                                         args.warmup, device)
     S, real, begin = plan.S, plan.real, plan.begin
@@ -778,6 +808,10 @@ def _main(argv=None):
                         "min_ms": min(times["flatten"]),
                         "bytes_per_elem": fb, "gbps": flat_gbs,
                         "traffic": counted_traffic(w.name, w.grad_dtype, "flatten")},
+            "flatten_by_bucket": {"calls": n_buckets, "ms": bflat_ms, "bytes_per_elem": fb,
+                                  "gbps": fb * S / (bflat_ms * 1e-3) / 1e9,
+                                  "what": "one zero_flatten_grads call per bucket of the shard, "
+                                          "timed as a whole"},
             "write_param": {"ms": write_ms, "bytes_per_elem": 6,
                             "gbps": 6 * real / (write_ms * 1e-3) / 1e9},
             "scan": {"ms": scan_ms, "bytes_per_elem": GRAD_BYTES[w.grad_dtype],

@@ -43,3 +43,5 @@ def test_bench_prints_one_complete_json_line():
     assert cb["value"] > 0 and isinstance(cb["sample"], str)
     assert cb["all_cores"]["cores"] >= 1 and cb["all_cores"]["value"] > 0
     assert d["graph_replay"]["ms_per_step"] > 0
+    fb = d["kernels"]["flatten_by_bucket"]
+    assert fb["calls"] >= 1 and fb["ms"] > 0 and fb["bytes_per_elem"] == 4
