@@ -229,6 +229,7 @@ def time_bucketed_flatten(bufs, reps=5):
     buckets = sorted({s.bucket for s in plan.segments()})
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     times = []
+    plan.set_timing(False)  # no per-call timing events: two of them cost ~7 us a call
     for r in range(reps + 1):
         e0.record()
         for b in buckets:
@@ -237,6 +238,7 @@ def time_bucketed_flatten(bufs, reps=5):
         e1.synchronize()
         if r:
             times.append(e0.elapsed_time(e1))
+    plan.set_timing(True)
     # the bookkeeping now says every bucket was flattened into `flat`, as the
     # one-call flatten leaves it
     return len(buckets), statistics.median(times)
