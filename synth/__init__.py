@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs shared by the CPU checker and the GPU path.
+"""Seeded synthetic inputs shared by the CPU oracle and the GPU path.
 
 Only random numbers and workload shapes live here: no partitioning, flatten,
 overflow test, optimizer arithmetic or half-precision rounding of the

@@ -3,7 +3,7 @@
  *
  * This module only draws numbers; it holds none of the optimizer's
  * arithmetic (no partitioning, no flatten, no overflow test, no Adam, no
- * half-precision cast).  Both the CPU checker and the GPU path take their
+ * half-precision cast).  Both the CPU oracle and the GPU path take their
  * inputs from it; a device twin (synth_dev.hip) implements the same
  * definition and is checked against this file bit for bit.
  *

@@ -15,7 +15,7 @@ pinned buffers, chunk by chunk, and the oracle runs over the same chunks on
 host threads (the step is elementwise once the overflow decision, taken over
 the whole shard first, is known).
 
-Sampled windows (the _run_sampled runs): the Llama-2-70B step on any box with
+Sampled windows (the _run_sampled runs): the Llama-2-70B step on any machine with
 its device memory (and its graph-replayed step where the host cannot hold the
 whole oracle state), the standalone cast and scan at that size, and the
 offload pipeline on Llama-3-8B.  The oracle recomputes fixed windows of the
@@ -330,7 +330,7 @@ def _run_sampled(case, flatten_mode="all", label="", step_mode="sync"):
 
 
 def _whole_70b_fits():
-    """Whether this box holds the oracle's whole 70B-class shard (~121 GB of
+    """Whether this host holds the oracle's whole 70B-class shard (~121 GB of
     host memory) beside the device state (~160 GB)."""
     import torch
     free, _ = torch.cuda.mem_get_info()
@@ -370,7 +370,7 @@ def test_dna_20b_rank2_graph_replayed_step_with_device_scaler():
 
 
 def test_llama2_70b_rank7_full_shard():
-    # sampled windows: runs on any box with the device memory
+    # sampled windows: runs on any machine with the device memory
     import torch
     free, _ = torch.cuda.mem_get_info()
     if free < 170e9:

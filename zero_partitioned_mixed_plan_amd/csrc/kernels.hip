@@ -18,7 +18,7 @@
 //     256 consecutive elements.  On a 70B-class shard (8.6e9 elements) the
 //     best shape was 128 threads with two elements each, t and t + 128,
 //     both loaded before the math: 37.1 ms vs 38.2 ms for 256 threads x 1
-//     element, 37.6 ms for 256 x 4 and 38.1 ms for 64 x 2 (same box, same
+//     element, 37.6 ms for 256 x 4 and 38.1 ms for 64 x 2 (same machine, same
 //     run).  Below 7.5e9 elements, and for fp32 gradients at any size,
 //     256 x 1 is faster (see adam_dispatch_d).
 //   * non-temporal loads and stores (the streaming cache policy) on the
@@ -507,7 +507,7 @@ void adam_launch(const AdamScalars* dsc, dim3 grid, hipStream_t s, const void* g
     }
 }
 
-// Shape by shard size (same box, same buffers, HIP events; bf16 update,
+// Shape by shard size (same machine, same buffers, HIP events; bf16 update,
 // fp32 state): 256 x 1 ran 2-5% faster than 128 x 2 from 1e9 to 4e9
 // elements and matched it at 7e9, but 1.3-1.5% slower at 8.6e9.  The
 // 128 x 2 shape was also 3-4% slower at 1e9 and 2.5e9 when the arrays were
