@@ -45,3 +45,36 @@ def test_bench_prints_one_complete_json_line():
     assert d["graph_replay"]["ms_per_step"] > 0
     fb = d["kernels"]["flatten_by_bucket"]
     assert fb["calls"] >= 1 and fb["ms"] > 0 and fb["bytes_per_elem"] == 4
+
+
+def _bench(*args, timeout=300):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True, timeout=timeout)
+    assert r.returncode == 0, r.stderr[-3000:]
+    return r.stdout
+
+
+def test_placement_probe_reports_every_trial():
+    out = _bench("--workload", "gpt2_small", "--placement-probe", "0,1")
+    trials = [ln for ln in out.splitlines() if ln.startswith("[placement]")]
+    assert len(trials) == 4, out[-2000:]           # 2 ballasts x 2 layouts
+    d = json.loads(out.strip().splitlines()[-1])
+    assert d["placement_probe_elems"] == 15_555_008 and d["ballasts_gb"] == [0.0, 1.0]
+    for layout in ("separate", "one"):
+        s = d["layouts"][layout]
+        assert 0 < s["min_ms"] <= s["median_ms"] <= s["max_ms"] and s["spread_pct"] >= 0
+
+
+def test_offload_timeline_is_summarised_and_written(tmp_path):
+    path = tmp_path / "timeline.json"
+    out = _bench("--mode", "offload", "--workload", "gpt2_small", "--steps", "4", "--warmup", "1",
+                 "--no-cpu-baseline", "--timeline", str(path))
+    d = json.loads(out.strip().splitlines()[-1])
+    tl = json.load(open(path))
+    for lag in ("lag1", "lag0"):
+        s = d["offload"][lag]["timeline"]
+        assert s["pieces"] >= 1 and s["steps"] >= 1
+        assert s["gradient_copy_ms"] > 0 and s["host_update_ms"] > 0 and s["parameter_copy_ms"] > 0
+        assert 0 <= s["copies_during_update_ms"] <= s["gradient_copy_ms"] + s["parameter_copy_ms"]
+        kinds = {r["kind"] for r in tl[lag]}
+        assert kinds == {"gradient copy", "host update", "parameter copy"}
