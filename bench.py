@@ -219,7 +219,6 @@ def time_bucketed_flatten(bufs, reps=5):
     registration order), bracketed as a whole by HIP events on the stream
     the calls are enqueued on.  Returns the call count and the median time
     of the whole sequence."""
-    import statistics
 
     import torch
 
@@ -323,7 +322,6 @@ def timeline_summary(tl):
     copying (gradients to the host, parameters back), updating on the host,
     and how much of the copying ran while the host update of the same step
     ran; medians over the steps after the first."""
-    import statistics
     steps = sorted({r["step"] for r in tl})
     rows = []
     for j in steps:
@@ -374,6 +372,10 @@ def run_offload(w, steps, warmup, device, n_threads, forward_ms=0.0, timeline_fi
                                   "for the forward and backward passes",
                           "gemms_per_step": k, "ms_alone": measured}
     timelines = {}
+    # the host's own streaming rate, taken before and after the timed lags
+    # (host rates drift within a run); past the caches at every shard size
+    ceiling_bytes = min(max(14 * S, 1 << 30), 4 << 30)
+    before = host_stream_ceiling(ceiling_bytes, n_threads)
     for lag in (1, 0):
         m = np.zeros(S, np.float32)
         v = np.zeros(S, np.float32)
@@ -428,7 +430,52 @@ def run_offload(w, steps, warmup, device, n_threads, forward_ms=0.0, timeline_fi
     if timeline_file:
         with open(timeline_file, "w") as f:
             json.dump({"workload": w.name, "forward_ms": forward_ms, **timelines}, f)
+    after = host_stream_ceiling(ceiling_bytes, n_threads)
+    best = max(before["gbps"], after["gbps"])
+    out["host_ceiling"] = {"what": before["what"], "bytes": before["bytes"],
+                           "threads": n_threads, "gbps_before": before["gbps"],
+                           "gbps_after": after["gbps"], "gbps": best}
+    for lag in (1, 0):
+        out[f"lag{lag}"]["host_update_frac"] = out[f"lag{lag}"]["host_update_gbps"] / best
     return plan, out
+
+
+def host_stream_ceiling(nbytes, n_threads, reps=7):
+    """The host DRAM rate that the host update's traffic can reach on the same
+    threads. The update reads 14 and writes 14 bytes per element, and every
+    state line it reads it writes back. An in-place fp32 scale has the same
+    mix: each line is read once and written back once, with no read for
+    ownership. nbytes of memory are split into n_threads contiguous chunks,
+    which are first touched and then scaled by the threads at once (numpy's
+    ufunc loops release the GIL). A pass moves 2 * nbytes. Returns the median
+    rate over reps passes, after one untimed pass."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    n = nbytes // 4 // n_threads * n_threads
+    a = np.empty(n, np.float32)
+    chunks = np.split(a, n_threads)
+    one = np.float32(1.0)
+
+    def touch(c):
+        np.copyto(c, one)
+
+    def scale(c):
+        np.multiply(c, one, out=c)
+
+    times = []
+    with ThreadPoolExecutor(n_threads) as ex:
+        list(ex.map(touch, chunks))
+        for _ in range(reps + 1):
+            t0 = time.perf_counter()
+            list(ex.map(scale, chunks))
+            times.append(time.perf_counter() - t0)
+    assert a[0] == 1.0 and a[-1] == 1.0
+    med = statistics.median(times[1:])
+    return {"what": f"in-place fp32 scale of {n * 4} bytes on {n_threads} threads (each line "
+                    f"read once and written once), median of {reps} passes",
+            "bytes": n * 4, "ms": med * 1e3, "gbps": 2 * n * 4 / med / 1e9}
 
 
 def host_info():
@@ -626,7 +673,6 @@ def placement_probe(S, ballasts_gb, device, reps=10):
     between trials, so even a repeated virtual address gets its physical
     pages afresh.  Prints one line per trial and a JSON summary."""
     import ctypes
-    import statistics
 
     import torch
 

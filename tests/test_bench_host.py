@@ -2,7 +2,8 @@
 it prices the kernels at, the kernel-source digest that gates the counted
 HBM traffic, the pricing of raw memory-request counts, and that the
 committed counter summaries were taken with the kernel source as it stands
-(so a GPU run reports `traffic` rather than null)."""
+(so a GPU run reports `traffic` rather than null), the offload timeline's
+summary, and the host streaming rate the host update is priced against."""
 import os
 import re
 import subprocess
@@ -96,3 +97,12 @@ def test_timeline_summary_by_hand():
                  "copies_during_update_ms": 3.0, "span_ms": 9.0, "pieces": 2, "steps": 1}
     assert bench._overlap([(0, 3), (5, 9)], [(2, 6), (8, 10)]) == 1 + 1 + 1
     assert bench._length([(0, 2), (1, 3), (5, 6)]) == 4
+
+
+def test_host_stream_ceiling_counts_a_read_and_a_write_per_byte():
+    nbytes = (32 << 20) + 12
+    r = bench.host_stream_ceiling(nbytes, 3, reps=2)
+    assert r["bytes"] == nbytes // 4 // 3 * 3 * 4 == 33_554_436   # whole floats, split evenly
+    assert r["ms"] > 0
+    assert abs(r["gbps"] - 2 * r["bytes"] / (r["ms"] * 1e-3) / 1e9) < 1e-9 * r["gbps"]
+    assert "3 threads" in r["what"] and "2 passes" in r["what"]

@@ -78,3 +78,9 @@ def test_offload_timeline_is_summarised_and_written(tmp_path):
         assert 0 <= s["copies_during_update_ms"] <= s["gradient_copy_ms"] + s["parameter_copy_ms"]
         kinds = {r["kind"] for r in tl[lag]}
         assert kinds == {"gradient copy", "host update", "parameter copy"}
+        hu = d["offload"][lag]
+        assert hu["host_update_gbps"] > 0
+        assert abs(hu["host_update_frac"] - hu["host_update_gbps"] / d["offload"]["host_ceiling"]["gbps"]) < 1e-12
+    hc = d["offload"]["host_ceiling"]
+    assert hc["bytes"] >= 1 << 29 and hc["threads"] == d["offload"]["host_threads"]
+    assert hc["gbps"] == max(hc["gbps_before"], hc["gbps_after"]) > 0
