@@ -277,3 +277,60 @@ def test_host_step_in_a_forked_child():
     assert proc.exitcode == 0
     for a, b in zip(got, want):
         assert np.array_equal(a, b)
+
+
+_NO_THREADS_CHILD = r"""
+import json, mmap, re, resource, sys
+import numpy as np
+sys.path.insert(0, sys.argv[1])
+import zero_partitioned_mixed_plan_amd as z
+
+n = 70001
+plan = z.zero_partition_plan([n], 1, 0, 64)
+S = plan.S
+rng = np.random.default_rng(5)
+g = (rng.normal(0, 1e-2, S).astype(np.float32)).astype(np.float16).view(np.uint16)
+m0 = rng.normal(0, 0.02, S).astype(np.float32)
+hp = z.AdamHParams(weight_decay=0.05, adamw=True)
+bufs = {}
+for name, threads in (("want", 1), ("got", 16)):
+    bufs[name] = [m0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
+                  np.zeros(S, np.uint16)]
+rc1 = z.zero_cpu_adam_step(plan, hp, 1, 1.0, g, *bufs["want"], 0, grad_dtype="f16",
+                           param_dtype="bf16", overflow=0, n_threads=1)
+# leave less address space than 16 thread stacks need
+vm = int(re.search(r"VmSize:\s+(\d+) kB", open("/proc/self/status").read()).group(1)) << 10
+soft, hard = resource.getrlimit(resource.RLIMIT_AS)
+resource.setrlimit(resource.RLIMIT_AS, (vm + (40 << 20), hard))
+try:
+    mmap.mmap(-1, 16 * resource.getrlimit(resource.RLIMIT_STACK)[0])
+    bites = False
+except OSError:
+    bites = True
+rc16 = z.zero_cpu_adam_step(plan, hp, 1, 1.0, g, *bufs["got"], 0, grad_dtype="f16",
+                            param_dtype="bf16", overflow=-1, n_threads=16)
+resource.setrlimit(resource.RLIMIT_AS, (soft, hard))
+same = all(np.array_equal(a, b) for a, b in zip(bufs["want"], bufs["got"]))
+print(json.dumps({"rc1": rc1, "rc16": rc16, "bites": bites, "same": same}))
+"""
+
+
+def test_host_step_when_threads_cannot_be_started():
+    # Thread creation can fail (here: too little address space left for
+    # the threads' stacks).  The call must neither abort the process nor
+    # fail: the calling thread takes the ranges that got no thread, and the
+    # result is the one-thread result.
+    import json
+    import resource
+    import subprocess
+    import sys
+    if resource.getrlimit(resource.RLIMIT_STACK)[0] in (resource.RLIM_INFINITY, 0):
+        pytest.skip("thread stacks are not sized by RLIMIT_STACK here")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, ZERO_CPU_ISA="scalar")
+    r = subprocess.run([sys.executable, "-c", _NO_THREADS_CHILD, root], capture_output=True,
+                       text=True, timeout=120, env=env)
+    assert r.returncode == 0, (r.returncode, r.stderr[-2000:])
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    assert d["bites"], "the address-space limit left room for 16 thread stacks"
+    assert d == {"rc1": 0, "rc16": 0, "bites": True, "same": True}

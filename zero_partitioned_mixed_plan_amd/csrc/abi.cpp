@@ -268,8 +268,14 @@ int run_host_step(const CpuAdamArgs& a, int32_t overflow, int n_threads) {
             g_host_pool = nullptr;
         }
         if (g_host_pool == nullptr) {
-            g_host_pool = new HostPool(n_threads);
-            g_host_pool_pid = getpid();
+            try {
+                g_host_pool = new HostPool(n_threads);
+                g_host_pool_pid = getpid();
+            } catch (const std::exception&) {
+                // its threads could not all be started: this call starts
+                // what it can itself (parallel_ranges), and a later call
+                // tries to build the pool again
+            }
         }
         pool = g_host_pool;
     }

@@ -28,6 +28,7 @@
 #include <chrono>
 #include <cstdlib>
 #include <cstring>
+#include <exception>
 #include <string>
 #include <thread>
 #include <vector>
@@ -432,7 +433,8 @@ int64_t range_chunk(int64_t n, int n_threads) {
 
 // Runs fn over [0, n) split into n_threads contiguous ranges; the calling
 // thread takes the first.  With a pool its threads run the others, else
-// threads are started for this call.
+// threads are started for this call, and the calling thread also runs the
+// ranges of any that could not be started.
 template <typename Fn>
 void parallel_ranges(int64_t n, int n_threads, HostPool* pool, Fn fn) {
     if (pool != nullptr) n_threads = pool->size();
@@ -446,13 +448,20 @@ void parallel_ranges(int64_t n, int n_threads, HostPool* pool, Fn fn) {
         return;
     }
     std::vector<std::thread> threads;
-    for (int t = 1; t < n_threads; ++t) {
-        const int64_t lo = t * chunk;
-        if (lo >= n) break;
-        const int64_t hi = std::min(n, lo + chunk);
-        threads.emplace_back([=] { fn(lo, hi); });
+    int t = 1;
+    try {
+        threads.reserve(static_cast<size_t>(n_threads - 1));
+        for (; t < n_threads && t * chunk < n; ++t) {
+            const int64_t lo = t * chunk;
+            const int64_t hi = std::min(n, lo + chunk);
+            threads.emplace_back([=] { fn(lo, hi); });
+        }
+    } catch (const std::exception&) {
+        // no thread could be started (std::system_error) or no memory for
+        // one: the ranges from t on have none, and this thread takes them
     }
     fn(0, std::min(n, chunk));
+    for (; t < n_threads && t * chunk < n; ++t) fn(t * chunk, std::min(n, t * chunk + chunk));
     for (auto& th : threads) th.join();
 }
 
