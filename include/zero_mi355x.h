@@ -480,8 +480,9 @@ int zero_offload_timeline_start(zero_offload_t* off, int64_t capacity);
 
 /* Copies up to `cap` recorded intervals into `out` (host memory; may be
  * NULL when cap is 0), in the order they were completed, and returns how
- * many are stored (at most the capacity given to zero_offload_timeline_start;
- * later intervals are dropped) or a negative error.  Call after
+ * many are stored (at most the capacity given to zero_offload_timeline_start,
+ * fewer if host memory ran out while recording; later intervals are
+ * dropped) or a negative error.  Call after
  * zero_offload_drain so that the last steps' parameter copies are included.
  * Errors: ZERO_ENULL, ZERO_EINVAL (cap < 0), ZERO_ESTATE (no timeline
  * started, or another device current). */

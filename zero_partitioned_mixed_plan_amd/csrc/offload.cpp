@@ -157,7 +157,13 @@ void tl_push(zero_offload* o, int64_t step, int piece, int kind, double t0, doub
     r.kind = kind;
     r.start_ms = t0;
     r.end_ms = t1;
-    o->tl.push_back(r);
+    try {
+        o->tl.push_back(r);
+    } catch (const std::bad_alloc&) {
+        // the worker thread must not throw: out of host memory, the
+        // timeline keeps what it holds and records nothing more
+        o->tl_cap = static_cast<int64_t>(o->tl.size());
+    }
 }
 
 // Start and end of an event pair on the host clock; false if not complete.
