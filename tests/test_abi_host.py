@@ -1,8 +1,9 @@
 """Host-side checks of libzero_mi355x (CPU only, no device compute).
 
 * the library loads and exports every function include/*.h declares;
-* its planner agrees with the oracle's on every rank of every workload and
-  on random small models (sizes, segments, buckets, byte accounting);
+* its planner agrees with the oracle's on every rank of every workload, on
+  random small models, and on generated ones with tensors of up to 2^40
+  elements (sizes, segments, buckets, byte accounting);
 * its loss-scale policy agrees with the oracle's on random sequences;
 * argument errors are reported before any device work.
 """
@@ -14,6 +15,8 @@ import re
 
 import numpy as np
 import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 import oracle
 import zero_partitioned_mixed_plan_amd as z
@@ -78,6 +81,16 @@ def test_planner_matches_oracle_random(seed):
     B = rng.choice([1, 50, 1000, 1 << 25])
     for r in range(R):
         _compare(numels, R, r, A, B)
+
+
+@settings(max_examples=400, deadline=None, derandomize=True, database=None)
+@given(numels=st.lists(st.one_of(st.integers(0, 70), st.integers(0, 1 << 40)), max_size=24),
+       R=st.integers(1, 64), A=st.sampled_from([1, 2, 3, 8, 64, 128, 4096]),
+       B=st.one_of(st.integers(1, 100), st.integers(1, 1 << 42)), data=st.data())
+def test_planner_matches_oracle_at_any_size(numels, R, A, B, data):
+    # sizes up to 2^40 elements a tensor and 64 ranks: the int64 offsets,
+    # padding and bucket sums far beyond the workloads
+    _compare(numels, R, data.draw(st.integers(0, R - 1)), A, B)
 
 
 @pytest.mark.parametrize("seed", range(20))
