@@ -514,7 +514,7 @@ void adam_launch(const AdamScalars* dsc, dim3 grid, hipStream_t s, const void* g
 // the process's first allocations than after 100 GB of other buffers, which
 // did not move 256 x 1.  With gradients kept in fp32 (30 B per element)
 // 256 x 1 stays ahead at 8.6e9 too: 40.8 against 42.6 ms, alternating the
-// two over six rounds.
+// two over six repetitions.
 template <int GDT, int PDT, bool ADAMW>
 hipError_t adam_dispatch_d(const AdamScalars* dsc, dim3 grid, hipStream_t s, const void* g,
                            float* master, float* m, float* v, uint16_t* param, int64_t S,
