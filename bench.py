@@ -751,9 +751,8 @@ def _main(argv=None):
                     help="device: the whole step on the GPU (default); offload: ZeRO-Offload "
                          "(host-resident state, host update, one-step delayed update)")
     ap.add_argument("--host-threads", type=int, default=None,
-                    help="threads of the offload host update (default: the usable CPUs "
-                         "less one, which the caller and the HIP runtime need while the "
-                         "delayed update runs)")
+                    help="threads of the offload host update (default: every usable CPU; "
+                         "the pipeline's caller thread mostly waits)")
     ap.add_argument("--forward-ms", type=float, default=0.0,
                     help="offload mode: run about this many ms of bf16 products on the GPU "
                          "before each step, a stand-in for the forward and backward passes "
@@ -797,7 +796,7 @@ def _main(argv=None):
         placement_probe(S, [float(x) for x in args.placement_probe.split(",")], device)
         return 0
     if args.mode == "offload":
-        threads = args.host_threads or max(1, host_info()["usable_cpus"] - 1)
+        threads = args.host_threads or host_info()["usable_cpus"]
         plan, res = run_offload(w, args.steps, args.warmup, device, threads, args.forward_ms,
                                 args.timeline)
         print(json.dumps({

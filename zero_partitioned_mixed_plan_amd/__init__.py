@@ -34,6 +34,7 @@ and ZeRO-Offload's host-side update (host buffers: numpy arrays or CPU tensors):
                        exp_avg_sq, param=None, param_base=0, grad_dtype=None,
                        param_dtype=None, overflow=-1, n_threads=None) -> 0 | 1
     zero_cpu_isa() -> "avx512" | "avx2" | "scalar"
+    default_host_threads() -> n (n_threads=None: the CPUs of the affinity mask, at most 16)
     zero_adam_scalars(hparams, t_first, count, loss_scale, out=None) -> [count, 10]
                                 (the update's fp32 scalars, formed on the host or
                                  on the device as the asynchronous step does)
@@ -46,6 +47,7 @@ from __future__ import annotations
 
 import atexit
 import ctypes
+import os
 import sys
 import weakref
 from dataclasses import dataclass
@@ -60,7 +62,7 @@ __all__ = ["Plan", "release_all", "AdamHParams", "LossScaler", "DeviceStepState"
            "zero_update_loss_scale", "zero_write_param_shard", "zero_state_upload",
            "zero_adam_step_async", "zero_state_download", "zero_state_device_scale",
            "zero_adam_step_noalloc",
-           "zero_cpu_adam_step", "zero_cpu_isa", "zero_adam_scalars", "SCALAR_FIELDS",
+           "zero_cpu_adam_step", "zero_cpu_isa", "default_host_threads", "zero_adam_scalars", "SCALAR_FIELDS",
            "Offload", "zero_last_error", "ZERO_F16",
            "ZERO_BF16", "ZERO_F32"]
 
@@ -487,7 +489,6 @@ def zero_cpu_adam_step(plan: Plan, hparams: AdamHParams, step: int, loss_scale: 
                        n_threads: Optional[int] = None) -> int:
     """ZeRO-Offload's update on host buffers; returns 0 applied, 1 skipped.
     overflow: -1 tests flat_grad here, 0 / 1 pass a known flag."""
-    import os
     gcode = _grad_code(flat_grad, grad_dtype)
     g, _ = _host_buffer(flat_grad, "flat_grad", plan.S, 4 if gcode == ZERO_F32 else 2)
     ptrs = [_host_buffer(t, name, plan.S, 4)[0] for name, t in
@@ -497,12 +498,22 @@ def zero_cpu_adam_step(plan: Plan, hparams: AdamHParams, step: int, loss_scale: 
         pptr, pnum = _host_buffer(param, "param", 0, 2)
         pdt = _half_code(param, param_dtype)
     if n_threads is None:
-        n_threads = max(1, min(16, os.cpu_count() or 1))
+        n_threads = default_host_threads()
     hp = hparams.to_c()
     return check(lib.zero_cpu_adam_step(plan.handle, ctypes.byref(hp), int(step),
                                         float(loss_scale), g, gcode,
                                         *ptrs, pptr, int(param_base), pnum, pdt, int(overflow),
                                         int(n_threads)), "zero_cpu_adam_step")
+
+
+def default_host_threads() -> int:
+    """Threads the host update uses when none are given: the CPUs this
+    process may run on (its affinity mask), at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def zero_cpu_isa() -> str:
@@ -543,13 +554,12 @@ class Offload:
 
     def __init__(self, plan: Plan, hparams: AdamHParams, grad_dtype, param_dtype, master,
                  exp_avg, exp_avg_sq, n_threads: Optional[int] = None):
-        import os
         self.plan = plan
         self._keep = (master, exp_avg, exp_avg_sq)
         ptrs = [_host_buffer(t, name, plan.S, 4)[0] for name, t in
                 (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq))]
         if n_threads is None:
-            n_threads = max(1, min(16, os.cpu_count() or 1))
+            n_threads = default_host_threads()
         pdt = 0 if param_dtype is None else _HALF_CODES[param_dtype]
         hp = hparams.to_c()
         h = ctypes.c_void_p()
