@@ -243,19 +243,22 @@ def time_bucketed_flatten(bufs, reps=5):
     return len(buckets), statistics.median(times)
 
 
-def time_standalone_kernels(bufs):
-    """One launch each of the kernels the default step does not run: the
-    standalone parameter cast (6 B/element) and the overflow scan of a flat
-    shard that was not flattened this step (2 B/element; it runs inside a
-    zero_adam_step, whose update is timed separately)."""
+def time_standalone_kernels(bufs, reps=5):
+    """The kernels the default step does not run, median of `reps` launches
+    each: the standalone parameter cast (6 B/element) and the overflow scan
+    of a flat shard that was not flattened this step (2 B/element; it runs
+    inside a zero_adam_step, whose update is timed separately)."""
     import zero_partitioned_mixed_plan_amd as z
 
     plan, master, m, v, flat, param, grads, hp, scaler = bufs
-    z.zero_write_param_shard(plan, master, param, plan.begin)
-    write_ms = plan.kernel_ms(3)
-    z.zero_adam_step(plan, hp, 1, scaler.scale, flat, master, m, v, param, plan.begin)
-    scan_ms = plan.kernel_ms(1)
-    return write_ms, scan_ms
+    write_ms, scan_ms = [], []
+    for _ in range(reps):
+        z.zero_write_param_shard(plan, master, param, plan.begin)
+        write_ms.append(plan.kernel_ms(3))
+    for _ in range(reps):
+        z.zero_adam_step(plan, hp, 1, scaler.scale, flat, master, m, v, param, plan.begin)
+        scan_ms.append(plan.kernel_ms(1))
+    return statistics.median(write_ms), statistics.median(scan_ms)
 
 
 def forward_stand_in(forward_ms, device):

@@ -345,25 +345,32 @@ def test_wrong_device_and_bad_buffers_raise():
 @pytest.mark.parametrize("pdt", ["f16", "bf16"])
 def test_write_param_ragged_sizes_and_windows(pdt):
     """The standalone cast on shards whose real length leaves a partial
-    2048-element block (and tiny ones), written through parameter windows
-    at several bases; everything outside the shard's range stays untouched."""
+    2048-element block or a partial 4-element vector (and tiny ones),
+    written through parameter windows at several bases; everything outside
+    the shard's range stays untouched.  A 16-byte aligned master with an
+    8-byte aligned destination takes the vector kernel, any other alignment
+    (a window 2 or 6 bytes off, a master 4 bytes off) the element kernel."""
     import torch
     rng = np.random.default_rng(23)
-    for numels, R, r, A in [([1], 1, 0, 1), ([5], 1, 0, 1), ([2049], 1, 0, 1),
+    for numels, R, r, A in [([1], 1, 0, 1), ([5], 1, 0, 1), ([7], 1, 0, 1), ([2049], 1, 0, 1),
                             ([4095, 3], 2, 1, 1), ([2048 * 7 + 1, 2047], 3, 2, 8),
-                            ([100003, 65, 2048], 2, 0, 64), ([100003, 65, 2048], 2, 1, 64)]:
+                            ([100003, 65, 2048], 2, 0, 64), ([100003, 65, 2048], 2, 1, 64),
+                            ([4096 * 3 + 6], 1, 0, 1), ([2048 * 9 + 3, 1], 2, 1, 2)]:
         plan = z.zero_partition_plan(numels, R, r, A)
         P, S, real, begin = sum(numels), plan.S, plan.real, plan.begin
         master = rng.normal(0, 0.5, S).astype(np.float32)
-        for base in (0, begin, max(begin - 3, 0)):
-            numel = P - base
-            buf = torch.full((numel + 5,), 7.0, dtype=torch_dtype(pdt), device=DEV)
-            win = buf[:numel]
-            z.zero_write_param_shard(plan, torch.from_numpy(master).to(DEV), win, base)
-            got = _bits(buf)
-            want = _bits(torch.full((numel + 5,), 7.0, dtype=torch_dtype(pdt)))
-            oracle.write_param(master, real, begin, base, want, pdt)
-            assert np.array_equal(got, want), (numels, R, r, base)
+        for moff in (0, 1):
+            mbuf = torch.zeros(S + 4, device=DEV)
+            mbuf[moff:moff + S] = torch.from_numpy(master).to(DEV)
+            for base in (0, begin, max(begin - 3, 0)):
+                numel = P - base
+                buf = torch.full((numel + 5,), 7.0, dtype=torch_dtype(pdt), device=DEV)
+                win = buf[:numel]
+                z.zero_write_param_shard(plan, mbuf[moff:moff + S], win, base)
+                got = _bits(buf)
+                want = _bits(torch.full((numel + 5,), 7.0, dtype=torch_dtype(pdt)))
+                oracle.write_param(master, real, begin, base, want, pdt)
+                assert np.array_equal(got, want), (numels, R, r, base, moff)
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
