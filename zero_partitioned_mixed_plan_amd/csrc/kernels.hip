@@ -86,8 +86,9 @@ constexpr int lds_per_cu(int bytes) {
 // workgroups share a CU (the pad and its 512 bytes of ballot table take 10
 // units).  A pure copy stream moves the most bytes with a bounded number of
 // requests in flight per CU; 12 workgroups (about 48 KiB of loads in
-// flight) ran the flatten 2-6% faster than the 16 that fit otherwise, 11
-// about as fast, and 10 or fewer slower.
+// flight) ran the flatten up to 4% faster than the 16 that fit otherwise
+// (0.3-2% once each XCD took runs of tiles, below), 11 about as fast, and
+// 10 or fewer slower.
 constexpr int kFlatPerCu = 12;
 constexpr unsigned kFlatLdsPad = 11776;
 static_assert(lds_per_cu(kFlatLdsPad + 512) == kFlatPerCu,
