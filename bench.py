@@ -675,8 +675,6 @@ def placement_probe(S, ballasts_gb, device, reps=10):
     carved back to back from one ("one").  The caching allocator is emptied
     between trials, so even a repeated virtual address gets its physical
     pages afresh.  Prints one line per trial and a JSON summary."""
-    import ctypes
-
     import torch
 
     import zero_partitioned_mixed_plan_amd as z

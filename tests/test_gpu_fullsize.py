@@ -52,7 +52,7 @@ import pytest
 import oracle
 import synth
 import zero_partitioned_mixed_plan_amd as z
-from harness import (GRAD_WORD, INF_BITS, PARAM_FILL, REL_TOL, ULP_TOL, Case, flat_offsets,
+from harness import (GRAD_WORD, INF_BITS, PARAM_FILL, ULP_TOL, Case, flat_offsets,
                      cast_library, grad_key, log, master_key, grad_bits_host, max_rel,
                      same_bits, torch_dtype, ulp_diff)
 from synth.workloads import get
